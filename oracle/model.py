@@ -1,0 +1,385 @@
+"""CPU oracle of one block-diffusion denoising step (NumPy, float64).
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's CPU
+baseline may import this module. The product path (the HIP library and its
+Python binding) never does, and this module imports nothing from it.
+
+Every function is a plain transcription of what the pages describe, computed
+in float64 on float64 copies of the bf16 weights. No blocking or fusion beyond
+what the definitions state; loops run over heads, experts and requests so the
+code can be checked against the pages by eye.
+
+Sources (cited by page and section):
+  [explainer]  codemajin.net DiffusionGemma architecture explainer
+               §2.1 base model (MoE: 8 of 128 experts plus 1 shared per token)
+               §3.1 discrete diffusion (uniform-state forward process, the
+                    network predicts clean-token distributions for all
+                    canvas positions in parallel)
+               §3.2 weight-shared causal encoder / bidirectional decoder,
+                    block-autoregressive KV cache, committed blocks never
+                    rewritten, tokens inside the block may still change
+               §3.3 sampler (confidence-ordered acceptance, re-noise the rest
+                    to uniform ids, temperature 0.8 -> 0.4 linear)
+               §5.1 TPF / TPS definitions
+  [aibars]     aibars.net news item: low-confidence tokens are re-noised to
+               random tokens; blocks are committed to the KV cache
+  [aiboss]     aiboss88.com product page: prefill uses causal attention into
+               the KV cache, denoising uses bidirectional attention over the
+               canvas; confident tokens are fixed step by step
+
+Readings where the pages are silent (each is listed in the design doc):
+  pre-norm RMSNorm (eps 1e-6) before attention and MoE plus a final norm;
+  rotate-half RoPE, theta 10000, canvas at absolute positions P..P+C-1;
+  scale 1/sqrt(head_dim), no soft-cap, no sliding window;
+  GQA: q head h reads kv head floor(h * Hkv / Hq);
+  router = top-k of the router logits (ties to the lower expert id), softmax
+  over the k selected logits, shared expert added with weight 1;
+  SwiGLU experts; LM head tied to the embedding, no input scaling;
+  confidence = log of the temperature-tau probability of the candidate token;
+  candidate = held token for committed positions, greedy argmax otherwise;
+  cumulative schedule k_s = floor(s * C / S);
+  committed positions hold their token until they fall out of the top-k_s.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .philox import uniform_ids
+
+
+def f64(a) -> np.ndarray:
+    """float64 copy of a weight or activation (bf16 values are exact in float64)."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# building blocks
+# ----------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain, per row (pre-norm reading)."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * f64(gain)
+
+
+def rope_angles(positions, head_dim: int, theta: float) -> np.ndarray:
+    """angle[p, j] = pos_p * theta^(-2j/head_dim), j < head_dim/2."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = np.power(float(theta), -2.0 * j / head_dim)
+    return np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
+
+
+def rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """Rotate-half RoPE: pairs (j, j + dh/2) rotated by angle[pos, j].
+
+    x: [n, heads, dh]; positions: [n].
+    """
+    dh = x.shape[-1]
+    half = dh // 2
+    ang = rope_angles(positions, dh, theta)
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_prefix: int,
+              causal: bool) -> np.ndarray:
+    """softmax(q k^T / sqrt(dh)) v per query head.
+
+    q: [n, Hq, dh] for the n canvas (or block) positions;
+    k, v: [n_prefix + n, Hkv, dh] = cached prefix rows followed by the rows of
+    the same n positions. Denoising is bidirectional over the canvas (no mask);
+    the causal encoder lets position i see the prefix and block positions <= i.
+    """
+    n, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    nk = k.shape[0]
+    assert nk == n_prefix + n
+    o = np.empty_like(q, dtype=np.float64)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        s = (q[:, h, :] @ k[:, g, :].T) / np.sqrt(dh)
+        if causal:
+            key_pos = np.arange(nk)[None, :]
+            limit = n_prefix + np.arange(n)[:, None]
+            s = np.where(key_pos <= limit, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        o[:, h, :] = p @ v[:, g, :]
+    return o
+
+
+def route(z: np.ndarray, top_k: int):
+    """Top-k experts per row (descending logit, ties to the lower expert id) and
+    the softmax of the k selected logits.
+
+    Returns idx int64 [n, k] (selection order) and w float64 [n, k].
+    """
+    z = np.asarray(z, np.float64)
+    n, E = z.shape
+    idx = np.empty((n, top_k), np.int64)
+    for t in range(n):
+        row = z[t].copy()
+        for j in range(top_k):
+            best = int(np.argmax(row))  # first maximum: the lower id wins ties
+            idx[t, j] = best
+            row[best] = -np.inf
+    sel = np.take_along_axis(z, idx, axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+def permutation(idx: np.ndarray, n_experts: int):
+    """Token -> expert grouping: counts, exclusive offsets, slot order, inverse.
+
+    perm lists token ids grouped by expert, tokens ascending within an expert;
+    slot[t, j] is the position in perm of token t's j-th selection.
+    """
+    n, k = idx.shape
+    cnt = np.array([np.count_nonzero(idx == e) for e in range(n_experts)], np.int64)
+    off = np.zeros(n_experts + 1, np.int64)
+    for e in range(n_experts):
+        off[e + 1] = off[e] + cnt[e]
+    perm = np.empty(n * k, np.int64)
+    slot = np.empty((n, k), np.int64)
+    for e in range(n_experts):
+        tok, sel = np.nonzero(idx == e)  # row-major: tokens ascending
+        perm[off[e]:off[e + 1]] = tok
+        slot[tok, sel] = off[e] + np.arange(len(tok))
+    return cnt, off, perm, slot
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu(x: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
+    """(silu(x Wg^T) * (x Wu^T)) Wd^T."""
+    return (silu(x @ f64(w_gate).T) * (x @ f64(w_up).T)) @ f64(w_down).T
+
+
+def moe(u: np.ndarray, idx: np.ndarray, w: np.ndarray, lw: Dict, n_experts: int,
+        perm_info=None) -> np.ndarray:
+    """sum_j w_tj * Expert_{idx_tj}(u_t) + Shared(u_t), experts run on their token groups."""
+    out = swiglu(u, lw["ws_gate"], lw["ws_up"], lw["ws_down"])
+    cnt, off, perm, slot = perm_info if perm_info is not None else permutation(idx, n_experts)
+    n, k = idx.shape
+    slot_weight = np.empty(n * k, np.float64)
+    for t in range(n):
+        for j in range(k):
+            slot_weight[slot[t, j]] = w[t, j]
+    wg, wu, wd = lw["w_gate"], lw["w_up"], lw["w_down"]
+    for e in range(n_experts):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        rows = perm[lo:hi]
+        y = swiglu(u[rows], wg[e], wu[e], wd[e])
+        out[rows] += slot_weight[lo:hi, None] * y
+    return out
+
+
+# ----------------------------------------------------------------------------
+# one transformer layer over the rows of one request
+# ----------------------------------------------------------------------------
+
+def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np.ndarray,
+                  n_prefix: int, causal: bool, keep: Optional[Dict] = None):
+    """One pre-norm attention + MoE layer on n rows at positions n_prefix..n_prefix+n-1.
+
+    cache_k, cache_v: [>= n_prefix, Hkv, dh] prefix rows (K already rotated).
+    Returns (new h, k rows [n, Hkv, dh] rotated, v rows). `keep`, when given,
+    receives the intermediates by name.
+    """
+    n, d = h.shape
+    Hq, Hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    pos = n_prefix + np.arange(n)
+    u = rms_norm(h, lw["attn_norm"], cfg.rms_eps)
+    qkv = u @ f64(lw["w_qkv"]).T
+    q = qkv[:, : Hq * dh].reshape(n, Hq, dh)
+    k = qkv[:, Hq * dh: (Hq + Hkv) * dh].reshape(n, Hkv, dh)
+    v = qkv[:, (Hq + Hkv) * dh:].reshape(n, Hkv, dh)
+    q = rope(q, pos, cfg.rope_theta)
+    k = rope(k, pos, cfg.rope_theta)
+    k_all = np.concatenate([f64(cache_k[:n_prefix]), k], axis=0)
+    v_all = np.concatenate([f64(cache_v[:n_prefix]), v], axis=0)
+    o = attention(q, k_all, v_all, n_prefix, causal)
+    h1 = h + o.reshape(n, Hq * dh) @ f64(lw["w_o"]).T
+    u2 = rms_norm(h1, lw["moe_norm"], cfg.rms_eps)
+    z = u2 @ f64(lw["w_router"]).T
+    idx, w = route(z, cfg.top_k)
+    pinfo = permutation(idx, cfg.n_experts)
+    h2 = h1 + moe(u2, idx, w, lw, cfg.n_experts, pinfo)
+    if keep is not None:
+        keep.update(u_attn=u, q=q, k=k, v=v, attn_o=o, h_mid=h1, u_moe=u2, z=z,
+                    idx=idx, w=w, cnt=pinfo[0], off=pinfo[1], perm=pinfo[2],
+                    slot=pinfo[3], h_out=h2)
+    return h2, k, v
+
+
+# ----------------------------------------------------------------------------
+# LM head statistics and the confidence sampler
+# ----------------------------------------------------------------------------
+
+def tau_at(step: int, n_steps: int, tau_first: float, tau_last: float) -> float:
+    """Temperature falling linearly from tau_first (step 1) to tau_last (step S)."""
+    if n_steps <= 1:
+        return float(tau_first)
+    return float(tau_first) + (float(tau_last) - float(tau_first)) * (step - 1) / (n_steps - 1)
+
+
+def commit_count(step: int, n_steps: int, canvas: int) -> int:
+    """Cumulative number of canvas positions accepted after step s: floor(s*C/S)."""
+    return (step * canvas) // n_steps
+
+
+def logits(h: np.ndarray, final_norm, embed, cfg, chunk: int = 32768) -> np.ndarray:
+    """RMSNorm(h) E^T over the whole vocabulary (tied LM head), float64 [n, V]."""
+    hf = rms_norm(h, final_norm, cfg.rms_eps)
+    V = embed.shape[0]
+    out = np.empty((h.shape[0], V), np.float64)
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = hf @ f64(embed[v0:v0 + chunk]).T
+    return out
+
+
+def row_stats(L: np.ndarray, held: np.ndarray, tau: float):
+    """Per row: max M, first argmax a, log Z with Z = sum_v exp((L_v - M)/tau),
+    and the logit of the held token."""
+    M = L.max(axis=1)
+    a = np.argmax(L, axis=1)
+    logZ = np.log(np.sum(np.exp((L - M[:, None]) / tau), axis=1))
+    gx = L[np.arange(L.shape[0]), held]
+    return M, a, logZ, gx
+
+
+def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
+           n_steps: int, seed: int, block: int, request: int, vocab: int):
+    """Confidence-ordered acceptance with uniform re-noise.
+
+    Candidate y_i: the held token if position i is committed, else the argmax.
+    Confidence c_i = log p_tau(y_i) = (L[y_i] - M_i)/tau - log Z_i.
+    The k_s positions of highest confidence (ties to the lower position) are
+    accepted (x_i = y_i, committed); every other position is re-noised to a
+    uniform id from Philox at counter (i, step, block, request).
+    Returns (new x, new committed mask, c, accepted-set boolean mask).
+    """
+    C = x.shape[0]
+    committed = np.asarray(m).astype(bool)
+    y = np.where(committed, x, a)
+    Ly = np.where(committed, gx, M)
+    c = (Ly - M) / tau - logZ
+    k_s = commit_count(step, n_steps, C)
+    order = sorted(range(C), key=lambda i: (-c[i], i))
+    accept = np.zeros(C, bool)
+    accept[order[:k_s]] = True
+    noise = uniform_ids(seed, np.arange(C), step, block, request, vocab)
+    x_new = np.where(accept, y, noise)
+    m_new = accept.astype(np.uint8)
+    return x_new.astype(np.int64), m_new, c, accept
+
+
+def init_canvas(seed: int, block: int, request: int, canvas: int, vocab: int):
+    """Canvas of uniform random placeholders (Philox step 0), nothing committed."""
+    x = uniform_ids(seed, np.arange(canvas), 0, block, request, vocab)
+    return x.astype(np.int64), np.zeros(canvas, np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# request state and the three calls of the loop
+# ----------------------------------------------------------------------------
+
+class Request:
+    """KV cache of one request: per layer K (rotated) and V rows, float64."""
+
+    def __init__(self, cfg, max_ctx: int):
+        self.cfg = cfg
+        L, Hkv, dh = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+        self.k = np.zeros((L, max_ctx, Hkv, dh), np.float64)
+        self.v = np.zeros((L, max_ctx, Hkv, dh), np.float64)
+        self.length = 0
+
+
+def forward_rows(weights, cfg, req: Request, ids: np.ndarray, causal: bool,
+                 keep_layers: Optional[List[Dict]] = None, stop_layer: Optional[int] = None):
+    """Embed ids and run the layer stack at positions req.length.. (no cache write)."""
+    h = f64(weights.embed[ids])
+    P = req.length
+    ks, vs = [], []
+    for l in range(cfg.n_layers if stop_layer is None else stop_layer):
+        keep = {} if keep_layers is not None else None
+        h, k, v = layer_forward(h, weights.layer(l), cfg, req.k[l], req.v[l], P, causal, keep)
+        if keep_layers is not None:
+            keep_layers.append(keep)
+        ks.append(k)
+        vs.append(v)
+    return h, ks, vs
+
+
+def append_rows(weights, cfg, req: Request, ids: np.ndarray):
+    """Causal encoder pass over ids; their K/V rows are appended to the cache.
+
+    Rows [0, length) are never written (committed blocks are immutable).
+    """
+    n = len(ids)
+    assert req.length + n <= req.k.shape[1]
+    _, ks, vs = forward_rows(weights, cfg, req, np.asarray(ids), causal=True)
+    P = req.length
+    for l in range(cfg.n_layers):
+        req.k[l, P:P + n] = ks[l]
+        req.v[l, P:P + n] = vs[l]
+    req.length = P + n
+
+
+def prefill(weights, cfg, req: Request, ids: np.ndarray):
+    """Causal prefill of a prompt into the KV cache."""
+    append_rows(weights, cfg, req, ids)
+
+
+def commit_block(weights, cfg, req: Request, canvas_ids: np.ndarray):
+    """Append a finished block: the same causal pass as prefill, over the canvas."""
+    append_rows(weights, cfg, req, canvas_ids)
+
+
+def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step: int,
+                 n_steps: int, seed: int, block: int, request: int,
+                 keep: Optional[Dict] = None):
+    """One denoising step of one request's canvas.
+
+    The canvas attends bidirectionally to itself and to the cached prefix; the
+    LM head gives per-row statistics; the sampler accepts the top-k_s positions
+    and re-noises the rest. The cache is read, never written.
+    """
+    layers = [] if keep is not None else None
+    h, _, _ = forward_rows(weights, cfg, req, np.asarray(x), causal=False, keep_layers=layers)
+    tau = tau_at(step, n_steps, cfg.tau_first, cfg.tau_last)
+    L = logits(h, weights.final_norm, weights.embed, cfg)
+    M, a, logZ, gx = row_stats(L, np.asarray(x), tau)
+    x_new, m_new, c, accept = sample(x, m, M, a, logZ, gx, tau, step, n_steps, seed, block,
+                                     request, cfg.vocab)
+    if keep is not None:
+        keep.update(layers=layers, h=h, logits=L, M=M, a=a, logZ=logZ, gx=gx, c=c,
+                    accept=accept, tau=tau)
+    return x_new, m_new
+
+
+def generate_block(weights, cfg, req: Request, n_steps: int, seed: int, block: int,
+                   request: int):
+    """Denoise one block from uniform noise for n_steps, then commit it."""
+    x, m = init_canvas(seed, block, request, cfg.canvas, cfg.vocab)
+    for s in range(1, n_steps + 1):
+        x, m = denoise_step(weights, cfg, req, x, m, s, n_steps, seed, block, request)
+    commit_block(weights, cfg, req, x)
+    return x, m
