@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark: denoising steps of the full block-diffusion step on one MI355X.
+
+A step is one pass of the whole hot path over one 256-token canvas: embedding,
+30 layers (RMSNorm, QKV + RoPE, canvas attention over [prefix ; canvas],
+output projection, router top-8 + permutation, grouped SwiGLU experts + the
+shared expert, combine), final norm, LM head with fused vocabulary
+statistics, and the confidence sampler. Inputs (weights, KV cache, canvas)
+are resident in HBM before the timed region; weights are seeded random-init
+bf16 with the workload's shapes.
+
+Prints one JSON line (stdout). Progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/s + canvas tok/s (256-tok block), % HBM/MFMA roofline, 1 GPU"
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16
+PAGES_TPF = 19.74          # tokens per forward, codemajin.net explainer §5.3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_model(cfg, prefix, rows, touched_experts):
+    """Bytes and flops per kernel class that one denoising step must move / do.
+
+    Weights: only the touched experts, plus attention, router, shared expert
+    weights and the tied LM head, each read once; the prefix + canvas KV read
+    once per layer; activations ignored (< 1% of the bytes).
+    """
+    d, E, F, Fs, V = cfg.d_model, cfg.n_experts, cfg.d_expert, cfg.d_shared, cfg.vocab
+    L, Hq, Hkv, dh, k = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.top_k
+    nk = prefix + cfg.canvas
+    kinds = {
+        "qkv": (cfg.qkv_rows * d * 2, 2 * rows * cfg.qkv_rows * d),
+        "attn": (nk * Hkv * dh * 2 * 2, 4 * rows * Hq * nk * dh),
+        "oproj": (d * Hq * dh * 2, 2 * rows * d * Hq * dh),
+        "router": (E * d * 2, 2 * rows * E * d),
+        "gateup": (touched_experts * 2 * F * d * 2 + 2 * Fs * d * 2,
+                   2 * rows * k * 2 * F * d + 2 * rows * 2 * Fs * d),
+        "down": (touched_experts * F * d * 2 + Fs * d * 2, 2 * rows * k * F * d + 2 * rows * Fs * d),
+    }
+    per_step = {name: (b * L, f * L) for name, (b, f) in kinds.items()}
+    per_step["lmhead"] = (V * d * 2, 2 * rows * V * d)
+    return kinds, per_step
+
+
+class _HostWeights:
+    """Host copies of the GPU weights, one layer at a time, for the oracle."""
+
+    def __init__(self, layers, embed, final_norm):
+        self._layers, self.embed, self.final_norm = layers, embed.cpu(), final_norm.cpu()
+        self._cache = {}
+
+    def layer(self, i):
+        if i not in self._cache:
+            self._cache = {i: {k: v.cpu() for k, v in self._layers[i].items()}}
+        return self._cache[i]
+
+
+def cpu_baseline(eng, hw, cfg, canvas_ids, prefix, n_layers_sample, step, n_steps):
+    """Time the float64 oracle on a bounded sample of the same step."""
+    import numpy as np
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:
+        blas_threads = 0
+    cores = len(os.sched_getaffinity(0))
+    req = om.Request(cfg, prefix + cfg.canvas)
+    kv = eng.kv_view()
+    x = canvas_ids.astype(np.int64)
+    t0 = time.perf_counter()
+    h = om.f64(hw.embed[x])
+    t_embed = time.perf_counter() - t0
+    t_layers = 0.0
+    for l in range(n_layers_sample):
+        lw = hw.layer(l)
+        ck = om.f64(kv[0, l, 0, :, :prefix].permute(1, 0, 2).cpu())
+        cv = om.f64(kv[0, l, 1, :, :prefix].permute(1, 0, 2).cpu())
+        t0 = time.perf_counter()
+        h, _, _ = om.layer_forward(h, lw, cfg, ck, cv, prefix, False)
+        t_layers += time.perf_counter() - t0
+        log(f"cpu baseline: layer {l} {time.perf_counter() - t0:.2f}s")
+    t0 = time.perf_counter()
+    tau = om.tau_at(step, n_steps, cfg.tau_first, cfg.tau_last)
+    Lg = om.logits(h, hw.final_norm, hw.embed, cfg)
+    M, a, logZ, gx = om.row_stats(Lg, x, tau)
+    om.sample(x, np.zeros_like(x, dtype=np.uint8), M, a, logZ, gx, tau, step, n_steps, 0, 0, 0,
+              cfg.vocab)
+    t_head = time.perf_counter() - t0
+    log(f"cpu baseline: head {t_head:.2f}s")
+    t_step = t_embed + t_layers * cfg.n_layers / n_layers_sample + t_head
+    return {
+        "value": 1.0 / t_step,
+        "unit": "denoise steps/s",
+        "cores": cores,
+        "blas_threads": blas_threads,
+        "kind": "oracle",
+        "ms_per_step": t_step * 1e3,
+        "sample": (f"float64 NumPy oracle: embedding + layers 0..{n_layers_sample - 1} of "
+                   f"{cfg.n_layers} on all {cfg.canvas} canvas rows (timed "
+                   f"{t_layers:.1f}s, scaled x{cfg.n_layers / n_layers_sample:g}) + full LM head over "
+                   f"{cfg.vocab} ids + sampler (timed {t_head:.1f}s)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full", choices=["full", "long", "batch", "tiny", "one_layer"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoising step "
+              "is measured on a single MI355X; multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_discrete_diffusion_dg_amd import synth
+    from block_discrete_diffusion_dg_amd.engine import Engine, gpu_weights
+
+    wl = synth.WORKLOADS[args.workload]
+    cfg, P, S, n_req = wl.model, wl.prefix, wl.n_steps, wl.n_req
+    C = cfg.canvas
+    rows = n_req * C
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"workload {wl.name}: L={cfg.n_layers} d={cfg.d_model} E={cfg.n_experts} V={cfg.vocab} "
+        f"prefix={P} canvas={C} n_req={n_req}")
+    t0 = time.time()
+    layers, embed, final = gpu_weights(cfg, wl.seed, 0.0, dev)
+    torch.cuda.synchronize()
+    log(f"weights generated on the GPU in {time.time() - t0:.1f}s")
+    eng = Engine(cfg, layers, embed, final, max_ctx=P + 2 * C, max_requests=n_req, max_rows=rows)
+    reqs = list(range(n_req))
+    seeds = [wl.seed + r for r in reqs]
+    blocks = [0] * n_req
+    t0 = time.time()
+    for r in reqs:
+        eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
+    torch.cuda.synchronize()
+    log(f"prefill of {n_req} x {P} tokens: {time.time() - t0:.2f}s")
+    x = torch.empty(rows, dtype=torch.int32, device=dev)
+    m = torch.empty(rows, dtype=torch.uint8, device=dev)
+    eng.init_canvas(reqs, x, m, seeds, blocks)
+    canvas0 = x.cpu().numpy()
+
+    def run(n, start):
+        for i in range(n):
+            s = (start + i) % S + 1
+            eng.denoise_step(reqs, x, m, s, S, seeds, blocks)
+
+    run(args.warmup, 0)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    run(args.steps, args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
+
+    # per-stage durations: a second pass with per-launch events on the same stream
+    eng.timing(True)
+    run(args.steps, args.warmup + args.steps)
+    stages = eng.timing_read()
+    eng.timing(False)
+    stage_ms = {k: v[0] / args.steps for k, v in stages.items() if v[1]}
+    launches = {k: v[1] // args.steps for k, v in stages.items() if v[1]}
+    log("stage ms/step: " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
+
+    # commit (the +K-1 forward of each block), timed once, then the length restored
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    eng.commit_block(reqs, x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    commit_ms = c0.elapsed_time(c1)
+    for r in reqs:
+        eng.set_cache_len(r, P)
+
+    cnt = eng.ws_view("cnt", torch.int32, (cfg.n_experts,)).cpu().numpy()
+    touched = int((cnt > 0).sum())
+    kinds, per_step = algorithmic_model(cfg, P, rows, touched)
+    t_roof = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in per_step.values())
+    b_gu, f_gu = kinds["gateup"]
+    gu_launch_ms = stages["gateup"][0] / max(1, stages["gateup"][1])
+    achieved = b_gu / (gu_launch_ms * 1e-3)
+    steps_per_s = 1e3 / ms
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init bf16 weights, uniform prompt ids (no datasets or checkpoints)",
+        "config": {"workload": wl.name, "layers": cfg.n_layers, "d_model": cfg.d_model,
+                   "experts": f"{cfg.n_experts} routed top-{cfg.top_k} + 1 shared",
+                   "vocab": cfg.vocab, "prefix": P, "canvas": C, "n_req": n_req,
+                   "denoise_steps_per_block": S},
+        "canvas_tok_s": round(steps_per_s * rows, 1),
+        "effective_tok_s": {"tpf_pages_19.74": round(steps_per_s * PAGES_TPF * n_req, 1),
+                            f"tpf_loop_{C / S:g}": round(steps_per_s * C / S * n_req, 1)},
+        "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms, 4),
+                          "touched_experts_per_layer": touched},
+        "roofline": {"kernel": "moe_gateup (routed + shared expert gate/up + SwiGLU)",
+                     "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+                     "bytes_per_launch": b_gu, "avg_launch_ms": round(gu_launch_ms, 4),
+                     "traffic": None},
+        "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
+        "launches_per_step": launches,
+        "commit_ms": round(commit_ms, 3),
+    }
+    if not args.no_cpu_baseline and args.workload in ("full", "one_layer", "tiny"):
+        hw = _HostWeights(layers, embed, final)
+        log("cpu baseline: timing the oracle on a sample of the step")
+        out["cpu_baseline"] = cpu_baseline(eng, hw, cfg, canvas0[:C], P,
+                                           min(args.cpu_layers, cfg.n_layers), 1, S)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

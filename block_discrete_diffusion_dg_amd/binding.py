@@ -1,0 +1,115 @@
+"""ctypes binding of libdg (include/dg.h, include/dg_test.h): argument marshalling only.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python -m block_discrete_diffusion_dg_amd.build``); a missing library is an
+error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+
+DG_OK, DG_EINVAL, DG_ECAPACITY, DG_EHIP, DG_ESTATE = 0, -1, -2, -3, -4
+STATUS_NAMES = {0: "DG_OK", -1: "DG_EINVAL", -2: "DG_ECAPACITY", -3: "DG_EHIP", -4: "DG_ESTATE"}
+
+c_i32 = ctypes.c_int32
+c_f32 = ctypes.c_float
+c_vp = ctypes.c_void_p
+c_size = ctypes.c_size_t
+
+
+class DGConfig(ctypes.Structure):
+    _fields_ = [(n, c_i32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
+                                     "n_experts", "top_k", "d_expert", "d_shared", "vocab",
+                                     "canvas", "max_ctx", "max_requests", "max_rows")] + \
+               [(n, c_f32) for n in ("rms_eps", "rope_theta", "tau_first", "tau_last")]
+
+
+LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "w_gate", "w_up", "w_down",
+                "ws_gate", "ws_up", "ws_down")
+
+
+class DGLayerWeights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in LAYER_FIELDS]
+
+
+class DGWeights(ctypes.Structure):
+    _fields_ = [("embed", c_vp), ("final_norm", c_vp), ("layers", ctypes.POINTER(DGLayerWeights))]
+
+
+class DGRowStats(ctypes.Structure):
+    _fields_ = [("max_logit", c_f32), ("log_z", c_f32), ("held_logit", c_f32), ("conf", c_f32),
+                ("argmax", c_i32), ("accepted", c_i32), ("pad", c_i32 * 2)]
+
+
+ROW_STATS_BYTES = ctypes.sizeof(DGRowStats)
+
+
+class DGStepArgs(ctypes.Structure):
+    _fields_ = [("n_req", c_i32), ("req", ctypes.POINTER(c_i32)), ("d_canvas", c_vp),
+                ("d_committed", c_vp), ("step", c_i32), ("n_steps", c_i32),
+                ("seed", ctypes.POINTER(ctypes.c_uint64)), ("block", ctypes.POINTER(c_i32)),
+                ("d_stats", c_vp)]
+
+
+WS_FIELDS = ("h", "u", "q", "attn_o", "attn_part", "attn_ml", "rope", "z", "idx", "w", "wslot",
+             "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "stats", "ids",
+             "total")
+
+
+class DGWsLayout(ctypes.Structure):
+    _fields_ = [(n, c_size) for n in WS_FIELDS]
+
+
+# name -> (restype, argtypes); every symbol declared in include/dg.h and include/dg_test.h
+SIGNATURES = {
+    "dg_kv_cache_bytes": (c_size, [ctypes.POINTER(DGConfig)]),
+    "dg_workspace_bytes": (c_size, [ctypes.POINTER(DGConfig)]),
+    "dg_create": (c_i32, [ctypes.POINTER(DGConfig), ctypes.POINTER(DGWeights), c_vp, c_vp, c_size,
+                          ctypes.POINTER(c_vp)]),
+    "dg_destroy": (None, [c_vp]),
+    "dg_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32]),
+    "dg_init_canvas": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
+    "dg_denoise_step": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
+    "dg_commit_block": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp]),
+    "dg_cache_len": (c_i32, [c_vp, c_i32]),
+    "dg_reset": (c_i32, [c_vp, c_i32]),
+    "dg_set_cache_len": (c_i32, [c_vp, c_i32, c_i32]),
+    "dg_last_error": (ctypes.c_char_p, [c_vp]),
+    "dg_workspace_layout": (c_i32, [ctypes.POINTER(DGConfig), ctypes.POINTER(DGWsLayout)]),
+    "dg_test_layer": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_i32]),
+    "dg_test_route": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "dg_test_head": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs), c_vp]),
+    "dg_timing_enable": (c_i32, [c_vp, c_i32]),
+    "dg_timing_read": (c_i32, [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32]),
+}
+
+STAGES = ("embed", "norm", "qkv", "attn", "oproj", "router", "topk", "permute", "gateup", "down",
+          "combine", "lmhead", "merge", "sampler")
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Open libdg.so (built in-tree) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m block_discrete_diffusion_dg_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status

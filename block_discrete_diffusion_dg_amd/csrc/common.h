@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 storage, MFMA
+// fragments, wave-level reductions, and the per-call request table.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DG_MAX_REQ 16       // requests batched into one call
+#define DG_ATTN_SPLITS 8    // maximum key splits of the attention kernel
+#define WAVE 64
+
+// Per-call request table, passed by value to the kernels that need positions
+// or KV-cache addresses. Row r*rows_per_req + i belongs to request r, at
+// sequence position pos0[r] + i.
+struct ReqTable {
+  int32_t n_req;
+  int32_t rows_per_req;
+  int32_t slot[DG_MAX_REQ];
+  int32_t pos0[DG_MAX_REQ];
+};
+
+// KV-cache geometry: [slot][layer][K|V][kv_head][max_ctx][head_dim] bf16.
+struct KvGeom {
+  bf16_t* base;
+  int64_t slot_stride;   // elements per request slot
+  int64_t layer_stride;  // elements per layer
+  int64_t head_stride;   // elements per (K|V, kv_head) plane = max_ctx * dh
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  __device__ __forceinline__ bf16_t* k_plane(int slot, int layer, int g) const {
+    return base + slot * slot_stride + layer * layer_stride + (int64_t)g * head_stride;
+  }
+  __device__ __forceinline__ bf16_t* v_plane(int slot, int layer, int g) const {
+    return base + slot * slot_stride + layer * layer_stride +
+           (int64_t)(n_kv_heads + g) * head_stride;
+  }
+};
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (bf16_t)(b >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// D = A(16x32) * B(32x16) + C on the gfx950 bf16 matrix core.
+// Lane l supplies A row (l % 16) and B column (l % 16), eight consecutive
+// reduction indices of group l / 16 (any fixed assignment of reduction
+// indices works as long as A and B use the same one). The result holds
+// D[4*(l/16) + r][l % 16] in element r.
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// (value, index) reduction: larger value wins, ties go to the lower index.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__host__ __device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }

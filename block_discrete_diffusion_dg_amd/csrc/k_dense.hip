@@ -1,0 +1,121 @@
+// Dense projections of a layer on the weight-streaming tile (stream.h):
+//   QKV + RoPE: every lane owns a rotate-half pair (head row j and j + dh/2)
+//     as the tile's two weight rows, so the rotation is lane-local; q goes to
+//     the workspace, k (rotated) and v to the request's KV-cache rows.
+//   output projection: h[row][col] += (o W_o^T)[row][col].
+// All token rows form one group cut into chunks of 16*MT rows; the chunks
+// of one column tile get work-group ids 8 apart (same XCD, shared L2 copy of
+// the weight tile) when the tile count is a multiple of 8.
+#include "common.h"
+#include "kernels.h"
+#include "stream.h"
+
+namespace {
+
+constexpr int DMT = 2;  // rows per chunk = 32
+constexpr int DBK = 128;
+
+__device__ __forceinline__ void tile_coords(int NT, int MC, int& nt, int& mc) {
+  const int b = blockIdx.x;
+  if ((NT & 7) == 0) {
+    mc = (b >> 3) % MC;
+    nt = (b & 7) + 8 * (b / (8 * MC));
+  } else {
+    mc = b % MC;
+    nt = b / MC;
+  }
+}
+
+struct QkvArgs {
+  bf16_t* q;  // [rows][Hq*dh]
+  KvGeom kv;
+  int layer, Hq, Hkv, dh;
+  const float2* rope;  // [rows][dh/2] (cos, sin)
+  ReqTable rt;
+};
+
+__global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, int rows, int d,
+                                                  const bf16_t* __restrict__ w, QkvArgs p) {
+  using T = StreamTile<DMT, DBK>;
+  __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
+  const int dh = p.dh, half = dh >> 1;
+  const int NT = (p.Hq + 2 * p.Hkv) * half / 64, MC = div_up(rows, T::CH);
+  int nt, mc;
+  tile_coords(NT, MC, nt, mc);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+  const int pc = nt * 64 + wave * 16 + l16;
+  const int head = pc / half, j = pc % half;
+  const int64_t r0 = (int64_t)head * dh + j;
+  const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
+  f32x4 a0[DMT], a1[DMT];
+  stream_tile<DMT, DBK, true>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
+  const bool rotate = head < p.Hq + p.Hkv;
+#pragma unroll
+  for (int mt = 0; mt < DMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 16 * mt + 4 * grp + r;
+      if (row >= rows) continue;
+      float x1 = a0[mt][r], x2 = a1[mt][r];
+      if (rotate) {
+        const float2 cs = p.rope[(int64_t)row * half + j];
+        const float y1 = x1 * cs.x - x2 * cs.y;
+        const float y2 = x2 * cs.x + x1 * cs.y;
+        x1 = y1;
+        x2 = y2;
+      }
+      bf16_t* dst;
+      if (head < p.Hq) {
+        dst = p.q + (int64_t)row * p.Hq * dh + (int64_t)head * dh;
+      } else {
+        const int rq = row / p.rt.rows_per_req, i = row % p.rt.rows_per_req;
+        const int pos = p.rt.pos0[rq] + i;
+        const int slot = p.rt.slot[rq];
+        dst = (head < p.Hq + p.Hkv ? p.kv.k_plane(slot, p.layer, head - p.Hq)
+                                   : p.kv.v_plane(slot, p.layer, head - p.Hq - p.Hkv)) +
+              (int64_t)pos * dh;
+      }
+      dst[j] = f2bf(x1);
+      dst[j + half] = f2bf(x2);
+    }
+}
+
+// h[row][col] += (A W^T)[row][col]
+__global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a, int rows, int K,
+                                                    const bf16_t* __restrict__ w, int N,
+                                                    float* __restrict__ h) {
+  using T = StreamTile<DMT, DBK>;
+  __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
+  const int NT = N / 64, MC = div_up(rows, T::CH);
+  int nt, mc;
+  tile_coords(NT, MC, nt, mc);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+  const int col = nt * 64 + wave * 16 + l16;
+  const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
+  f32x4 acc[DMT], unused[DMT];
+  stream_tile<DMT, DBK, false>(a, K, nullptr, row0, nrows, w + (int64_t)col * K, nullptr, K, acc, unused,
+                               lds);
+#pragma unroll
+  for (int mt = 0; mt < DMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 16 * mt + 4 * grp + r;
+      if (row < rows) h[(int64_t)row * N + col] += acc[mt][r];
+    }
+}
+
+}  // namespace
+
+void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
+                const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
+                const ReqTable& rt) {
+  QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt};
+  const int NT = (Hq + 2 * Hkv) * (dh / 2) / 64;
+  const int MC = div_up(rows, StreamTile<DMT, DBK>::CH);
+  hipLaunchKernelGGL(qkv_kernel, dim3(NT * MC), dim3(256), 0, s, u, rows, d, w, p);
+}
+
+void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h) {
+  const int MC = div_up(rows, StreamTile<DMT, DBK>::CH);
+  hipLaunchKernelGGL(resid_kernel, dim3((N / 64) * MC), dim3(256), 0, s, a, rows, K, w, N, h);
+}

@@ -1,0 +1,120 @@
+// Row-wise kernels of the step: embedding gather, RMSNorm, the RoPE table,
+// and the uniform initial canvas.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "philox.h"
+
+namespace {
+
+// h[row] = E[ids[row]] in fp32 and u[row] = bf16(RMSNorm(h[row]) * gain).
+// Ids outside [0, V) are clamped (no fault).
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids,
+                                                    const bf16_t* __restrict__ E, int d, int V,
+                                                    float* __restrict__ h,
+                                                    const bf16_t* __restrict__ gain, float eps,
+                                                    bf16_t* __restrict__ u) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int id = ids[row];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  const bf16_t* src = E + (int64_t)id * d;
+  float* dst = h + (int64_t)row * d;
+  float ss = 0.f;
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    const u32x4 v = ld16(src + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = __uint_as_float(v[j] << 16), b = __uint_as_float(v[j] & 0xffff0000u);
+      dst[c + 2 * j] = a;
+      dst[c + 2 * j + 1] = b;
+      ss += a * a + b * b;
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    const u32x4 v = ld16(src + c);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = __uint_as_float(v[j] << 16), b = __uint_as_float(v[j] & 0xffff0000u);
+      o[j] = pack_bf16x2(a * inv * bf2f(gain[c + 2 * j]), b * inv * bf2f(gain[c + 2 * j + 1]));
+    }
+    *reinterpret_cast<u32x4*>(u + (int64_t)row * d + c) = o;
+  }
+}
+
+// u[row] = bf16( h[row] / sqrt(mean(h[row]^2) + eps) * gain )
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h,
+                                                      const bf16_t* __restrict__ gain, int d,
+                                                      float eps, bf16_t* __restrict__ u) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const float* x = h + (int64_t)row * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(x + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  bf16_t* o = u + (int64_t)row * d;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(x + c);
+    const uint32_t lo = pack_bf16x2(v.x * inv * bf2f(gain[c]), v.y * inv * bf2f(gain[c + 1]));
+    const uint32_t hi = pack_bf16x2(v.z * inv * bf2f(gain[c + 2]), v.w * inv * bf2f(gain[c + 3]));
+    *reinterpret_cast<u32x2*>(o + c) = u32x2{lo, hi};
+  }
+}
+
+// cs[row][j] = (cos, sin)(pos * theta^(-2j/dh)), evaluated in double and
+// rounded once to fp32.
+__global__ void rope_table_kernel(ReqTable rt, int dh, double theta, float2* __restrict__ cs) {
+  const int row = blockIdx.x, j = threadIdx.x, half = dh >> 1;
+  if (j >= half) return;
+  const int r = row / rt.rows_per_req, i = row % rt.rows_per_req;
+  const double pos = (double)(rt.pos0[r] + i);
+  const double ang = pos * pow(theta, -2.0 * (double)j / (double)dh);
+  cs[(int64_t)row * half + j] = float2{(float)cos(ang), (float)sin(ang)};
+}
+
+__global__ void init_canvas_kernel(SampleTable st, int C, int V, int32_t* __restrict__ canvas,
+                                   uint8_t* __restrict__ committed) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < C; i += blockDim.x) {
+    const uint32_t w0 = philox4x32_10_word0(i, 0, st.block[r], st.slot[r], st.key_lo[r], st.key_hi[r]);
+    canvas[r * C + i] = (int32_t)(((uint64_t)w0 * (uint64_t)V) >> 32);
+    committed[r * C + i] = 0;
+  }
+}
+
+}  // namespace
+
+void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
+                  float* h, const bf16_t* gain, float eps, bf16_t* u) {
+  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, ids, embed, d, V, h, gain, eps, u);
+}
+
+void launch_rmsnorm(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
+                    bf16_t* u) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, h, gain, d, eps, u);
+}
+
+void launch_rope_table(hipStream_t s, const ReqTable& rt, int dh, float theta, float2* cs) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(rt.n_req * rt.rows_per_req), dim3(64), 0, s, rt, dh,
+                     (double)theta, cs);
+}
+
+void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas, uint8_t* committed,
+                        const uint64_t* seeds_host, const int32_t* blocks_host,
+                        const int32_t* slots_host) {
+  SampleTable st = make_sample_table(n_req, seeds_host, blocks_host, slots_host);
+  hipLaunchKernelGGL(init_canvas_kernel, dim3(n_req), dim3(256), 0, s, st, C, V, canvas, committed);
+}

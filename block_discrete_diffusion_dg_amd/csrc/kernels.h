@@ -1,0 +1,65 @@
+// Host-side launchers of the gfx950 kernels (internal to libdg).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+// k_elem.hip
+void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
+                  float* h, const bf16_t* gain, float eps, bf16_t* u);
+void launch_rmsnorm(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
+                    bf16_t* u);
+void launch_rope_table(hipStream_t s, const ReqTable& rt, int dh, float theta, float2* cs);
+void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas, uint8_t* committed,
+                        const uint64_t* seeds_host, const int32_t* blocks_host,
+                        const int32_t* slots_host);
+
+// k_dense.hip (weight-streaming dense projections)
+void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
+                const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
+                const ReqTable& rt);
+void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h);
+
+// k_gemm.hip (LM head: LDS-tiled GEMM with fused vocabulary statistics)
+void launch_gemm_lmhead(hipStream_t s, int mt, const bf16_t* a, int rows, int K, const bf16_t* embed,
+                        int V, const int32_t* held, float tau, float4* part, float* held_logit,
+                        int held_stride);
+int lmhead_parts(int V);
+
+// k_attn.hip
+int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows);
+void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer,
+                      const ReqTable& rt, int Hq, int Hkv, int dh, int causal, int nsplit,
+                      float* opart, float2* ml, bf16_t* out);
+
+// k_route.hip
+void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t* idx, float* w);
+void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
+                             const bf16_t* wr, int E, int k, bf16_t* u, float* z, int32_t* idx, float* w);
+void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
+                    int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
+                    int32_t* widx, int32_t* items_gu, int32_t* items_dn);
+size_t permute_lds_bytes(int rows, int E, int k);
+
+// k_moe.hip
+int moe_rows_per_chunk(int rows, int E, int k);
+int moe_item_bound(int rows, int E, int k, int n_tiles_routed, int n_tiles_shared);
+void launch_moe_gateup(hipStream_t s, const bf16_t* u, int rows, int d, const int32_t* perm,
+                       const int32_t* cnt, const int32_t* off, const int32_t* items,
+                       const bf16_t* wg, const bf16_t* wu, int F, int E, int k, const bf16_t* sg,
+                       const bf16_t* su, int Fs, bf16_t* hid, bf16_t* hid_s);
+void launch_moe_down(hipStream_t s, const bf16_t* hid, const bf16_t* hid_s, int rows, int d,
+                     const int32_t* cnt, const int32_t* off, const float* w, const int32_t* widx,
+                     const int32_t* items, const bf16_t* wd, int F, int E, int k, const bf16_t* sd,
+                     int Fs, float* y, float* ys);
+void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y,
+                        const int32_t* slot, int rows, int d, int k, const bf16_t* next_gain,
+                        float eps, bf16_t* u);
+
+// k_head.hip
+void launch_lm_merge(hipStream_t s, const float4* part, int n_parts, int rows, float tau,
+                     void* stats);
+void launch_sampler(hipStream_t s, void* stats, int n_req, int C, int V, int32_t* canvas,
+                    uint8_t* committed, int step, int k_s, float tau, const uint64_t* seeds_host,
+                    const int32_t* blocks_host, const int32_t* slots_host, void* stats_out);

@@ -1,0 +1,207 @@
+"""Engine: torch-allocated device memory around one libdg context.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+denoising path runs in libdg's kernels. This module only marshals tensors into
+the C entry points (include/dg.h) and strings them into the block loop the
+pages describe (codemajin.net DiffusionGemma explainer §3.2: denoise a
+256-token block to completion, append it to the KV cache, start the next).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+from .synth import LAYER_TENSORS, ModelConfig
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Engine:
+    """One context: weights (bf16, on the GPU), KV cache and workspace tensors."""
+
+    def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
+                 embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
+                 max_requests: int = 1, max_rows: Optional[int] = None):
+        self.lib = B.load()
+        self.cfg = cfg
+        dev = embed.device
+        if dev.type != "cuda":
+            raise RuntimeError("Engine needs weights on a GPU device")
+        self.max_rows = max_rows or cfg.canvas * max_requests
+        c = B.DGConfig()
+        for name in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts",
+                     "top_k", "d_expert", "d_shared", "vocab", "canvas"):
+            setattr(c, name, getattr(cfg, name))
+        c.max_ctx, c.max_requests, c.max_rows = max_ctx, max_requests, self.max_rows
+        c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
+        c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
+        self.c_cfg = c
+        self._keep = [embed, final_norm] + [t for lw in layers for t in lw.values()]
+        arr = (B.DGLayerWeights * max(1, len(layers)))()
+        for i, lw in enumerate(layers):
+            for name in LAYER_TENSORS:
+                t = lw[name]
+                assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == dev, name
+                setattr(arr[i], name, t.data_ptr())
+        self._layer_arr = arr
+        w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr)
+        kv_bytes = self.lib.dg_kv_cache_bytes(ctypes.byref(c))
+        ws_bytes = self.lib.dg_workspace_bytes(ctypes.byref(c))
+        if ws_bytes == 0:
+            raise B.DGError(B.DG_EINVAL, "unsupported configuration")
+        self.kv = torch.zeros(max(256, max_requests * kv_bytes), dtype=torch.uint8, device=dev)
+        self.kv_bytes = max_requests * kv_bytes
+        self.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        h = ctypes.c_void_p()
+        st = self.lib.dg_create(ctypes.byref(c), ctypes.byref(w), self.kv.data_ptr(),
+                                self.ws.data_ptr(), ws_bytes, ctypes.byref(h))
+        if st != B.DG_OK:
+            raise B.DGError(st, "dg_create failed")
+        self.ctx = h
+        self.layout = B.DGWsLayout()
+        self._check(self.lib.dg_workspace_layout(ctypes.byref(c), ctypes.byref(self.layout)))
+        self.max_ctx = max_ctx
+        self.max_requests = max_requests
+
+    # ------------------------------------------------------------------ plumbing
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.dg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, status: int):
+        if status != B.DG_OK:
+            msg = self.lib.dg_last_error(self.ctx).decode() if getattr(self, "ctx", None) else ""
+            raise B.DGError(status, msg)
+
+    def kv_view(self) -> torch.Tensor:
+        """[slot][layer][K|V][kv_head][max_ctx][head_dim] bf16 view of the cache."""
+        c = self.cfg
+        return self.kv[:self.kv_bytes].view(torch.bfloat16).view(
+            self.max_requests, c.n_layers, 2, c.n_kv_heads, self.max_ctx, c.head_dim)
+
+    def ws_view(self, name: str, dtype: torch.dtype, shape) -> torch.Tensor:
+        off = getattr(self.layout, name)
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(*shape)
+
+    def cache_len(self, req: int) -> int:
+        return self.lib.dg_cache_len(self.ctx, req)
+
+    def set_cache_len(self, req: int, n: int):
+        self._check(self.lib.dg_set_cache_len(self.ctx, req, n))
+
+    def _args(self, reqs, canvas, committed, step, n_steps, seeds, blocks, stats):
+        n = len(reqs)
+        a = B.DGStepArgs()
+        a.n_req = n
+        self._req_arr = (ctypes.c_int32 * n)(*reqs)
+        self._seed_arr = (ctypes.c_uint64 * n)(*[int(s) & (2**64 - 1) for s in seeds])
+        self._block_arr = (ctypes.c_int32 * n)(*blocks)
+        a.req = self._req_arr
+        a.seed = self._seed_arr
+        a.block = self._block_arr
+        assert canvas.dtype == torch.int32 and canvas.is_cuda and canvas.is_contiguous()
+        assert committed.dtype == torch.uint8 and committed.is_cuda and committed.is_contiguous()
+        assert canvas.numel() == n * self.cfg.canvas and committed.numel() == n * self.cfg.canvas
+        a.d_canvas = canvas.data_ptr()
+        a.d_committed = committed.data_ptr()
+        a.step, a.n_steps = step, n_steps
+        a.d_stats = _ptr(stats)
+        return a
+
+    # ------------------------------------------------------------------ the calls
+    def prefill(self, req: int, ids: torch.Tensor):
+        assert ids.dtype == torch.int32 and ids.is_cuda and ids.is_contiguous()
+        self._check(self.lib.dg_prefill(self.ctx, _stream(), req, ids.data_ptr(), ids.numel()))
+
+    def init_canvas(self, reqs, canvas, committed, seeds, blocks):
+        a = self._args(reqs, canvas, committed, 0, 1, seeds, blocks, None)
+        self._check(self.lib.dg_init_canvas(self.ctx, _stream(), ctypes.byref(a)))
+
+    def denoise_step(self, reqs, canvas, committed, step, n_steps, seeds, blocks,
+                     stats: Optional[torch.Tensor] = None):
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats)
+        self._check(self.lib.dg_denoise_step(self.ctx, _stream(), ctypes.byref(a)))
+
+    def commit_block(self, reqs, canvas):
+        arr = (ctypes.c_int32 * len(reqs))(*reqs)
+        self._check(self.lib.dg_commit_block(self.ctx, _stream(), len(reqs), arr, canvas.data_ptr()))
+
+    def new_stats(self, n_req: int) -> torch.Tensor:
+        return torch.zeros((n_req * self.cfg.canvas, B.ROW_STATS_BYTES // 4), dtype=torch.int32,
+                           device=self.kv.device)
+
+    # ------------------------------------------------------------------ per-stage timing
+    def timing(self, enable: bool):
+        self._check(self.lib.dg_timing_enable(self.ctx, int(enable)))
+
+    def timing_read(self) -> Dict[str, tuple]:
+        """{stage: (total ms, launches)} since the last read (waits for the GPU)."""
+        n = len(B.STAGES)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int32 * n)()
+        self._check(self.lib.dg_timing_read(self.ctx, ms, cnt, n))
+        return {name: (ms[i], cnt[i]) for i, name in enumerate(B.STAGES)}
+
+    # ------------------------------------------------------------------ stage-level entry points
+    def test_layer(self, req: int, layer: int, h: torch.Tensor, causal: bool):
+        assert h.dtype == torch.float32 and h.is_cuda and h.is_contiguous()
+        self._check(self.lib.dg_test_layer(self.ctx, _stream(), req, layer, h.data_ptr(),
+                                           h.shape[0], int(causal)))
+
+    def test_route(self, z: torch.Tensor):
+        rows = z.shape[0]
+        k, E = self.cfg.top_k, self.cfg.n_experts
+        dev = z.device
+        out = dict(idx=torch.empty((rows, k), dtype=torch.int32, device=dev),
+                   w=torch.empty((rows, k), dtype=torch.float32, device=dev),
+                   cnt=torch.empty(E, dtype=torch.int32, device=dev),
+                   off=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(rows * k, dtype=torch.int32, device=dev),
+                   slot=torch.empty((rows, k), dtype=torch.int32, device=dev))
+        self._check(self.lib.dg_test_route(self.ctx, _stream(), z.data_ptr(), rows,
+                                           *[out[n].data_ptr() for n in
+                                             ("idx", "w", "cnt", "off", "perm", "slot")]))
+        return out
+
+    def test_head(self, reqs, h, canvas, committed, step, n_steps, seeds, blocks, stats=None):
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats)
+        self._check(self.lib.dg_test_head(self.ctx, _stream(), ctypes.byref(a), h.data_ptr()))
+
+
+def stats_fields(stats: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Split a [rows][8] int32 dg_row_stats tensor into named CPU tensors."""
+    s = stats.cpu()
+    f = s.view(torch.float32)
+    return dict(max_logit=f[:, 0], log_z=f[:, 1], held_logit=f[:, 2], conf=f[:, 3],
+                argmax=s[:, 4], accepted=s[:, 5])
+
+
+def gpu_weights(cfg: ModelConfig, model_seed: int = 0, gain_jitter: float = 0.0,
+                device: str = "cuda"):
+    """Generate a model's weights directly on the GPU (same bits as on the CPU)."""
+    from . import synth
+    layers = [synth.make_layer_weights(cfg, l, model_seed, device, gain_jitter)
+              for l in range(cfg.n_layers)]
+    embed = synth.make_embedding(cfg, model_seed, device)
+    final = synth.make_final_norm(cfg, model_seed, device, gain_jitter)
+    return layers, embed, final

@@ -1,0 +1,196 @@
+/*
+ * dg.h - one block-diffusion denoising step on MI355X (gfx950), C ABI.
+ *
+ * The model is the one the pages describe (codemajin.net DiffusionGemma
+ * explainer §2.1-§3.3; aiboss88.com product page, "technical principles"):
+ * a weight-shared MoE transformer used two ways.
+ *   - As a causal encoder it turns the prompt, and every finished 256-token
+ *     block, into K/V rows appended to a per-request KV cache (dg_prefill,
+ *     dg_commit_block). Committed rows are never rewritten (explainer §3.2).
+ *   - As a bidirectional decoder it denoises the current canvas: every canvas
+ *     position attends to the cached prefix and to every other canvas
+ *     position, the LM head gives a distribution per position, and the
+ *     confidence sampler keeps the most confident tokens and re-noises the
+ *     rest to uniform random ids (dg_denoise_step; explainer §3.3, aibars.net
+ *     news item, "Uniform State Diffusion").
+ *
+ * Conventions (all calls):
+ *   - Plain C types only. Device pointers are named d_*; everything else is
+ *     host memory. A stream is a hipStream_t passed as void* (NULL = the
+ *     null stream).
+ *   - The caller owns all device memory: weights, KV cache, workspace, canvas,
+ *     masks. The library never allocates device memory; it keeps the raw
+ *     pointers given to dg_create, which must stay valid until dg_destroy.
+ *     The dg_ctx itself is host memory owned by the library.
+ *   - Weights are bf16, row-major, in the [out][in] convention (y = x W^T).
+ *   - Every call validates its arguments and the cache capacity before it
+ *     enqueues anything; on DG_EINVAL / DG_ECAPACITY nothing has been
+ *     launched and no state changed. Work is enqueued asynchronously on the
+ *     given stream. A HIP launch error returns DG_EHIP and makes the context
+ *     sticky: every later call returns DG_ESTATE until dg_destroy.
+ *     dg_last_error() gives a message. No C++ exception crosses the ABI.
+ *   - One context per stream at a time; not thread-safe.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_EINVAL = -1,     /* bad argument or unsupported shape */
+  DG_ECAPACITY = -2,  /* KV cache or workspace too small for the call */
+  DG_EHIP = -3,       /* a HIP call failed; the context is now sticky */
+  DG_ESTATE = -4      /* the context is sticky after an earlier failure */
+} dg_status;
+
+/* Model shape and sampler constants.
+ * Supported shapes: head_dim in {64, 128}; d_model a multiple of 256, at most
+ * 4096;
+ * n_q_heads a multiple of n_kv_heads; (n_q_heads*head_dim) and
+ * (n_kv_heads*head_dim) multiples of 128; n_experts <= 128 and a multiple
+ * of 8; top_k <= 8; d_expert and d_shared multiples of 64; vocab a multiple
+ * of 256; canvas a multiple of 16, at most 1024.
+ * tau_first / tau_last: temperature at the first / last step, falling
+ * linearly (explainer §3.3: 0.8 -> 0.4). */
+typedef struct dg_config {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, d_expert, d_shared, vocab;
+  int32_t canvas;        /* C: tokens per block (explainer §3.2: 256) */
+  int32_t max_ctx;       /* KV rows per request and layer */
+  int32_t max_requests;  /* number of request slots in the KV cache */
+  int32_t max_rows;      /* largest number of rows one call processes */
+  float rms_eps, rope_theta, tau_first, tau_last;
+} dg_config;
+
+/* One layer's weights (device, bf16):
+ *   attn_norm [d]        w_qkv [(Hq+2Hkv)*dh][d]   (q heads, then k, then v)
+ *   w_o [d][Hq*dh]       moe_norm [d]              w_router [E][d]
+ *   w_gate, w_up [E][F][d]   w_down [E][d][F]
+ *   ws_gate, ws_up [Fs][d]   ws_down [d][Fs]       (shared expert)          */
+typedef struct dg_layer_weights {
+  const void *attn_norm, *w_qkv, *w_o, *moe_norm, *w_router;
+  const void *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
+} dg_layer_weights;
+
+/* embed [V][d] is also the LM head (tied); final_norm [d];
+ * layers: host array of n_layers entries (copied by dg_create). */
+typedef struct dg_weights {
+  const void *embed, *final_norm;
+  const dg_layer_weights *layers;
+} dg_weights;
+
+/* Per-position statistics of a denoising step (optional output). */
+typedef struct dg_row_stats {
+  float max_logit;   /* M_i = max_v L_iv */
+  float log_z;       /* log sum_v exp((L_iv - M_i) / tau_s) */
+  float held_logit;  /* L_i[x_i] for the token held before the step */
+  float conf;        /* c_i = log p_tau(candidate) */
+  int32_t argmax;    /* lowest v with L_iv = M_i */
+  int32_t accepted;  /* 1 if position i is in the accepted set */
+  int32_t pad[2];
+} dg_row_stats;
+
+/* Arguments of dg_init_canvas / dg_denoise_step.
+ *   n_req        number of requests in the batch (rows = n_req * canvas)
+ *   req          host [n_req]: KV-cache slot of each request (distinct)
+ *   d_canvas     device int32 [n_req][canvas], read and updated in place
+ *   d_committed  device uint8 [n_req][canvas], read and updated in place
+ *   step, n_steps  1 <= step <= n_steps (dg_init_canvas ignores them)
+ *   seed         host uint64 [n_req]: Philox key per request
+ *   block        host int32 [n_req]: block index (Philox counter word 2)
+ *   d_stats      optional device dg_row_stats [n_req][canvas] (NULL = none)
+ * Re-noise ids come from Philox4x32-10 (Salmon et al., SC'11) with
+ * key = (low, high 32 bits of seed[r]) and counter = (i, step, block[r],
+ * req[r]) for canvas position i of request r; id = (word0 * vocab) >> 32.
+ * dg_init_canvas uses step 0. */
+typedef struct dg_step_args {
+  int32_t n_req;
+  const int32_t *req;
+  int32_t *d_canvas;
+  uint8_t *d_committed;
+  int32_t step, n_steps;
+  const uint64_t *seed;
+  const int32_t *block;
+  dg_row_stats *d_stats;
+} dg_step_args;
+
+typedef struct dg_ctx dg_ctx;
+
+/* Bytes of KV cache for ONE request slot:
+ * n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2.
+ * Layout of the whole cache: [req][layer][K|V][kv_head][max_ctx][head_dim]
+ * bf16, K stored after RoPE. */
+size_t dg_kv_cache_bytes(const dg_config *cfg);
+
+/* Bytes of device workspace needed for calls of up to cfg->max_rows rows. */
+size_t dg_workspace_bytes(const dg_config *cfg);
+
+/* Validate cfg, copy the weight pointer table and bind the caller's KV cache
+ * (max_requests * dg_kv_cache_bytes) and workspace (dg_workspace_bytes).
+ * Every request slot starts empty (cache length 0). */
+dg_status dg_create(const dg_config *cfg, const dg_weights *w, void *d_kv_cache,
+                    void *d_workspace, size_t workspace_bytes, dg_ctx **out);
+void dg_destroy(dg_ctx *ctx);
+
+/* Causal prefill (aiboss88.com, "hybrid attention": prefill is causal and
+ * writes the KV cache): runs the encoder over d_ids[0..n) (device int32) at
+ * positions len..len+n-1 of slot req and appends their K/V rows.
+ * Needs len + n <= max_ctx (else DG_ECAPACITY). Processes the
+ * prompt in chunks of at most max_rows rows; the result equals one causal
+ * pass over the whole prompt. */
+dg_status dg_prefill(dg_ctx *ctx, void *stream, int32_t req, const int32_t *d_ids,
+                     int32_t n);
+
+/* Fill each canvas with uniform random ids (Philox step 0) and clear its
+ * committed mask (aiboss88.com: the canvas starts as random placeholders). */
+dg_status dg_init_canvas(dg_ctx *ctx, void *stream, const dg_step_args *a);
+
+/* One denoising step over n_req canvases (explainer §3.1-§3.3):
+ *   embed the canvas; for each layer: RMSNorm, QKV projection, RoPE at
+ *   positions len..len+C-1, attention of every canvas position over
+ *   [cached prefix ; canvas] with no mask, output projection + residual,
+ *   RMSNorm, router top-k softmax, token->expert permutation, grouped SwiGLU
+ *   experts plus the shared expert, weighted combine + residual;
+ *   final RMSNorm; tied LM head reduced per row to (max, argmax, log-sum-exp,
+ *   held-token logit) without materialising the logits; sampler:
+ *     tau_s = tau_first + (tau_last - tau_first) * (step-1)/(n_steps-1),
+ *     k_s   = floor(step * canvas / n_steps),
+ *     candidate y_i = x_i if committed else argmax_i,
+ *     c_i = (L_i[y_i] - M_i)/tau_s - log Z_i,
+ *     the k_s positions of highest c_i (ties: lower i) take y_i and are marked
+ *     committed; all others get a fresh uniform id and are cleared.
+ * The canvas K/V rows are written to cache rows [len, len+C) as scratch; the
+ * cache length does not change and rows [0, len) are only read.
+ * Needs len + C <= max_ctx for every request (else DG_ECAPACITY). */
+dg_status dg_denoise_step(dg_ctx *ctx, void *stream, const dg_step_args *a);
+
+/* Append finished blocks (explainer §3.2: each finished block is appended to
+ * the KV cache before the next block starts): the causal encoder pass over
+ * d_canvas [n_req][canvas] writes K/V rows [len, len+C) of each request's
+ * slot, then len += C. Needs len + C <= max_ctx (else DG_ECAPACITY). */
+dg_status dg_commit_block(dg_ctx *ctx, void *stream, int32_t n_req, const int32_t *req,
+                          const int32_t *d_canvas);
+
+/* Committed KV length of a request slot (host-side bookkeeping), or -1. */
+int32_t dg_cache_len(const dg_ctx *ctx, int32_t req);
+
+/* Forget a slot's cache (length 0). Does not touch device memory. */
+dg_status dg_reset(dg_ctx *ctx, int32_t req);
+
+/* Set a slot's committed length without running the encoder, for callers that
+ * fill the cache rows themselves (e.g. a restored snapshot of the cache). */
+dg_status dg_set_cache_len(dg_ctx *ctx, int32_t req, int32_t len);
+
+/* Last error message of the context ("" if none). */
+const char *dg_last_error(const dg_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

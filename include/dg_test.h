@@ -1,0 +1,89 @@
+/*
+ * dg_test.h - entry points that run parts of the denoising step on given
+ * inputs, so each stage can be compared with an independent implementation.
+ * They use the same kernels as dg_denoise_step; conventions as in dg.h.
+ */
+#ifndef DG_TEST_H
+#define DG_TEST_H
+
+#include "dg.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Byte offsets of the buffers inside the workspace (for inspection).
+ * rows = max_rows; E = n_experts; k = top_k.
+ *   h        fp32 [rows][d]          residual stream
+ *   u        bf16 [rows][d]          RMSNorm output (GEMM operand)
+ *   q        bf16 [rows][Hq][dh]     rotated queries
+ *   attn_o   bf16 [rows][Hq*dh]      attention output
+ *   z        fp32 [rows][E]          router logits
+ *   idx      int32 [rows][k]         selected experts (descending logit)
+ *   w        fp32 [rows][k]          softmax over the selected logits
+ *   wslot    int32 [rows*k]          t*k + j of each expert slot (index into w)
+ *   cnt      int32 [E]; off int32 [E+1]
+ *   items    int32 [2][260]          work-item offsets of the grouped expert
+ *                                    kernels (gate/up, then down) per group
+ *   perm     int32 [rows*k]          token of each expert slot
+ *   slot     int32 [rows][k]         slot of each (token, choice)
+ *   hid      bf16 [rows*k][F]        routed expert SwiGLU activations
+ *   hid_s    bf16 [rows][Fs]         shared expert SwiGLU activations
+ *   y        fp32 [rows*k][d]        routed expert outputs (weighted)
+ *   stats    dg_row_stats [rows]     per-row LM-head statistics          */
+typedef struct dg_ws_layout {
+  size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
+      slot, hid, hid_s, y, lm_part, stats, ids, total;
+} dg_ws_layout;
+
+dg_status dg_workspace_layout(const dg_config *cfg, dg_ws_layout *out);
+
+/* One layer over n rows of request slot req at positions len..len+n-1
+ * (len = dg_cache_len). d_h: device fp32 [n][d], input and output. causal=0:
+ * denoising attention (no mask inside the rows); causal=1: encoder attention.
+ * K/V rows are written to cache rows [len, len+n); the length is unchanged.
+ * Intermediates stay in the workspace (dg_workspace_layout). */
+dg_status dg_test_layer(dg_ctx *ctx, void *stream, int32_t req, int32_t layer, float *d_h,
+                        int32_t n, int32_t causal);
+
+/* Router top-k and permutation from given router logits d_z fp32 [rows][E]
+ * (device). Outputs (device, any may be NULL): idx [rows][k], w [rows][k],
+ * cnt [E], off [E+1], perm [rows*k], slot [rows][k]. */
+dg_status dg_test_route(dg_ctx *ctx, void *stream, const float *d_z, int32_t rows,
+                        int32_t *d_idx, float *d_w, int32_t *d_cnt, int32_t *d_off,
+                        int32_t *d_perm, int32_t *d_slot);
+
+/* Final RMSNorm, LM head statistics and sampler from a given residual stream
+ * d_h fp32 [n_req*canvas][d] (device), with the same arguments and effects on
+ * canvas / committed / stats as dg_denoise_step. */
+dg_status dg_test_head(dg_ctx *ctx, void *stream, const dg_step_args *a, const float *d_h);
+
+/* Per-stage timing. While enabled, every launch of a stage is bracketed by a
+ * pair of hipEvents recorded on the call's stream; dg_timing_read waits for
+ * the last recorded event, adds the elapsed times into ms[stage] and
+ * launches[stage] (arrays of n_stages >= DG_STAGE_COUNT entries, overwritten)
+ * and recycles the events. Stages: */
+enum {
+  DG_STAGE_EMBED = 0,   /* embedding gather (+ RoPE table) */
+  DG_STAGE_NORM,        /* RMSNorm */
+  DG_STAGE_QKV,         /* QKV projection + RoPE + KV write */
+  DG_STAGE_ATTN,        /* canvas attention (split keys + merge) */
+  DG_STAGE_OPROJ,       /* output projection + residual */
+  DG_STAGE_ROUTER,      /* router logits + top-k + softmax (fused) */
+  DG_STAGE_TOPK,        /* top-k from given logits (test entry point only) */
+  DG_STAGE_PERMUTE,     /* token -> expert permutation */
+  DG_STAGE_GATEUP,      /* grouped expert gate/up + SwiGLU (routed + shared) */
+  DG_STAGE_DOWN,        /* grouped expert down projection (routed + shared) */
+  DG_STAGE_COMBINE,     /* weighted combine + residual */
+  DG_STAGE_LMHEAD,      /* LM head with fused vocabulary statistics */
+  DG_STAGE_MERGE,       /* vocabulary statistics merge */
+  DG_STAGE_SAMPLER,     /* confidence sampler / initial canvas */
+  DG_STAGE_COUNT
+};
+dg_status dg_timing_enable(dg_ctx *ctx, int32_t enable);
+dg_status dg_timing_read(dg_ctx *ctx, double *ms, int32_t *launches, int32_t n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_TEST_H */

@@ -196,12 +196,16 @@ def moe(u: np.ndarray, idx: np.ndarray, w: np.ndarray, lw: Dict, n_experts: int,
 # ----------------------------------------------------------------------------
 
 def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np.ndarray,
-                  n_prefix: int, causal: bool, keep: Optional[Dict] = None):
+                  n_prefix: int, causal: bool, keep: Optional[Dict] = None,
+                  idx_override: Optional[np.ndarray] = None):
     """One pre-norm attention + MoE layer on n rows at positions n_prefix..n_prefix+n-1.
 
     cache_k, cache_v: [>= n_prefix, Hkv, dh] prefix rows (K already rotated).
     Returns (new h, k rows [n, Hkv, dh] rotated, v rows). `keep`, when given,
-    receives the intermediates by name.
+    receives the intermediates by name. `idx_override` (test harness only)
+    imposes the expert choice of another implementation, taken where its
+    router logits are tied within floating-point noise; the routing weights
+    are still the softmax of this oracle's own logits at those experts.
     """
     n, d = h.shape
     Hq, Hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -220,6 +224,11 @@ def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np
     u2 = rms_norm(h1, lw["moe_norm"], cfg.rms_eps)
     z = u2 @ f64(lw["w_router"]).T
     idx, w = route(z, cfg.top_k)
+    if idx_override is not None:
+        idx = np.asarray(idx_override, np.int64)
+        sel = np.take_along_axis(z, idx, axis=1)
+        ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+        w = ex / ex.sum(axis=1, keepdims=True)
     pinfo = permutation(idx, cfg.n_experts)
     h2 = h1 + moe(u2, idx, w, lw, cfg.n_experts, pinfo)
     if keep is not None:

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the headers declare, sizes its buffers as documented, and
+rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_discrete_diffusion_dg_amd import binding as B
+from block_discrete_diffusion_dg_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    for h in ("dg.h", "dg_test.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(dg_[a-z_0-9]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdg.so not built: run __graft_entry__.build()")
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SIGNATURES), set(names) ^ set(B.SIGNATURES)
+
+
+def _cfg(model=synth.FULL, max_ctx=4096, max_requests=2, max_rows=512, **kw):
+    c = B.DGConfig()
+    for name in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
+                 "d_expert", "d_shared", "vocab", "canvas"):
+        setattr(c, name, getattr(model, name))
+    c.max_ctx, c.max_requests, c.max_rows = max_ctx, max_requests, max_rows
+    c.rms_eps, c.rope_theta, c.tau_first, c.tau_last = 1e-6, 1e4, 0.8, 0.4
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_buffer_sizes(lib):
+    c = _cfg()
+    want_kv = 30 * 2 * 8 * 4096 * 128 * 2
+    assert lib.dg_kv_cache_bytes(ctypes.byref(c)) == want_kv
+    ws = lib.dg_workspace_bytes(ctypes.byref(c))
+    lay = B.DGWsLayout()
+    assert lib.dg_workspace_layout(ctypes.byref(c), ctypes.byref(lay)) == B.DG_OK
+    assert lay.total == ws > 0
+    offs = [getattr(lay, n) for n in B.WS_FIELDS[:-1]]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    assert ctypes.sizeof(B.DGRowStats) == 32
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("d_model", 1000), ("n_experts", 136),
+                                         ("top_k", 9), ("vocab", 1000), ("canvas", 24),
+                                         ("max_rows", 100), ("n_q_heads", 12), ("max_ctx", 300)])
+def test_unsupported_shapes_rejected(lib, field, value):
+    c = _cfg(**{field: value})
+    assert lib.dg_workspace_bytes(ctypes.byref(c)) == 0
+    w = B.DGWeights(1, 1, None)
+    h = ctypes.c_void_p()
+    assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 1, 1, 1 << 40, ctypes.byref(h)) == B.DG_EINVAL
+
+
+def _fake_ctx(lib, **kw):
+    """A context over fake device addresses: only host-side paths may run on it."""
+    c = _cfg(model=synth.TINY, max_ctx=256, max_requests=2, max_rows=64, **kw)
+    layers = (B.DGLayerWeights * c.n_layers)()
+    for i in range(c.n_layers):
+        for n in B.LAYER_FIELDS:
+            setattr(layers[i], n, 0x1000)
+    w = B.DGWeights(0x1000, 0x1000, layers)
+    h = ctypes.c_void_p()
+    ws = lib.dg_workspace_bytes(ctypes.byref(c))
+    assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws - 1,
+                         ctypes.byref(h)) == B.DG_ECAPACITY
+    assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws, ctypes.byref(h)) == B.DG_OK
+    return h
+
+
+def test_argument_and_capacity_errors_launch_nothing(lib):
+    h = _fake_ctx(lib)
+    try:
+        assert lib.dg_cache_len(h, 0) == 0 and lib.dg_cache_len(h, 5) == -1
+        # bad slot / negative length / null ids
+        assert lib.dg_prefill(h, None, 7, 0x2000, 10) == B.DG_EINVAL
+        assert lib.dg_prefill(h, None, 0, 0x2000, -1) == B.DG_EINVAL
+        assert lib.dg_prefill(h, None, 0, None, 10) == B.DG_EINVAL
+        # prompt beyond max_ctx (256): capacity error, length unchanged
+        assert lib.dg_prefill(h, None, 0, 0x2000, 257) == B.DG_ECAPACITY
+        assert lib.dg_cache_len(h, 0) == 0
+        assert b"max_ctx" in lib.dg_last_error(h)
+        # set_cache_len bounds
+        assert lib.dg_set_cache_len(h, 0, 257) == B.DG_ECAPACITY
+        assert lib.dg_set_cache_len(h, 0, 225) == B.DG_OK and lib.dg_cache_len(h, 0) == 225
+        # a block of 32 rows no longer fits: capacity error, nothing launched
+        req = (ctypes.c_int32 * 1)(0)
+        assert lib.dg_commit_block(h, None, 1, req, 0x2000) == B.DG_ECAPACITY
+        assert lib.dg_cache_len(h, 0) == 225
+        dup = (ctypes.c_int32 * 2)(1, 1)
+        assert lib.dg_commit_block(h, None, 2, dup, 0x2000) == B.DG_EINVAL
+        # step arguments
+        a = B.DGStepArgs()
+        reqs = (ctypes.c_int32 * 1)(1)
+        seeds = (ctypes.c_uint64 * 1)(0)
+        blocks = (ctypes.c_int32 * 1)(0)
+        a.n_req, a.req, a.seed, a.block = 1, reqs, seeds, blocks
+        a.d_canvas, a.d_committed = 0x3000, 0x4000
+        a.step, a.n_steps = 1, 4
+        lib.dg_set_cache_len(h, 1, 225)
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_ECAPACITY
+        lib.dg_set_cache_len(h, 1, 0)
+        a.step = 0
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        a.step = 5
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        a.n_req = 3  # 3 * 32 rows > max_rows 64
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_ECAPACITY
+        assert lib.dg_reset(h, 0) == B.DG_OK and lib.dg_cache_len(h, 0) == 0
+        assert lib.dg_reset(h, 9) == B.DG_EINVAL
+    finally:
+        lib.dg_destroy(h)

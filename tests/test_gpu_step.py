@@ -1,0 +1,136 @@
+"""Whole-loop parity on the tiny workload (1 layer, d 256, V 4096, C 32,
+prefix 64, 4 steps): prefill, initial canvas, every denoising step and the
+block commit, each compared with the float64 oracle. The oracle is
+teacher-forced with the GPU's KV cache and canvas state before each call so a
+near-tie decision cannot propagate; every comparison states its band."""
+import numpy as np
+import pytest
+import torch
+
+from block_discrete_diffusion_dg_amd import synth
+from block_discrete_diffusion_dg_amd.engine import stats_fields
+from oracle import model as om
+from tests.gpu_util import REL_TOL, make_engine, max_rel, say, tie_gap_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_request(eng, cfg, slot, length):
+    req = om.Request(cfg, eng.max_ctx)
+    kv = eng.kv_view()
+    for l in range(cfg.n_layers):
+        req.k[l, :length] = om.f64(kv[slot, l, 0, :, :length].permute(1, 0, 2).cpu())
+        req.v[l, :length] = om.f64(kv[slot, l, 1, :, :length].permute(1, 0, 2).cpu())
+    req.length = length
+    return req
+
+
+def test_tiny_block_loop_parity():
+    wl = synth.WORKLOADS["tiny"]
+    cfg, P, S = wl.model, wl.prefix, wl.n_steps
+    C = cfg.canvas
+    eng, hw = make_engine(cfg, max_ctx=P + 2 * C)
+    prompt = synth.make_prompt(P, cfg.vocab, wl.seed)
+    say("[tiny] prefill")
+    eng.prefill(0, prompt.cuda())
+    torch.cuda.synchronize()
+    assert eng.cache_len(0) == P
+    ref = om.Request(cfg, eng.max_ctx)
+    om.prefill(hw, cfg, ref, prompt.numpy().astype(np.int64))
+    gpu_req = _oracle_request(eng, cfg, 0, P)
+    assert max_rel(gpu_req.k[:, :P], ref.k[:, :P]) <= REL_TOL
+    assert max_rel(gpu_req.v[:, :P], ref.v[:, :P]) <= REL_TOL
+    kv_prefix = eng.kv_view()[0, :, :, :, :P].clone()
+
+    x = torch.empty(C, dtype=torch.int32, device="cuda")
+    m = torch.empty(C, dtype=torch.uint8, device="cuda")
+    seed, block = 1234, 0
+    eng.init_canvas([0], x, m, [seed], [block])
+    x0, m0 = om.init_canvas(seed, block, 0, C, cfg.vocab)
+    assert np.array_equal(x.cpu().numpy(), x0) and not m.cpu().numpy().any()
+
+    for s in range(1, S + 1):
+        say(f"[tiny] step {s}")
+        x_in = x.cpu().numpy().astype(np.int64)
+        m_in = m.cpu().numpy()
+        stats = eng.new_stats(1)
+        eng.denoise_step([0], x, m, s, S, [seed], [block], stats)
+        torch.cuda.synchronize()
+        st = stats_fields(stats)
+        keep = {}
+        xo, mo = om.denoise_step(hw, cfg, gpu_req, x_in, m_in, s, S, seed, block, 0, keep)
+        big = np.abs(keep["logits"]).max()
+        assert max_rel(st["max_logit"], keep["M"]) <= REL_TOL
+        clear = np.array([tie_gap_ok(keep["logits"][i], 1, 2 * REL_TOL * big) for i in range(C)])
+        assert np.array_equal(st["argmax"].numpy()[clear], keep["a"][clear])
+        assert np.abs(st["conf"].double().numpy() - keep["c"]).max() <= REL_TOL * big / keep["tau"] * 4
+        k_s = om.commit_count(s, S, C)
+        acc = st["accepted"].numpy().astype(bool)
+        assert acc.sum() == k_s == m.cpu().numpy().sum()
+        if tie_gap_ok(keep["c"], k_s, REL_TOL * big / keep["tau"] * 4) and clear.all():
+            assert np.array_equal(acc, keep["accept"])
+            assert np.array_equal(x.cpu().numpy(), xo)
+        # the KV cache is only read by a denoising step
+        assert torch.equal(eng.kv_view()[0, :, :, :, :P], kv_prefix)
+        assert eng.cache_len(0) == P
+    assert m.cpu().numpy().all()
+
+    say("[tiny] commit")
+    final = x.clone()
+    eng.commit_block([0], final)
+    torch.cuda.synchronize()
+    assert eng.cache_len(0) == P + C
+    assert torch.equal(eng.kv_view()[0, :, :, :, :P], kv_prefix)  # committed rows never rewritten
+    om.commit_block(hw, cfg, gpu_req, final.cpu().numpy().astype(np.int64))
+    after = _oracle_request(eng, cfg, 0, P + C)
+    assert max_rel(after.k[:, P:P + C], gpu_req.k[:, P:P + C]) <= REL_TOL
+    assert max_rel(after.v[:, P:P + C], gpu_req.v[:, P:P + C]) <= REL_TOL
+
+
+def test_prefill_chunking_and_commit_are_causally_consistent():
+    cfg = synth.TINY
+    C = cfg.canvas
+    n = 3 * C + 7  # ragged: several chunks of max_rows=C rows plus a tail
+    eng, hw = make_engine(cfg, max_ctx=n + C + 2 * C, max_requests=3, max_rows=C)
+    ids = synth.make_prompt(n + C, cfg.vocab, 9).cuda()
+    eng.prefill(0, ids)                       # whole sequence, chunked by the library
+    eng.prefill(1, ids[:n].contiguous())      # prefix only ...
+    eng.commit_block([1], ids[n:].contiguous())  # ... then the block as a commit
+    torch.cuda.synchronize()
+    assert eng.cache_len(0) == eng.cache_len(1) == n + C
+    kv = eng.kv_view()
+    a = kv[0, :, :, :, :n + C].float().cpu().numpy()
+    b = kv[1, :, :, :, :n + C].float().cpu().numpy()
+    assert max_rel(b, a) <= REL_TOL
+    ref = om.Request(cfg, n + 3 * C)
+    om.prefill(hw, cfg, ref, ids.cpu().numpy().astype(np.int64))
+    got = _oracle_request(eng, cfg, 0, n + C)
+    assert max_rel(got.k[:, :n + C], ref.k[:, :n + C]) <= REL_TOL
+    assert max_rel(got.v[:, :n + C], ref.v[:, :n + C]) <= REL_TOL
+
+
+def test_step_is_deterministic_and_batch_matches_single():
+    cfg = synth.TINY
+    C = cfg.canvas
+    eng, hw = make_engine(cfg, max_ctx=64 + 2 * C, max_requests=2, max_rows=2 * C)
+    for slot in (0, 1):
+        eng.prefill(slot, synth.make_prompt(64, cfg.vocab, 5 + slot).cuda())
+    x = torch.empty(2 * C, dtype=torch.int32, device="cuda")
+    m = torch.empty(2 * C, dtype=torch.uint8, device="cuda")
+    eng.init_canvas([0, 1], x, m, [1, 2], [0, 0])
+    outs = []
+    for _ in range(2):
+        xx, mm = x.clone(), m.clone()
+        st = eng.new_stats(2)
+        eng.denoise_step([0, 1], xx, mm, 2, 4, [1, 2], [0, 0], st)
+        outs.append((xx.cpu(), mm.cpu(), st.cpu()))
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[1]))
+    # request 1 alone gives the same statistics (tolerance: its attention split may differ)
+    x1, m1 = x[C:].clone(), m[C:].clone()
+    st1 = eng.new_stats(1)
+    eng.denoise_step([1], x1, m1, 2, 4, [2], [0], st1)
+    torch.cuda.synchronize()
+    a = stats_fields(outs[0][2][C:])
+    b = stats_fields(st1)
+    assert max_rel(b["max_logit"], a["max_logit"]) < 1e-4
+    assert torch.equal(a["argmax"], b["argmax"])
