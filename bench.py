@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--workload", default="full", choices=["full", "long", "batch", "tiny", "one_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy this many MiB device-to-device with a plain copy "
+                         "kernel (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoising step "
@@ -246,6 +249,20 @@ def main():
         log("cpu baseline: timing the oracle on a sample of the step")
         out["cpu_baseline"] = cpu_baseline(eng, hw, cfg, canvas0[:C], P,
                                            min(args.cpu_layers, cfg.n_layers), 1, S)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        dst.copy_(src)
+        p1.record(stream)
+        torch.cuda.synchronize()
+        out["copy_probe"] = {"bytes_read": n, "bytes_written": n, "ms": round(p0.elapsed_time(p1), 4),
+                             "GB_s_read_plus_write": round(2 * n / (p0.elapsed_time(p1) * 1e-3) / 1e9, 1)}
     print(json.dumps(out), flush=True)
 
 

@@ -46,7 +46,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.wslot = take(R * k * 4);
   L.cnt = take(256 * 4);
   L.off = take(257 * 4);
-  L.items = take(2 * 260 * 4);
+  L.items = take(2 * 260 * 4 + 64);  // item offsets (gate/up, down), then two queue heads
   L.perm = take(R * k * 4);
   L.slot = take(R * k * 4);
   L.hid = take(R * k * c.d_expert * 2);
@@ -195,21 +195,22 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
                                                  c->buf<float>(L.w)));
   int32_t* items_gu = c->buf<int32_t>(L.items);
   int32_t* items_dn = items_gu + 260;
+  int32_t* queues = items_gu + 520;
   const int ch = moe_rows_per_chunk(rows, g.n_experts, g.top_k);
   STAGE(DG_STAGE_PERMUTE, launch_permute(s, c->buf<int32_t>(L.idx), rows, g.n_experts, g.top_k, ch,
                                          g.d_expert / 64, g.d_shared / 64, d / 64, c->buf<int32_t>(L.cnt),
                                          c->buf<int32_t>(L.off), c->buf<int32_t>(L.perm),
                                          c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items_gu,
-                                         items_dn));
+                                         items_dn, queues));
   STAGE(DG_STAGE_GATEUP, launch_moe_gateup(s, u, rows, d, c->buf<int32_t>(L.perm), c->buf<int32_t>(L.cnt),
-                                           c->buf<int32_t>(L.off), items_gu, w.w_gate, w.w_up,
+                                           c->buf<int32_t>(L.off), items_gu, queues, w.w_gate, w.w_up,
                                            g.d_expert, g.n_experts, g.top_k, w.ws_gate, w.ws_up,
                                            g.d_shared, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s)));
   float* y = c->buf<float>(L.y);
   float* ys = y + (size_t)g.max_rows * g.top_k * d;
   STAGE(DG_STAGE_DOWN, launch_moe_down(s, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s), rows, d,
                                        c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<float>(L.w),
-                                       c->buf<int32_t>(L.wslot), items_dn, w.w_down, g.d_expert,
+                                       c->buf<int32_t>(L.wslot), items_dn, queues + 1, w.w_down, g.d_expert,
                                        g.n_experts, g.top_k, w.ws_down, g.d_shared, y, ys));
   STAGE(DG_STAGE_COMBINE, launch_moe_combine(s, h, ys, y, c->buf<int32_t>(L.slot), rows, d, g.top_k,
                                              next_gain, g.rms_eps, u));
@@ -498,7 +499,7 @@ dg_status dg_test_route(dg_ctx* c, void* stream, const float* d_z, int32_t rows,
   launch_permute(s, c->buf<int32_t>(L.idx), rows, E, k, moe_rows_per_chunk(rows, E, k), g.d_expert / 64,
                  g.d_shared / 64, g.d_model / 64, c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off),
                  c->buf<int32_t>(L.perm), c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items_gu,
-                 items_gu + 260);
+                 items_gu + 260, items_gu + 520);
   auto cp = [&](void* dst, size_t off, size_t bytes) {
     if (dst) (void)hipMemcpyAsync(dst, c->ws + off, bytes, hipMemcpyDeviceToDevice, s);
   };

@@ -13,7 +13,6 @@
 namespace {
 
 constexpr int DMT = 2;  // rows per chunk = 32
-constexpr int DBK = 128;
 
 __device__ __forceinline__ void tile_coords(int NT, int MC, int& nt, int& mc) {
   const int b = blockIdx.x;
@@ -36,7 +35,7 @@ struct QkvArgs {
 
 __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, int rows, int d,
                                                   const bf16_t* __restrict__ w, QkvArgs p) {
-  using T = StreamTile<DMT, DBK>;
+  using T = StreamTile<DMT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
   const int dh = p.dh, half = dh >> 1;
   const int NT = (p.Hq + 2 * p.Hkv) * half / 64, MC = div_up(rows, T::CH);
@@ -48,7 +47,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
   const int64_t r0 = (int64_t)head * dh + j;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 a0[DMT], a1[DMT];
-  stream_tile<DMT, DBK, true>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
+  stream_tile<DMT, true>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
   const bool rotate = head < p.Hq + p.Hkv;
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
 __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a, int rows, int K,
                                                     const bf16_t* __restrict__ w, int N,
                                                     float* __restrict__ h) {
-  using T = StreamTile<DMT, DBK>;
+  using T = StreamTile<DMT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
   const int NT = N / 64, MC = div_up(rows, T::CH);
   int nt, mc;
@@ -93,7 +92,7 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
   const int col = nt * 64 + wave * 16 + l16;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 acc[DMT], unused[DMT];
-  stream_tile<DMT, DBK, false>(a, K, nullptr, row0, nrows, w + (int64_t)col * K, nullptr, K, acc, unused,
+  stream_tile<DMT, false>(a, K, nullptr, row0, nrows, w + (int64_t)col * K, nullptr, K, acc, unused,
                                lds);
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
@@ -111,11 +110,11 @@ void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w
                 const ReqTable& rt) {
   QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt};
   const int NT = (Hq + 2 * Hkv) * (dh / 2) / 64;
-  const int MC = div_up(rows, StreamTile<DMT, DBK>::CH);
+  const int MC = div_up(rows, StreamTile<DMT>::CH);
   hipLaunchKernelGGL(qkv_kernel, dim3(NT * MC), dim3(256), 0, s, u, rows, d, w, p);
 }
 
 void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h) {
-  const int MC = div_up(rows, StreamTile<DMT, DBK>::CH);
+  const int MC = div_up(rows, StreamTile<DMT>::CH);
   hipLaunchKernelGGL(resid_kernel, dim3((N / 64) * MC), dim3(256), 0, s, a, rows, K, w, N, h);
 }

@@ -2,6 +2,8 @@
 // logits, then the token -> expert permutation (counting sort by expert,
 // tokens ascending inside an expert) built with wave ballots and a
 // wave-level prefix sum.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -73,71 +75,121 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
   wave_topk(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
 }
 
-// MoE pre-norm, router logits and top-k for one token row per work-group:
-//   u = bf16(RMSNorm(h) * g)        (also the experts' input rows)
-//   z[e] = u . W_r[e]               (fp32; wave w takes experts w, w+4, ...,
-//                                    each lane 1/64 of the row, then a
-//                                    wave-level sum)
-//   top-k of z with softmax weights (wave_topk).
+// MoE pre-norm, router logits and top-k for 8 token rows per work-group.
+//  1. RMSNorm: wave w normalises rows 2w and 2w+1; u goes to the workspace
+//     (the experts' input rows) and to an LDS tile (bf16, [8][d + 8]).
+//  2. z = u W_r^T on the matrix cores: wave w reduces over its quarter of d
+//     for all experts (8 subtiles of 16 experts, indices clamped to E-1; the
+//     A rows 8..15 repeat rows 0..7 and are discarded).
+//  3. z = sum of the four partial sums (fixed order); wave w selects the
+//     experts of rows 2w and 2w+1 (wave_topk).
+constexpr int RT_ROWS = 8;
+
 __global__ __launch_bounds__(256) void norm_router_topk_kernel(
-    const float* __restrict__ h, const bf16_t* __restrict__ gain, int d, float eps,
+    const float* __restrict__ h, const bf16_t* __restrict__ gain, int rows, int d, float eps,
     const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
     int32_t* __restrict__ idx, float* __restrict__ w) {
-  extern __shared__ float sh[];  // u as fp32 [d], then z [E]
-  __shared__ float red[4];
-  float* us = sh;
-  float* zl = sh + d;
-  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* x = h + (int64_t)row * d;
-  float ss = 0.f;
-  for (int c = tid * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
-  bf16_t* uo = u + (int64_t)row * d;
-  for (int c = tid * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(x + c);
-    const bf16_t b0 = f2bf(v.x * inv * bf2f(gain[c])), b1 = f2bf(v.y * inv * bf2f(gain[c + 1]));
-    const bf16_t b2 = f2bf(v.z * inv * bf2f(gain[c + 2])), b3 = f2bf(v.w * inv * bf2f(gain[c + 3]));
-    *reinterpret_cast<u32x2*>(uo + c) =
-        u32x2{(uint32_t)b0 | ((uint32_t)b1 << 16), (uint32_t)b2 | ((uint32_t)b3 << 16)};
-    us[c] = bf2f(b0);
-    us[c + 1] = bf2f(b1);
-    us[c + 2] = bf2f(b2);
-    us[c + 3] = bf2f(b3);
-  }
-  __syncthreads();
-  const int per = d / 64;  // elements of the row per lane (multiple of 4)
-  for (int e = wave; e < E; e += 4) {
-    const bf16_t* wrow = wr + (int64_t)e * d + lane * per;
-    const float* ur = us + lane * per;
-    float acc = 0.f;
-    for (int j = 0; j < per; j += 4) {
-      const u32x2 wv = *reinterpret_cast<const u32x2*>(wrow + j);
-      acc += ur[j] * __uint_as_float(wv.x << 16);
-      acc += ur[j + 1] * __uint_as_float(wv.x & 0xffff0000u);
-      acc += ur[j + 2] * __uint_as_float(wv.y << 16);
-      acc += ur[j + 3] * __uint_as_float(wv.y & 0xffff0000u);
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) {
-      zl[e] = acc;
-      z[(int64_t)row * E + e] = acc;
+  extern __shared__ __align__(16) char rt_lds[];
+  const int LDU = d + 8;
+  bf16_t* Us = reinterpret_cast<bf16_t*>(rt_lds);   // [8][LDU]
+  float* part = reinterpret_cast<float*>(rt_lds);   // after phase 2: [4][8][E], then z [8][E]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int t0 = blockIdx.x * RT_ROWS;
+
+  for (int i = 0; i < 2; ++i) {
+    const int rr = wave * 2 + i, t = t0 + rr;
+    bf16_t* urow = Us + rr * LDU;
+    if (t < rows) {
+      const float* x = h + (int64_t)t * d;
+      float ss = 0.f;
+      for (int c = lane * 4; c < d; c += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(x + c);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+      for (int c = lane * 4; c < d; c += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(x + c);
+        const u32x2 pk = {pack_bf16x2(v.x * inv * bf2f(gain[c]), v.y * inv * bf2f(gain[c + 1])),
+                          pack_bf16x2(v.z * inv * bf2f(gain[c + 2]), v.w * inv * bf2f(gain[c + 3]))};
+        *reinterpret_cast<u32x2*>(u + (int64_t)t * d + c) = pk;
+        *reinterpret_cast<u32x2*>(urow + c) = pk;
+      }
+    } else {
+      for (int c = lane * 4; c < d; c += 256) *reinterpret_cast<u32x2*>(urow + c) = u32x2{0u, 0u};
     }
   }
   __syncthreads();
-  if (wave == 0) {
+
+  const int kq = d / 4, kb = wave * kq;
+  const bf16_t* arow = Us + (l16 & 7) * LDU + kb + 8 * grp;
+  const bf16_t* brow[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) brow[n] = wr + (int64_t)min(16 * n + l16, E - 1) * d + kb + 8 * grp;
+  f32x4 acc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Weight loads run two 32-wide steps ahead (three register sets, loop
+  // unrolled by three; steps past the end reload the last step and are
+  // multiplied by a zeroed A operand).
+  const int nk = kq / 32;
+  u32x4 b[3][8];
+  auto issue = [&](auto S, int st) {
+    constexpr int s = decltype(S)::value;
+    const int k0 = min(st, nk - 1) * 32;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) b[s][n] = ld16(brow[n] + k0);
+  };
+  auto compute = [&](auto S, int st) {
+    constexpr int s = decltype(S)::value;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 a0 = ld16(arow + min(st, nk - 1) * 32);
+    const u32x4 a = st < nk ? a0 : zero;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = mfma_bf16(a, b[s][n], acc[n]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue(I0{}, 0);
+  issue(I1{}, 1);
+  for (int it = 0; it < nk; it += 3) {
+    issue(I2{}, it + 2);
+    compute(I0{}, it);
+    issue(I0{}, it + 3);
+    compute(I1{}, it + 1);
+    issue(I1{}, it + 4);
+    compute(I2{}, it + 2);
+  }
+  __syncthreads();  // the u tile is no longer read: reuse the LDS for partial sums
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int e = 16 * n + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = 4 * grp + r;  // rows 0..15 of the MFMA tile; 8..15 are repeats
+      if (rr < RT_ROWS && e < E) part[(wave * RT_ROWS + rr) * E + e] = acc[n][r];
+    }
+  }
+  __syncthreads();
+  float* zl = part + 4 * RT_ROWS * E;
+  for (int i = tid; i < RT_ROWS * E; i += 256) {
+    const float v = part[i] + part[RT_ROWS * E + i] + part[2 * RT_ROWS * E + i] + part[3 * RT_ROWS * E + i];
+    zl[i] = v;
+    const int t = t0 + i / E;
+    if (t < rows) z[(int64_t)t * E + (i % E)] = v;
+  }
+  __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const int rr = wave * 2 + i, t = t0 + rr;
+    if (t >= rows) break;
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? zl[e] : -INFINITY;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = e < E ? zl[rr * E + e] : -INFINITY;
     }
-    wave_topk(v, E, k, lane, idx + (int64_t)row * k, w + (int64_t)row * k);
+    wave_topk(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
   }
 }
 
@@ -183,7 +235,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ slot,
                                                        int32_t* __restrict__ widx,
                                                        int32_t* __restrict__ items_gu,
-                                                       int32_t* __restrict__ items_dn) {
+                                                       int32_t* __restrict__ items_dn,
+                                                       int32_t* __restrict__ queues) {
   extern __shared__ uint32_t dyn[];  // bits [rows][ceil(E/32)], then choices [rows*k] bytes
   __shared__ int32_t s_cnt[257];
   __shared__ int32_t s_off[258];
@@ -227,6 +280,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     off[e] = s_off[e];
   }
   if (tid == 0) off[E] = s_off[E];
+  if (tid < 2) queues[tid] = 0;  // work-queue heads of the two expert kernels
   for (int g = tid; g <= E + 1; g += 1024) {
     items_gu[g] = s_igu[g];
     items_dn[g] = s_idn[g];
@@ -260,17 +314,19 @@ void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t*
 
 void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
                              const bf16_t* wr, int E, int k, bf16_t* u, float* z, int32_t* idx, float* w) {
-  const size_t lds = (size_t)(d + E) * sizeof(float);
-  hipLaunchKernelGGL(norm_router_topk_kernel, dim3(rows), dim3(256), lds, s, h, gain, d, eps, wr, E, k, u, z,
-                     idx, w);
+  const size_t tile = (size_t)RT_ROWS * (d + 8) * sizeof(bf16_t);
+  const size_t sums = (size_t)5 * RT_ROWS * E * sizeof(float);
+  const size_t lds = tile > sums ? tile : sums;
+  hipLaunchKernelGGL(norm_router_topk_kernel, dim3(div_up(rows, RT_ROWS)), dim3(256), lds, s, h, gain, rows, d,
+                     eps, wr, E, k, u, z, idx, w);
 }
 
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
                     int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
-                    int32_t* widx, int32_t* items_gu, int32_t* items_dn) {
+                    int32_t* widx, int32_t* items_gu, int32_t* items_dn, int32_t* queues) {
   const size_t lds = permute_lds_bytes(rows, E, k);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, idx, rows, E, k, ch, ft_routed, ft_shared,
-                     dt, cnt, off, perm, slot, widx, items_gu, items_dn);
+                     dt, cnt, off, perm, slot, widx, items_gu, items_dn, queues);
 }
 
 size_t permute_lds_bytes(int rows, int E, int k) {

@@ -7,24 +7,30 @@
 // GATED the lane also owns a second weight row (the "up" row of a SwiGLU, or
 // the rotate-half partner of a RoPE pair) and a second accumulator.
 //
-// The A rows (optionally gathered through a row map) are staged per K-step in
-// a double-buffered LDS tile shared by the four waves. The next K-step's A
-// and B loads are issued before the current step's MFMAs; one barrier per
-// step.
+// Pipeline: K advances in steps of BK = 64. Loads run two steps ahead of the
+// matrix cores: while step it is multiplied, the loads of steps it+1 and
+// it+2 are in flight (three register sets for the weights and for the A
+// staging; a double-buffered LDS tile for A, shared by the four waves). HBM
+// latency is paid once per tile, not once per step. The loop is unrolled by
+// three so every register set has a static index; steps past the end reload
+// the last step (in-bounds, branch-free) and their weight operands are
+// zeroed, so the matrix-core instructions never sit under control flow.
 //
-// Reduction-index assignment per K-step of BK: lane group g, MFMA step s
-// uses k0 + g*(BK/4) + 8s .. +7 for both operands, so each lane reads BK/2
-// contiguous bytes of its weight row per step.
+// Reduction-index assignment per K-step: lane group g, MFMA step q in {0,1}
+// uses k0 + 16g + 8q .. +7 for both operands (each lane reads 32 contiguous
+// bytes of its weight row per step).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
-template <int MT, int BK>
+template <int MT>
 struct StreamTile {
-  static constexpr int CH = 16 * MT;          // rows per chunk
-  static constexpr int LDA = BK + 8;          // padded LDS row (bf16)
-  static constexpr int S = BK / 32;           // MFMA steps per K-step
-  static constexpr int ACH = CH * BK / 8 / 256;  // 16-byte A chunks per thread
+  static constexpr int BK = 64;
+  static constexpr int CH = 16 * MT;             // rows per chunk
+  static constexpr int LDA = BK + 8;             // padded LDS row (bf16)
+  static constexpr int ACH = CH * BK / 8 / 256;  // 16-byte A chunks per thread and step
   static constexpr int LDS_ELEMS = 2 * CH * LDA;
   static_assert(ACH >= 1, "tile too small for 256 threads");
 };
@@ -33,23 +39,21 @@ struct StreamTile {
 // row = row0 + 16*mt + 4*(lane/16) + r of the chunk, against the lane's
 // weight row(s) w0 (w1). A row i of the chunk is A + map(row0 + i) * lda with
 // map = rowmap or identity. Rows past nrows repeat the chunk's first row; their
-// accumulators are meaningless and must not be stored.
-template <int MT, int BK, bool GATED>
+// accumulators are meaningless and must not be stored. K % 64 == 0.
+template <int MT, bool GATED>
 __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
                                             const int32_t* __restrict__ rowmap, int row0, int nrows,
                                             const bf16_t* __restrict__ w0,
                                             const bf16_t* __restrict__ w1, int K,
                                             f32x4 (&acc0)[MT], f32x4 (&acc1)[MT], bf16_t* lds) {
-  using T = StreamTile<MT, BK>;
-  constexpr int S = T::S, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
+  using T = StreamTile<MT>;
+  constexpr int BK = T::BK, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int kl = grp * (BK / 4);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Rows past nrows re-read the chunk's first row (branch-free loads; their
-  // results are never stored).
   const bf16_t* arow[ACH];
   int aoff[ACH];
 #pragma unroll
@@ -60,58 +64,68 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     arow[i] = A + (int64_t)row * lda + kc;
     aoff[i] = r * LDA + kc;
   }
-  u32x4 ra[ACH];
-  u32x4 b0[2][S], b1[2][S];
+  const int nk = K / BK;
 
-  auto loadA = [&](int k0) {
+  u32x4 ra[3][ACH];
+  u32x4 b0[3][2], b1[3][2];
+
+  // loads of step st (clamped to the last step) into register set S
+  auto issue = [&](auto S, int st) {
+    constexpr int s = decltype(S)::value;
+    const int k0 = min(st, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = ld16(arow[i] + k0);
-  };
-  auto storeA = [&](int buf) {
+    for (int i = 0; i < ACH; ++i) ra[s][i] = ld16(arow[i] + k0);
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(lds + buf * CH * LDA + aoff[i]) = ra[i];
-  };
-  auto loadB = [&](int buf, int k0) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      b0[buf][s] = ld16(w0 + k0 + kl + 8 * s);
-      if (GATED) b1[buf][s] = ld16(w1 + k0 + kl + 8 * s);
+    for (int q = 0; q < 2; ++q) {
+      b0[s][q] = ld16(w0 + k0 + kl + 8 * q);
+      if (GATED) b1[s][q] = ld16(w1 + k0 + kl + 8 * q);
     }
   };
-  auto compute = [&](int buf) {
-    const bf16_t* As = lds + buf * CH * LDA;
+  auto stage = [&](auto S, int buf) {
+    constexpr int s = decltype(S)::value;
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(lds + buf * CH * LDA + aoff[i]) = ra[s][i];
+  };
+  auto compute = [&](auto S, int buf, int st) {
+    constexpr int s = decltype(S)::value;
+    const bool live = st < nk;  // past the end: weight operands zeroed
+    const bf16_t* As = lds + buf * CH * LDA;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const u32x4 bq0 = live ? b0[s][q] : zero;
+      const u32x4 bq1 = live ? b1[s][q] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 a = ld16(As + (16 * mt + l16) * LDA + kl + 8 * s);
-        acc0[mt] = mfma_bf16(a, b0[buf][s], acc0[mt]);
-        if (GATED) acc1[mt] = mfma_bf16(a, b1[buf][s], acc1[mt]);
+        const u32x4 a = ld16(As + (16 * mt + l16) * LDA + kl + 8 * q);
+        acc0[mt] = mfma_bf16(a, bq0, acc0[mt]);
+        if (GATED) acc1[mt] = mfma_bf16(a, bq1, acc1[mt]);
       }
+    }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
-  const int nk = K / BK;
-  loadA(0);
-  loadB(0, 0);
-  storeA(0);
+  issue(I0{}, 0);
+  issue(I1{}, 1);
+  stage(I0{}, 0);
   __syncthreads();
-  for (int it = 0; it < nk; it += 2) {
-    const bool more1 = it + 1 < nk;
-    if (more1) {
-      loadA((it + 1) * BK);
-      loadB(1, (it + 1) * BK);
-    }
-    compute(0);
-    if (more1) storeA(1);
+  // Step it multiplies LDS buffer it&1 with weight set it%3. Before it, the
+  // loads of step it+2 are issued into set (it+2)%3; after it, step it+1's A
+  // (set (it+1)%3) moves into LDS buffer (it+1)&1, last read by step it-1.
+  for (int it = 0; it < nk; it += 3) {
+    issue(I2{}, it + 2);
+    compute(I0{}, it & 1, it);
+    stage(I1{}, (it + 1) & 1);
     __syncthreads();
-    if (!more1) break;
-    const bool more2 = it + 2 < nk;
-    if (more2) {
-      loadA((it + 2) * BK);
-      loadB(0, (it + 2) * BK);
-    }
-    compute(1);
-    if (more2) storeA(0);
+    issue(I0{}, it + 3);
+    compute(I1{}, (it + 1) & 1, it + 1);
+    stage(I2{}, it & 1);
+    __syncthreads();
+    issue(I1{}, it + 4);
+    compute(I2{}, it & 1, it + 2);
+    stage(I0{}, (it + 1) & 1);
     __syncthreads();
   }
 }
