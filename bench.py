@@ -32,11 +32,13 @@ def log(*a):
 
 
 def algorithmic_model(cfg, prefix, rows, touched_experts):
-    """Bytes and flops per kernel class that one denoising step must move / do.
+    """Bytes and flops per kernel class (per launch) that one denoising step
+    must move / do.
 
-    Weights: only the touched experts, plus attention, router, shared expert
-    weights and the tied LM head, each read once; the prefix + canvas KV read
-    once per layer; activations ignored (< 1% of the bytes).
+    Weights: only the touched experts (the measured mean over the timed
+    layers), plus attention, router, shared expert weights and the tied LM
+    head, each read once; the prefix + canvas KV read once per layer;
+    activations ignored (< 1% of the bytes).
     """
     d, E, F, Fs, V = cfg.d_model, cfg.n_experts, cfg.d_expert, cfg.d_shared, cfg.vocab
     L, Hq, Hkv, dh, k = cfg.n_layers, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.top_k
@@ -46,9 +48,8 @@ def algorithmic_model(cfg, prefix, rows, touched_experts):
         "attn": (nk * Hkv * dh * 2 * 2, 4 * rows * Hq * nk * dh),
         "oproj": (d * Hq * dh * 2, 2 * rows * d * Hq * dh),
         "router": (E * d * 2, 2 * rows * E * d),
-        "gateup": (touched_experts * 2 * F * d * 2 + 2 * Fs * d * 2,
-                   2 * rows * k * 2 * F * d + 2 * rows * 2 * Fs * d),
-        "down": (touched_experts * F * d * 2 + Fs * d * 2, 2 * rows * k * F * d + 2 * rows * Fs * d),
+        "experts": (touched_experts * 3 * F * d * 2 + 3 * Fs * d * 2,
+                    2 * rows * k * 3 * F * d + 2 * rows * 3 * Fs * d),
     }
     per_step = {name: (b * L, f * L) for name, (b, f) in kinds.items()}
     per_step["lmhead"] = (V * d * 2, 2 * rows * V * d)
@@ -174,6 +175,7 @@ def main():
     run(args.warmup, 0)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
+    moe0 = eng.moe_counters()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -185,11 +187,20 @@ def main():
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
+    moe1 = eng.moe_counters()
+    if moe1["spin_timeouts"] != moe0["spin_timeouts"]:
+        raise RuntimeError("expert kernel waits ran out during the timed steps")
+    touched = (moe1["touched_total"] - moe0["touched_total"]) / max(1, moe1["permute_calls"] - moe0["permute_calls"])
 
     # per-stage durations: a second pass with per-launch events on the same stream
     eng.timing(True)
+    moe2 = eng.moe_counters()
     run(args.steps, args.warmup + args.steps)
     stages = eng.timing_read()
+    moe3 = eng.moe_counters()
+    # mean touched experts per layer over the launches the stage timing covers
+    touched_staged = (moe3["touched_total"] - moe2["touched_total"]) / max(
+        1, moe3["permute_calls"] - moe2["permute_calls"])
     eng.timing(False)
     stage_ms = {k: v[0] / args.steps for k, v in stages.items() if v[1]}
     launches = {k: v[1] // args.steps for k, v in stages.items() if v[1]}
@@ -205,13 +216,11 @@ def main():
     for r in reqs:
         eng.set_cache_len(r, P)
 
-    cnt = eng.ws_view("cnt", torch.int32, (cfg.n_experts,)).cpu().numpy()
-    touched = int((cnt > 0).sum())
     kinds, per_step = algorithmic_model(cfg, P, rows, touched)
     t_roof = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in per_step.values())
-    b_gu, f_gu = kinds["gateup"]
-    gu_launch_ms = stages["gateup"][0] / max(1, stages["gateup"][1])
-    achieved = b_gu / (gu_launch_ms * 1e-3)
+    b_ex, f_ex = algorithmic_model(cfg, P, rows, touched_staged)[0]["experts"]
+    ex_launch_ms = stages["experts"][0] / max(1, stages["experts"][1])
+    achieved = b_ex / (ex_launch_ms * 1e-3)
     steps_per_s = 1e3 / ms
     out = {
         "metric": METRIC,
@@ -234,11 +243,11 @@ def main():
         "effective_tok_s": {"tpf_pages_19.74": round(steps_per_s * PAGES_TPF * n_req, 1),
                             f"tpf_loop_{C / S:g}": round(steps_per_s * C / S * n_req, 1)},
         "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof * 1e3 / ms, 4),
-                          "touched_experts_per_layer": touched},
-        "roofline": {"kernel": "moe_gateup (routed + shared expert gate/up + SwiGLU)",
+                          "touched_experts_per_layer": round(touched, 2)},
+        "roofline": {"kernel": "moe_experts (routed + shared experts: gate/up + SwiGLU + down)",
                      "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
-                     "bytes_per_launch": b_gu, "avg_launch_ms": round(gu_launch_ms, 4),
+                     "bytes_per_launch": round(b_ex), "avg_launch_ms": round(ex_launch_ms, 4),
                      "traffic": None},
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,

@@ -29,6 +29,9 @@ class DGConfig(ctypes.Structure):
 
 LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "w_gate", "w_up", "w_down",
                 "ws_gate", "ws_up", "ws_down")
+# Streamed projection matrices: passed to dg_create in the fragment-major
+# layout made by dg_pack_weight; the other fields stay row-major.
+PACKED_FIELDS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
 
 
 class DGLayerWeights(ctypes.Structure):
@@ -70,6 +73,7 @@ SIGNATURES = {
     "dg_create": (c_i32, [ctypes.POINTER(DGConfig), ctypes.POINTER(DGWeights), c_vp, c_vp, c_size,
                           ctypes.POINTER(c_vp)]),
     "dg_destroy": (None, [c_vp]),
+    "dg_pack_weight": (c_i32, [c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32]),
     "dg_init_canvas": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
     "dg_denoise_step": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
@@ -86,7 +90,13 @@ SIGNATURES = {
     "dg_timing_read": (c_i32, [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32]),
 }
 
-STAGES = ("embed", "norm", "qkv", "attn", "oproj", "router", "topk", "permute", "gateup", "down",
+# Words of the workspace "items" buffer (include/dg_test.h): expert-kernel
+# waits that ran out (int32), and running routing statistics (uint64).
+ITEMS_SPIN_TIMEOUTS = 409
+ITEMS_TOUCHED_TOTAL = 410
+ITEMS_PERMUTE_CALLS = 412
+
+STAGES = ("embed", "norm", "qkv", "attn", "oproj", "router", "topk", "permute", "experts",
           "combine", "lmhead", "merge", "sampler")
 
 _lib = None

@@ -12,6 +12,10 @@
 #include "common.h"
 #include "kernels.h"
 
+static_assert(MOE_SPIN_TIMEOUTS == DG_ITEMS_SPIN_TIMEOUTS && MOE_TOUCHED_TOTAL == DG_ITEMS_TOUCHED_TOTAL &&
+                  MOE_PERMUTE_CALLS == DG_ITEMS_PERMUTE_CALLS,
+              "test header and kernels disagree");
+
 namespace {
 
 struct LayerW {
@@ -46,7 +50,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.wslot = take(R * k * 4);
   L.cnt = take(256 * 4);
   L.off = take(257 * 4);
-  L.items = take(2 * 260 * 4 + 64);  // item offsets (gate/up, down), then two queue heads
+  L.items = take(((size_t)MOE_DONE + moe_chunk_bound(c.max_rows, c.n_experts, c.top_k)) * 4);
   L.perm = take(R * k * 4);
   L.slot = take(R * k * 4);
   L.hid = take(R * k * c.d_expert * 2);
@@ -193,25 +197,19 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   STAGE(DG_STAGE_ROUTER, launch_norm_router_topk(s, h, w.moe_norm, rows, d, g.rms_eps, w.w_router, g.n_experts,
                                                  g.top_k, u, c->buf<float>(L.z), c->buf<int32_t>(L.idx),
                                                  c->buf<float>(L.w)));
-  int32_t* items_gu = c->buf<int32_t>(L.items);
-  int32_t* items_dn = items_gu + 260;
-  int32_t* queues = items_gu + 520;
+  int32_t* items = c->buf<int32_t>(L.items);
   const int ch = moe_rows_per_chunk(rows, g.n_experts, g.top_k);
   STAGE(DG_STAGE_PERMUTE, launch_permute(s, c->buf<int32_t>(L.idx), rows, g.n_experts, g.top_k, ch,
-                                         g.d_expert / 64, g.d_shared / 64, d / 64, c->buf<int32_t>(L.cnt),
+                                         g.d_expert / 64, g.d_shared / 64, d / 128, c->buf<int32_t>(L.cnt),
                                          c->buf<int32_t>(L.off), c->buf<int32_t>(L.perm),
-                                         c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items_gu,
-                                         items_dn, queues));
-  STAGE(DG_STAGE_GATEUP, launch_moe_gateup(s, u, rows, d, c->buf<int32_t>(L.perm), c->buf<int32_t>(L.cnt),
-                                           c->buf<int32_t>(L.off), items_gu, queues, w.w_gate, w.w_up,
-                                           g.d_expert, g.n_experts, g.top_k, w.ws_gate, w.ws_up,
-                                           g.d_shared, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s)));
+                                         c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items));
   float* y = c->buf<float>(L.y);
   float* ys = y + (size_t)g.max_rows * g.top_k * d;
-  STAGE(DG_STAGE_DOWN, launch_moe_down(s, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s), rows, d,
-                                       c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<float>(L.w),
-                                       c->buf<int32_t>(L.wslot), items_dn, queues + 1, w.w_down, g.d_expert,
-                                       g.n_experts, g.top_k, w.ws_down, g.d_shared, y, ys));
+  STAGE(DG_STAGE_EXPERTS,
+        launch_moe_experts(s, u, rows, d, g.d_expert, g.d_shared, g.n_experts, g.top_k, c->buf<int32_t>(L.perm),
+                           c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<float>(L.w),
+                           c->buf<int32_t>(L.wslot), items, w.w_gate, w.w_up, w.w_down, w.ws_gate, w.ws_up,
+                           w.ws_down, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s), y, ys));
   STAGE(DG_STAGE_COMBINE, launch_moe_combine(s, h, ys, y, c->buf<int32_t>(L.slot), rows, d, g.top_k,
                                              next_gain, g.rms_eps, u));
 }
@@ -359,6 +357,16 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
 
 void dg_destroy(dg_ctx* c) { delete c; }
 
+dg_status dg_pack_weight(void* stream, const void* d_src, void* d_dst, int64_t n, int32_t k) {
+  if (!d_src || !d_dst || n <= 0 || k <= 0 || n % 16 != 0 || k % 64 != 0) return DG_EINVAL;
+  const char* s0 = (const char*)d_src;
+  const char* d0 = (const char*)d_dst;
+  const int64_t bytes = n * (int64_t)k * 2;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return DG_EINVAL;  // overlapping buffers
+  launch_pack((hipStream_t)stream, (const bf16_t*)d_src, (bf16_t*)d_dst, n, k);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
+}
+
 int32_t dg_cache_len(const dg_ctx* c, int32_t req) {
   if (!c || req < 0 || req >= c->cfg.max_requests) return -1;
   return c->len[req];
@@ -495,11 +503,10 @@ dg_status dg_test_route(dg_ctx* c, void* stream, const float* d_z, int32_t rows,
   const dg_ws_layout& L = c->lay;
   const int E = g.n_experts, k = g.top_k;
   launch_topk(s, d_z, rows, E, k, c->buf<int32_t>(L.idx), c->buf<float>(L.w));
-  int32_t* items_gu = c->buf<int32_t>(L.items);
   launch_permute(s, c->buf<int32_t>(L.idx), rows, E, k, moe_rows_per_chunk(rows, E, k), g.d_expert / 64,
-                 g.d_shared / 64, g.d_model / 64, c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off),
-                 c->buf<int32_t>(L.perm), c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items_gu,
-                 items_gu + 260, items_gu + 520);
+                 g.d_shared / 64, g.d_model / 128, c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off),
+                 c->buf<int32_t>(L.perm), c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot),
+                 c->buf<int32_t>(L.items));
   auto cp = [&](void* dst, size_t off, size_t bytes) {
     if (dst) (void)hipMemcpyAsync(dst, c->ws + off, bytes, hipMemcpyDeviceToDevice, s);
   };

@@ -12,6 +12,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define DG_MAX_REQ 16       // requests batched into one call
+
+// Expert work list (int32 words in the workspace "items" buffer), written by
+// the permutation kernel and consumed by the expert kernel. Groups: 0 = the
+// shared expert, 1 + e = routed expert e.
+constexpr int MOE_MAX_GROUPS = 129;       // E <= 128, plus the shared expert
+constexpr int MOE_ITEMS_GU = 0;           // [G+1] exclusive gate/up item offsets
+constexpr int MOE_ITEMS_DN = 136;         // [G+1] exclusive down item offsets
+constexpr int MOE_CHUNKS = 272;           // [G+1] exclusive row-chunk offsets
+constexpr int MOE_QUEUE = 408;            // work-queue head
+constexpr int MOE_SPIN_TIMEOUTS = 409;    // waits that ran out (never reset)
+constexpr int MOE_TOUCHED_TOTAL = 410;    // uint64: experts with >= 1 row, summed over calls
+constexpr int MOE_PERMUTE_CALLS = 412;    // uint64: permutation calls (both never reset)
+constexpr int MOE_DONE = 416;             // per-chunk count of finished gate/up tiles
 #define DG_ATTN_SPLITS 8    // maximum key splits of the attention kernel
 #define WAVE 64
 

@@ -1,6 +1,8 @@
-// Dense projections of a layer on the weight-streaming tile (stream.h):
+// Dense projections of a layer on the weight-streaming tile (stream.h), with
+// fragment-major packed weights:
 //   QKV + RoPE: every lane owns a rotate-half pair (head row j and j + dh/2)
-//     as the tile's two weight rows, so the rotation is lane-local; q goes to
+//     as the tile's two weight rows, so the rotation is lane-local; a wave's
+//     16 pairs are two 16-row blocks (dh/2 is a multiple of 16). q goes to
 //     the workspace, k (rotated) and v to the request's KV-cache rows.
 //   output projection: h[row][col] += (o W_o^T)[row][col].
 // All token rows form one group cut into chunks of 16*MT rows; the chunks
@@ -42,9 +44,9 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
   int nt, mc;
   tile_coords(NT, MC, nt, mc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
-  const int pc = nt * 64 + wave * 16 + l16;
-  const int head = pc / half, j = pc % half;
-  const int64_t r0 = (int64_t)head * dh + j;
+  const int pw = nt * 64 + wave * 16;  // the wave's first pair
+  const int head = pw / half, j = pw % half + l16;
+  const int64_t r0 = (int64_t)head * dh + pw % half;  // first row of the wave's block
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 a0[DMT], a1[DMT];
   stream_tile<DMT, true>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
@@ -89,11 +91,10 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
   int nt, mc;
   tile_coords(NT, MC, nt, mc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
-  const int col = nt * 64 + wave * 16 + l16;
+  const int col0 = nt * 64 + wave * 16, col = col0 + l16;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 acc[DMT], unused[DMT];
-  stream_tile<DMT, false>(a, K, nullptr, row0, nrows, w + (int64_t)col * K, nullptr, K, acc, unused,
-                               lds);
+  stream_tile<DMT, false>(a, K, nullptr, row0, nrows, w + (int64_t)col0 * K, nullptr, K, acc, unused, lds);
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
 #pragma unroll

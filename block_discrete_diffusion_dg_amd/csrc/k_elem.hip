@@ -1,10 +1,12 @@
 // Row-wise kernels of the step: embedding gather, RMSNorm, the RoPE table,
-// and the uniform initial canvas.
+// the uniform initial canvas, and the weight repacking into the
+// fragment-major layout of the streaming tile.
 #include <math.h>
 
 #include "common.h"
 #include "kernels.h"
 #include "philox.h"
+#include "stream.h"
 
 namespace {
 
@@ -95,7 +97,34 @@ __global__ void init_canvas_kernel(SampleTable st, int C, int V, int32_t* __rest
   }
 }
 
+// dst = fragment-major copy of the row-major [n][k] matrix src: thread c
+// writes the c-th 16-byte piece of dst, read from the 8 elements of src that
+// pack_index maps there.
+__global__ void pack_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst, int64_t n, int k) {
+  const int64_t pieces = n * (k / 8);
+  const int steps = k / 64;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < pieces;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(c & 63);
+    int64_t t = c >> 6;
+    const int q = (int)(t & 1);
+    t >>= 1;
+    const int ks = (int)(t % steps);
+    const int64_t nb = t / steps;
+    const int64_t row = nb * 16 + (lane & 15);
+    const int col = ks * 64 + q * 32 + (lane >> 4) * 8;
+    *reinterpret_cast<u32x4*>(dst + c * 8) = ld16(src + row * k + col);
+  }
+}
+
 }  // namespace
+
+void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k) {
+  const int64_t pieces = n * (k / 8);
+  const int64_t want = (pieces + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, src, dst, n, k);
+}
 
 void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
                   float* h, const bf16_t* gain, float eps, bf16_t* u) {

@@ -1,14 +1,25 @@
-// Grouped SwiGLU experts over a device-built work list.
+// Grouped SwiGLU experts over a device-built work list, in one persistent
+// kernel.
 //
-// A group is a routed expert (its tokens are the permutation slots
-// off[e] .. off[e+1]) or the shared expert (all tokens). Each group's rows are
+// A group is the shared expert (group 0: all tokens) or a routed expert
+// (group 1+e: the permutation slots off[e] .. off[e+1]). Each group's rows are
 // cut into chunks of CH = 16*MT rows, and every (group, column tile, row
-// chunk) is one work item; the permutation kernel writes the exclusive item
-// offsets per group, so any routing, however uneven, becomes a flat list of
-// equal-sized items: a group with many tokens gets many items.
+// chunk) is one work item, of one of two kinds:
+//   gate/up:  hid[slot][f] = silu(x W_gate[f]) * (x W_up[f])   (bf16; 64 columns f)
+//   down:     y[slot][c]   = w_slot * (hid[slot] W_down[c])     (fp32, 128 columns c;
+//                                                              shared: ys[t][c])
+// The permutation kernel writes the exclusive item offsets of both kinds and
+// the chunk offsets per group, and zeroes the queue head and the per-chunk
+// completion counters. Work-groups take items from the queue: all gate/up
+// items first, then all down items, so a work-group that runs out of gate/up
+// work starts on down items while the last gate/up items are still streaming
+// (no second launch, no idle tail). A down item waits until every gate/up
+// column tile of its chunk has published its rows to device-coherent memory
+// (those items may run on another XCD, whose L2 is not coherent with this
+// one). Every gate/up item is taken before any down item and
+// never waits, so the wait always ends; it is still bounded, and a wait that
+// runs out counts itself in the spin-timeout word instead of hanging.
 //
-// gate/up:  hid[slot][f] = silu(x W_gate[f]) * (x W_up[f])   (bf16)
-// down:     y[slot][c]   = w_slot * (hid[slot] W_down[c])     (fp32; shared: ys[t][c])
 // combine:  h[t] += ys[t] + sum_j y[slot[t][j]]               (fixed order)
 #include "common.h"
 #include "kernels.h"
@@ -16,133 +27,145 @@
 
 namespace {
 
-// Both expert kernels are persistent: a fixed grid of work-groups takes work
-// items from an atomic counter (zeroed by the permutation kernel) until the
-// list is exhausted, so a launch never ends with a second, mostly idle round
-// of work-groups. Every work-group exits once the counter passes the item
-// count.
+constexpr int SPIN_LIMIT = 1 << 20;  // polls (about a second) before giving up
+
+struct MoeArgs {
+  const bf16_t* u;  // [rows][d] normalised tokens
+  int rows, d, F, Fs, E;
+  const int32_t *perm, *cnt, *off;  // permutation (slot -> token), per-expert counts and offsets
+  const float* wts;                 // routing weights [rows*k]
+  const int32_t* widx;              // slot -> index into wts
+  int32_t* items;                   // MoeItems layout
+  const bf16_t *wg, *wu, *wd, *sg, *su, *sd;  // fragment-major weights
+  bf16_t *hid, *hid_s;
+  float *y, *ys;
+};
+
+// 16-byte store that writes through to device-coherent memory (visible to
+// every XCD once complete; no L2 write-back needed). The nop covers the
+// store-data read hazard of wide vector stores.
+__device__ __forceinline__ void store16_coherent(bf16_t* dst, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
+
+// Wait until every vector memory operation of this wave has completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ int next_item(int32_t* counter, int* s_slot) {
   __syncthreads();  // everyone has read the previous item
   if (threadIdx.x == 0) *s_slot = atomicAdd(counter, 1);
   __syncthreads();
-  return *s_slot;
+  return __builtin_amdgcn_readfirstlane(*s_slot);  // wave-uniform: branches stay scalar
 }
 
 template <int MT>
-__global__ __launch_bounds__(256) void moe_gateup_kernel(
-    const bf16_t* __restrict__ u, int rows, int d, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ items, int32_t* __restrict__ queue, const bf16_t* __restrict__ wg,
-    const bf16_t* __restrict__ wu, int F, int E, const bf16_t* __restrict__ sg,
-    const bf16_t* __restrict__ su, int Fs, bf16_t* __restrict__ hid, bf16_t* __restrict__ hid_s) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_experts_kernel(MoeArgs p) {
   using T = StreamTile<MT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
-  __shared__ int32_t s_items[258];
-  __shared__ int s_item;
-  const int n_groups = E + 1;
-  for (int i = threadIdx.x; i <= n_groups; i += 256) s_items[i] = items[i];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
-  for (;;) {
-    const int b = next_item(queue, &s_item);
-    if (b >= s_items[n_groups]) break;
-    const int g = find_group(s_items, n_groups, b);
-    int n, ldo;
-    const int32_t* rowmap;
-    const bf16_t *W0, *W1;
-    bf16_t* out;
-    if (g < E) {
-      n = cnt[g];
-      const int base = off[g];
-      rowmap = perm + base;
-      W0 = wg + (int64_t)g * F * d;
-      W1 = wu + (int64_t)g * F * d;
-      out = hid + (int64_t)base * F;
-      ldo = F;
-    } else {
-      n = rows;
-      rowmap = nullptr;
-      W0 = sg;
-      W1 = su;
-      out = hid_s;
-      ldo = Fs;
-    }
-    const int nmc = div_up(n, T::CH);
-    const int local = b - s_items[g];
-    const int nt = local / nmc, mc = local % nmc;
-    const int row0 = mc * T::CH, nrows = min(T::CH, n - row0);
-    const int col = nt * 64 + wave * 16 + l16;
-    f32x4 ag[MT], au[MT];
-    stream_tile<MT, true>(u, d, rowmap, row0, nrows, W0 + (int64_t)col * d, W1 + (int64_t)col * d, d, ag, au,
-                          lds);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = row0 + 16 * mt + 4 * grp + r;
-        if (p < n) {
-          const float gv = ag[mt][r];
-          out[(int64_t)p * ldo + col] = f2bf(gv / (1.0f + expf(-gv)) * au[mt][r]);
-        }
-      }
-  }
-}
-
-template <int MT>
-__global__ __launch_bounds__(256) void moe_down_kernel(
-    const bf16_t* __restrict__ hid, const bf16_t* __restrict__ hid_s, int rows, int d,
-    const int32_t* __restrict__ cnt, const int32_t* __restrict__ off,
-    const float* __restrict__ wts_all, const int32_t* __restrict__ widx,
-    const int32_t* __restrict__ items, int32_t* __restrict__ queue, const bf16_t* __restrict__ wd, int F,
-    int E, const bf16_t* __restrict__ sd, int Fs, float* __restrict__ y, float* __restrict__ ys) {
-  using T = StreamTile<MT>;
-  __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
-  __shared__ int32_t s_items[258];
+  __shared__ int32_t s_gu[MOE_MAX_GROUPS + 1], s_dn[MOE_MAX_GROUPS + 1], s_ch[MOE_MAX_GROUPS + 1];
   __shared__ float s_w[T::CH];
   __shared__ int s_item;
-  const int n_groups = E + 1;
-  for (int i = threadIdx.x; i <= n_groups; i += 256) s_items[i] = items[i];
+  const int G = p.E + 1;
+  for (int i = threadIdx.x; i <= G; i += 256) {
+    s_gu[i] = p.items[MOE_ITEMS_GU + i];
+    s_dn[i] = p.items[MOE_ITEMS_DN + i];
+    s_ch[i] = p.items[MOE_CHUNKS + i];
+  }
+  int32_t* queue = p.items + MOE_QUEUE;
+  int32_t* done = p.items + MOE_DONE;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
   for (;;) {
     const int b = next_item(queue, &s_item);
-    if (b >= s_items[n_groups]) break;
-    const int g = find_group(s_items, n_groups, b);
-    int n, K;
-    const bf16_t *A, *W;
-    float* out;
-    const bool routed = g < E;
-    int base = 0;
-    if (routed) {
-      n = cnt[g];
-      base = off[g];
-      A = hid + (int64_t)base * F;
-      K = F;
-      W = wd + (int64_t)g * d * F;
-      out = y + (int64_t)base * d;
-    } else {
-      n = rows;
-      A = hid_s;
-      K = Fs;
-      W = sd;
-      out = ys;
-    }
+    const int n_gu = s_gu[G], total = n_gu + s_dn[G];
+    if (b >= total) break;
+    const bool up = b < n_gu;
+    const int32_t* s_it = up ? s_gu : s_dn;
+    const int bl = up ? b : b - n_gu;
+    const int gi = __builtin_amdgcn_readfirstlane(find_group(s_it, G, bl));
+    const bool shared = gi == 0;
+    const int e = gi - 1;
+    const int n = shared ? p.rows : p.cnt[e];
+    const int base = shared ? 0 : p.off[e];
     const int nmc = div_up(n, T::CH);
-    const int local = b - s_items[g];
+    const int local = bl - s_it[gi];
     const int nt = local / nmc, mc = local % nmc;
     const int row0 = mc * T::CH, nrows = min(T::CH, n - row0);
-    // routing weights of the chunk's slots, staged while the weights stream
-    if (threadIdx.x < T::CH)
-      s_w[threadIdx.x] = (routed && threadIdx.x < nrows) ? wts_all[widx[base + row0 + threadIdx.x]] : 1.0f;
-    const int col = nt * 64 + wave * 16 + l16;
-    f32x4 acc[MT], unused[MT];
-    stream_tile<MT, false>(A, K, nullptr, row0, nrows, W + (int64_t)col * K, nullptr, K, acc, unused, lds);
+    const int chunk = s_ch[gi] + mc;
+    if (up) {
+      const int col0 = nt * 64 + wave * 16;
+      const int ldo = shared ? p.Fs : p.F;
+      const bf16_t* W0 = shared ? p.sg : p.wg + (int64_t)e * p.F * p.d;
+      const bf16_t* W1 = shared ? p.su : p.wu + (int64_t)e * p.F * p.d;
+      bf16_t* out = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
+      f32x4 ag[MT], au[MT];
+      stream_tile<MT, true>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0 + (int64_t)col0 * p.d,
+                            W1 + (int64_t)col0 * p.d, p.d, ag, au, lds);
+      // Publish: stage the 64-column tile in LDS, write whole 128-byte row
+      // segments with write-through (agent-coherent) stores, wait until they
+      // complete, then move the chunk's counter. An agent-scope release fence
+      // would instead write back this XCD's whole L2 for every item.
+      __syncthreads();   // the tile's last LDS reads are done
+      bf16_t* st = lds;  // [CH][72] bf16, inside the A tile buffers
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int q = 16 * mt + 4 * grp + r;
-        const int p = row0 + q;
-        if (p < n) out[(int64_t)p * d + col] = acc[mt][r] * s_w[q];
+        for (int r = 0; r < 4; ++r) {
+          const float gv = ag[mt][r];
+          st[(16 * mt + 4 * grp + r) * 72 + wave * 16 + l16] = f2bf(gv / (1.0f + expf(-gv)) * au[mt][r]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < T::CH * 8 / 256; ++i) {
+        const int c = threadIdx.x + 256 * i, rr = c >> 3, seg = (c & 7) * 8;
+        if (row0 + rr < n)
+          store16_coherent(out + (int64_t)(row0 + rr) * ldo + nt * 64 + seg,
+                           *reinterpret_cast<const u32x4*>(st + rr * 72 + seg));
       }
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(done + chunk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int need = (shared ? p.Fs : p.F) / 64;  // gate/up column tiles of the chunk
+      // Poll with device-coherent relaxed loads. No cache invalidation is
+      // needed after the wait (an agent-scope acquire would invalidate this
+      // XCD's whole L2 on every poll): caches start the kernel invalidated,
+      // and the chunk's rows of hid are read only by down items of this
+      // chunk, all after the wait, so no L1 or L2 can hold a stale copy.
+      if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(done + chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++spins > SPIN_LIMIT) {
+            atomicAdd(p.items + MOE_SPIN_TIMEOUTS, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      const int K = shared ? p.Fs : p.F;
+      const bf16_t* A = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
+      const bf16_t* W = shared ? p.sd : p.wd + (int64_t)e * p.d * p.F;
+      float* out = shared ? p.ys : p.y + (int64_t)base * p.d;
+      // routing weights of the chunk's slots, staged while the weights stream
+      if (threadIdx.x < T::CH)
+        s_w[threadIdx.x] = (!shared && threadIdx.x < nrows) ? p.wts[p.widx[base + row0 + threadIdx.x]] : 1.0f;
+      // 128 output columns per item: the wave owns two 16-row weight blocks
+      const int c0 = nt * 128 + wave * 32;
+      f32x4 acc0[MT], acc1[MT];
+      stream_tile<MT, true>(A, K, nullptr, row0, nrows, W + (int64_t)c0 * K, W + (int64_t)(c0 + 16) * K, K, acc0,
+                            acc1, lds);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 16 * mt + 4 * grp + r;
+          if (row0 + q < n) {
+            float* o = out + (int64_t)(row0 + q) * p.d + c0 + l16;
+            o[0] = acc0[mt][r] * s_w[q];
+            o[16] = acc1[mt][r] * s_w[q];
+          }
+        }
+    }
   }
 }
 
@@ -204,67 +227,52 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
 
 }  // namespace
 
-// Rows per work item. 128-row chunks let one work-group reuse each weight
-// tile across all the tokens of a busy expert (routing is far from uniform);
-// small experts waste matrix-core work on empty rows, which is cheap next to
-// the weight stream. Tiny batches use 32-row chunks.
+// Rows per work item: 64-row chunks once experts average at least 8 rows,
+// else 32 (tiny batches).
 int moe_rows_per_chunk(int rows, int E, int k) {
-  return rows * k >= 8 * E ? 128 : 32;
+  return rows * k >= 8 * E ? 64 : 32;
 }
 
-int moe_item_bound(int rows, int E, int k, int n_tiles_routed, int n_tiles_shared) {
-  const int CH = moe_rows_per_chunk(rows, E, k);
-  const int chunks = div_up(rows * k, CH) + min(E, rows * k);
-  return chunks * n_tiles_routed + div_up(rows, CH) * n_tiles_shared;
+// Chunks over all groups: sum_e ceil(cnt_e / ch) + ceil(rows / ch) is at most
+// rows*k/ch + E + rows/ch + 1.
+int moe_chunk_bound(int rows, int E, int k) {
+  const int ch = moe_rows_per_chunk(rows, E, k);
+  return div_up(rows * k, ch) + E + div_up(rows, ch) + 1;
 }
 
 // Persistent grid: as many work-groups as the GPU holds at once (queried
-// once per kernel from its resource use), never more than the item bound.
+// once per kernel from its resource use).
 template <typename Kernel>
-static int persistent_grid(Kernel kernel, int bound, int& resident) {
-  if (resident == 0) {
+static int resident_blocks(Kernel kernel, int& cache) {
+  if (cache == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0)
-      resident = 1024;
+      cache = 1024;
     else
-      resident = cus * per_cu;
+      cache = cus * per_cu;
   }
-  return bound < resident ? bound : resident;
+  return cache;
 }
-static int g_resident[4];  // gate/up MT=8, MT=2; down MT=8, MT=2
+static int g_resident[2];  // MT=4, MT=2
 
-void launch_moe_gateup(hipStream_t s, const bf16_t* u, int rows, int d, const int32_t* perm,
-                       const int32_t* cnt, const int32_t* off, const int32_t* items, int32_t* queue,
-                       const bf16_t* wg, const bf16_t* wu, int F, int E, int k, const bf16_t* sg,
-                       const bf16_t* su, int Fs, bf16_t* hid, bf16_t* hid_s) {
-  const int bound = moe_item_bound(rows, E, k, F / 64, Fs / 64);
-  if (moe_rows_per_chunk(rows, E, k) == 128)
-    hipLaunchKernelGGL(moe_gateup_kernel<8>, dim3(persistent_grid(moe_gateup_kernel<8>, bound, g_resident[0])), dim3(256), 0,
-                       s, u, rows, d, perm, cnt, off, items, queue, wg, wu, F, E, sg, su, Fs, hid, hid_s);
+void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, int Fs, int E, int k,
+                        const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
+                        const int32_t* widx, int32_t* items, const bf16_t* wg, const bf16_t* wu,
+                        const bf16_t* wd, const bf16_t* sg, const bf16_t* su, const bf16_t* sd, bf16_t* hid,
+                        bf16_t* hid_s, float* y, float* ys) {
+  MoeArgs p{u, rows, d, F, Fs, E, perm, cnt, off, wts, widx, items, wg, wu, wd, sg, su, sd, hid, hid_s, y, ys};
+  if (moe_rows_per_chunk(rows, E, k) == 64)
+    hipLaunchKernelGGL(moe_experts_kernel<4>, dim3(resident_blocks(moe_experts_kernel<4>, g_resident[0])),
+                       dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(moe_gateup_kernel<2>, dim3(persistent_grid(moe_gateup_kernel<2>, bound, g_resident[1])), dim3(256), 0,
-                       s, u, rows, d, perm, cnt, off, items, queue, wg, wu, F, E, sg, su, Fs, hid, hid_s);
+    hipLaunchKernelGGL(moe_experts_kernel<2>, dim3(resident_blocks(moe_experts_kernel<2>, g_resident[1])),
+                       dim3(256), 0, s, p);
 }
 
-void launch_moe_down(hipStream_t s, const bf16_t* hid, const bf16_t* hid_s, int rows, int d,
-                     const int32_t* cnt, const int32_t* off, const float* w, const int32_t* widx,
-                     const int32_t* items, int32_t* queue, const bf16_t* wd, int F, int E, int k,
-                     const bf16_t* sd, int Fs, float* y, float* ys) {
-  const int bound = moe_item_bound(rows, E, k, d / 64, d / 64);
-  if (moe_rows_per_chunk(rows, E, k) == 128)
-    hipLaunchKernelGGL(moe_down_kernel<8>, dim3(persistent_grid(moe_down_kernel<8>, bound, g_resident[2])), dim3(256), 0, s,
-                       hid, hid_s, rows, d, cnt, off, w, widx, items, queue, wd, F, E, sd, Fs, y, ys);
-  else
-    hipLaunchKernelGGL(moe_down_kernel<2>, dim3(persistent_grid(moe_down_kernel<2>, bound, g_resident[3])), dim3(256), 0, s,
-                       hid, hid_s, rows, d, cnt, off, w, widx, items, queue, wd, F, E, sd, Fs, y, ys);
-}
-
-void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y,
-                        const int32_t* slot, int rows, int d, int k, const bf16_t* next_gain,
-                        float eps, bf16_t* u) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps,
-                     u);
+void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y, const int32_t* slot,
+                        int rows, int d, int k, const bf16_t* next_gain, float eps, bf16_t* u) {
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps, u);
 }

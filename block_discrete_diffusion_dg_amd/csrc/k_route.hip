@@ -234,14 +234,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ slot,
                                                        int32_t* __restrict__ widx,
-                                                       int32_t* __restrict__ items_gu,
-                                                       int32_t* __restrict__ items_dn,
-                                                       int32_t* __restrict__ queues) {
+                                                       int32_t* __restrict__ items) {
   extern __shared__ uint32_t dyn[];  // bits [rows][ceil(E/32)], then choices [rows*k] bytes
   __shared__ int32_t s_cnt[257];
   __shared__ int32_t s_off[258];
-  __shared__ int32_t s_ngu[257], s_ndn[257];
-  __shared__ int32_t s_igu[258], s_idn[258];
+  __shared__ int32_t s_ngu[MOE_MAX_GROUPS], s_ndn[MOE_MAX_GROUPS], s_nch[MOE_MAX_GROUPS];
+  __shared__ int32_t s_igu[MOE_MAX_GROUPS + 1], s_idn[MOE_MAX_GROUPS + 1], s_ich[MOE_MAX_GROUPS + 1];
   const int words = (E + 31) / 32;
   uint32_t* bits = dyn;
   uint8_t* choice = reinterpret_cast<uint8_t*>(dyn + rows * words);
@@ -264,27 +262,42 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     if (lane == 0) s_cnt[e] = c;
   }
   __syncthreads();
+  // groups: 0 = shared expert (all rows), 1 + e = routed expert e
   for (int g = tid; g <= E; g += 1024) {
-    const int n = g < E ? s_cnt[g] : rows;
+    const int n = g == 0 ? rows : s_cnt[g - 1];
     const int nmc = (n + ch - 1) / ch;
-    s_ngu[g] = nmc * (g < E ? ft_routed : ft_shared);
+    s_nch[g] = nmc;
+    s_ngu[g] = nmc * (g == 0 ? ft_shared : ft_routed);
     s_ndn[g] = nmc * dt;
   }
   __syncthreads();
   if (wave == 0) wave_exclusive_scan(s_cnt, s_off, E, lane);
   if (wave == 1) wave_exclusive_scan(s_ngu, s_igu, E + 1, lane);
   if (wave == 2) wave_exclusive_scan(s_ndn, s_idn, E + 1, lane);
+  if (wave == 3) wave_exclusive_scan(s_nch, s_ich, E + 1, lane);
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     cnt[e] = s_cnt[e];
     off[e] = s_off[e];
   }
-  if (tid == 0) off[E] = s_off[E];
-  if (tid < 2) queues[tid] = 0;  // work-queue heads of the two expert kernels
-  for (int g = tid; g <= E + 1; g += 1024) {
-    items_gu[g] = s_igu[g];
-    items_dn[g] = s_idn[g];
+  if (tid == 0) {
+    off[E] = s_off[E];
+    items[MOE_QUEUE] = 0;
   }
+  if (wave == 4) {  // running statistics: experts touched per call
+    int touched = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) touched += __popcll(__ballot(e0 + lane < E && s_cnt[e0 + lane] > 0));
+    if (lane == 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(items + MOE_TOUCHED_TOTAL), (unsigned long long)touched);
+      atomicAdd(reinterpret_cast<unsigned long long*>(items + MOE_PERMUTE_CALLS), 1ull);
+    }
+  }
+  for (int g = tid; g <= E + 1; g += 1024) {
+    items[MOE_ITEMS_GU + g] = s_igu[g];
+    items[MOE_ITEMS_DN + g] = s_idn[g];
+    items[MOE_CHUNKS + g] = s_ich[g];
+  }
+  for (int c = tid; c < s_ich[E + 1]; c += 1024) items[MOE_DONE + c] = 0;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int e = wave; e < E; e += 16) {
     int run = s_off[e];
@@ -323,10 +336,10 @@ void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, 
 
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
                     int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
-                    int32_t* widx, int32_t* items_gu, int32_t* items_dn, int32_t* queues) {
+                    int32_t* widx, int32_t* items) {
   const size_t lds = permute_lds_bytes(rows, E, k);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, idx, rows, E, k, ch, ft_routed, ft_shared,
-                     dt, cnt, off, perm, slot, widx, items_gu, items_dn, queues);
+                     dt, cnt, off, perm, slot, widx, items);
 }
 
 size_t permute_lds_bytes(int rows, int E, int k) {

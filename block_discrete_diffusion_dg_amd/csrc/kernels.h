@@ -14,6 +14,7 @@ void launch_rope_table(hipStream_t s, const ReqTable& rt, int dh, float theta, f
 void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas, uint8_t* committed,
                         const uint64_t* seeds_host, const int32_t* blocks_host,
                         const int32_t* slots_host);
+void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k);
 
 // k_dense.hip (weight-streaming dense projections)
 void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
@@ -39,20 +40,17 @@ void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, 
                              const bf16_t* wr, int E, int k, bf16_t* u, float* z, int32_t* idx, float* w);
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
                     int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
-                    int32_t* widx, int32_t* items_gu, int32_t* items_dn, int32_t* queues);
+                    int32_t* widx, int32_t* items);
 size_t permute_lds_bytes(int rows, int E, int k);
 
 // k_moe.hip
 int moe_rows_per_chunk(int rows, int E, int k);
-int moe_item_bound(int rows, int E, int k, int n_tiles_routed, int n_tiles_shared);
-void launch_moe_gateup(hipStream_t s, const bf16_t* u, int rows, int d, const int32_t* perm,
-                       const int32_t* cnt, const int32_t* off, const int32_t* items, int32_t* queue,
-                       const bf16_t* wg, const bf16_t* wu, int F, int E, int k, const bf16_t* sg,
-                       const bf16_t* su, int Fs, bf16_t* hid, bf16_t* hid_s);
-void launch_moe_down(hipStream_t s, const bf16_t* hid, const bf16_t* hid_s, int rows, int d,
-                     const int32_t* cnt, const int32_t* off, const float* w, const int32_t* widx,
-                     const int32_t* items, int32_t* queue, const bf16_t* wd, int F, int E, int k,
-                     const bf16_t* sd, int Fs, float* y, float* ys);
+int moe_chunk_bound(int rows, int E, int k);
+void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, int Fs, int E, int k,
+                        const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
+                        const int32_t* widx, int32_t* items, const bf16_t* wg, const bf16_t* wu,
+                        const bf16_t* wd, const bf16_t* sg, const bf16_t* su, const bf16_t* sd, bf16_t* hid,
+                        bf16_t* hid_s, float* y, float* ys);
 void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y,
                         const int32_t* slot, int rows, int d, int k, const bf16_t* next_gain,
                         float eps, bf16_t* u);

@@ -7,18 +7,22 @@
 // GATED the lane also owns a second weight row (the "up" row of a SwiGLU, or
 // the rotate-half partner of a RoPE pair) and a second accumulator.
 //
+// Weights are in the fragment-major layout (see pack_index below): the 16
+// rows a wave owns form one contiguous block, and each K-step of that block
+// is 2 KB in the exact order the lanes consume it, so every weight load of a
+// wave is one fully used, contiguous 1 KB request.
+//
 // Pipeline: K advances in steps of BK = 64. Loads run two steps ahead of the
 // matrix cores: while step it is multiplied, the loads of steps it+1 and
 // it+2 are in flight (three register sets for the weights and for the A
-// staging; a double-buffered LDS tile for A, shared by the four waves). HBM
-// latency is paid once per tile, not once per step. The loop is unrolled by
-// three so every register set has a static index; steps past the end reload
-// the last step (in-bounds, branch-free) and their weight operands are
-// zeroed, so the matrix-core instructions never sit under control flow.
+// staging; a double-buffered LDS tile for A, shared by the four waves). The
+// loop is unrolled by three so every register set has a static index; steps
+// past the end reload the last step (in-bounds, branch-free) and their
+// weight operands are zeroed, so the matrix-core instructions never sit under
+// control flow.
 //
-// Reduction-index assignment per K-step: lane group g, MFMA step q in {0,1}
-// uses k0 + 16g + 8q .. +7 for both operands (each lane reads 32 contiguous
-// bytes of its weight row per step).
+// Reduction-index assignment per K-step: MFMA step q in {0,1}, lane group g
+// uses k0 + 32q + 8g .. +7 for both operands.
 #pragma once
 
 #include <type_traits>
@@ -35,11 +39,23 @@ struct StreamTile {
   static_assert(ACH >= 1, "tile too small for 256 threads");
 };
 
-// acc0[mt][r] (and acc1 when GATED) = sum_k A[row][k] * W[k] for
-// row = row0 + 16*mt + 4*(lane/16) + r of the chunk, against the lane's
-// weight row(s) w0 (w1). A row i of the chunk is A + map(row0 + i) * lda with
-// map = rowmap or identity. Rows past nrows repeat the chunk's first row; their
-// accumulators are meaningless and must not be stored. K % 64 == 0.
+// Fragment-major index of W[n][k] for a [N][K] matrix (N % 16 == 0,
+// K % 64 == 0): block n/16 of 16 rows is contiguous (16*K elements); inside
+// it, K-step k/64 is 1024 elements ordered [q][lane][8] with
+// q = (k%64)/32, lane = 16*((k%32)/8) + n%16 and element k%8.
+__host__ __device__ __forceinline__ int64_t pack_index(int64_t n, int64_t k, int64_t K) {
+  const int64_t kk = k & 63;
+  return (n >> 4) * 16 * K + (k >> 6) * 1024 + (kk >> 5) * 512 + (((kk & 31) >> 3) * 16 + (n & 15)) * 8 +
+         (kk & 7);
+}
+
+// acc0[mt][r] (and acc1 when GATED) = sum_k A[row][k] * W[n][k] for
+// row = row0 + 16*mt + 4*(lane/16) + r of the chunk and n = the lane's weight
+// row: lane l16 of the wave's 16-row block(s) w0 (w1), packed fragment-major
+// (w0 = packed matrix + 16*K * block index). A row i of the chunk is
+// A + map(row0 + i) * lda with map = rowmap or identity. Rows past nrows
+// repeat the chunk's first row; their accumulators are meaningless and must
+// not be stored. K % 64 == 0.
 template <int MT, bool GATED>
 __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
                                             const int32_t* __restrict__ rowmap, int row0, int nrows,
@@ -49,7 +65,6 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
   using T = StreamTile<MT>;
   constexpr int BK = T::BK, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int kl = grp * (BK / 4);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -65,11 +80,14 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     aoff[i] = r * LDA + kc;
   }
   const int nk = K / BK;
+  const bf16_t* wl0 = w0 + lane * 8;
+  const bf16_t* wl1 = GATED ? w1 + lane * 8 : nullptr;
 
   u32x4 ra[3][ACH];
   u32x4 b0[3][2], b1[3][2];
 
-  // loads of step st (clamped to the last step) into register set S
+  // A loads first, then weights: the wait for A of the next step (in-order
+  // completion) then never waits on weights issued after it.
   auto issue = [&](auto S, int st) {
     constexpr int s = decltype(S)::value;
     const int k0 = min(st, nk - 1) * BK;
@@ -77,8 +95,8 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     for (int i = 0; i < ACH; ++i) ra[s][i] = ld16(arow[i] + k0);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      b0[s][q] = ld16(w0 + k0 + kl + 8 * q);
-      if (GATED) b1[s][q] = ld16(w1 + k0 + kl + 8 * q);
+      b0[s][q] = ld16(wl0 + k0 * 16 + q * 512);
+      if (GATED) b1[s][q] = ld16(wl1 + k0 * 16 + q * 512);
     }
   };
   auto stage = [&](auto S, int buf) {
@@ -97,7 +115,7 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
       const u32x4 bq1 = live ? b1[s][q] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 a = ld16(As + (16 * mt + l16) * LDA + kl + 8 * q);
+        const u32x4 a = ld16(As + (16 * mt + l16) * LDA + 32 * q + 8 * grp);
         acc0[mt] = mfma_bf16(a, bq0, acc0[mt]);
         if (GATED) acc1[mt] = mfma_bf16(a, bq1, acc1[mt]);
       }

@@ -25,8 +25,25 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def pack_weight(t: torch.Tensor) -> torch.Tensor:
+    """Fragment-major copy of a row-major bf16 GPU matrix (dg_pack_weight);
+    a [E][N][K] bank is packed as one [E*N][K] matrix."""
+    lib = B.load()
+    assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous()
+    k = t.shape[-1]
+    out = torch.empty_like(t)
+    st = lib.dg_pack_weight(_stream(), t.data_ptr(), out.data_ptr(), t.numel() // k, k)
+    if st != B.DG_OK:
+        raise B.DGError(st, f"dg_pack_weight failed for shape {tuple(t.shape)}")
+    return out
+
+
 class Engine:
-    """One context: weights (bf16, on the GPU), KV cache and workspace tensors."""
+    """One context: weights (bf16, on the GPU), KV cache and workspace tensors.
+
+    `layers` holds row-major tensors (the synth/oracle convention); the
+    streamed projection matrices are repacked on the GPU into the library's
+    fragment-major layout, and only the packed copies are kept."""
 
     def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
                  embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
@@ -45,12 +62,15 @@ class Engine:
         c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
         c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
         self.c_cfg = c
-        self._keep = [embed, final_norm] + [t for lw in layers for t in lw.values()]
+        self._keep = [embed, final_norm]
         arr = (B.DGLayerWeights * max(1, len(layers)))()
         for i, lw in enumerate(layers):
             for name in LAYER_TENSORS:
                 t = lw[name]
                 assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == dev, name
+                if name in B.PACKED_FIELDS:
+                    t = pack_weight(t)
+                self._keep.append(t)
                 setattr(arr[i], name, t.data_ptr())
         self._layer_arr = arr
         w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr)
@@ -102,6 +122,14 @@ class Engine:
             n *= s
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
         return self.ws[off:off + nbytes].view(dtype).view(*shape)
+
+    def moe_counters(self) -> Dict[str, int]:
+        """Running expert-kernel counters kept in the workspace (waits for the
+        GPU): spin timeouts, touched experts summed over layer calls, calls."""
+        w = self.ws_view("items", torch.int32, (B.ITEMS_PERMUTE_CALLS + 2,)).cpu()
+        w64 = w[B.ITEMS_TOUCHED_TOTAL:B.ITEMS_PERMUTE_CALLS + 2].view(torch.int64)
+        return {"spin_timeouts": int(w[B.ITEMS_SPIN_TIMEOUTS]), "touched_total": int(w64[0]),
+                "permute_calls": int(w64[1])}
 
     def cache_len(self, req: int) -> int:
         return self.lib.dg_cache_len(self.ctx, req)

@@ -22,7 +22,9 @@
  *     masks. The library never allocates device memory; it keeps the raw
  *     pointers given to dg_create, which must stay valid until dg_destroy.
  *     The dg_ctx itself is host memory owned by the library.
- *   - Weights are bf16, row-major, in the [out][in] convention (y = x W^T).
+ *   - Weights are bf16 in the [out][in] convention (y = x W^T). Norm gains,
+ *     the router and the embedding are row-major; the streamed projection
+ *     matrices are in the fragment-major layout made by dg_pack_weight.
  *   - Every call validates its arguments and the cache capacity before it
  *     enqueues anything; on DG_EINVAL / DG_ECAPACITY nothing has been
  *     launched and no state changed. Work is enqueued asynchronously on the
@@ -72,7 +74,11 @@ typedef struct dg_config {
  *   attn_norm [d]        w_qkv [(Hq+2Hkv)*dh][d]   (q heads, then k, then v)
  *   w_o [d][Hq*dh]       moe_norm [d]              w_router [E][d]
  *   w_gate, w_up [E][F][d]   w_down [E][d][F]
- *   ws_gate, ws_up [Fs][d]   ws_down [d][Fs]       (shared expert)          */
+ *   ws_gate, ws_up [Fs][d]   ws_down [d][Fs]       (shared expert)
+ * attn_norm, moe_norm and w_router are row-major. w_qkv, w_o, w_gate, w_up,
+ * w_down, ws_gate, ws_up and ws_down are fragment-major: the shapes above,
+ * each converted with dg_pack_weight (an expert bank [E][N][K] is converted
+ * as one [E*N][K] matrix). */
 typedef struct dg_layer_weights {
   const void *attn_norm, *w_qkv, *w_o, *moe_norm, *w_router;
   const void *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
@@ -121,6 +127,19 @@ typedef struct dg_step_args {
 } dg_step_args;
 
 typedef struct dg_ctx dg_ctx;
+
+/* Convert a row-major bf16 matrix W [n][k] into the fragment-major layout of
+ * the streamed projection weights: element W[i][j] moves to index
+ *   (i/16)*16*k + (j/64)*1024 + ((j%64)/32)*512 + (((j%32)/8)*16 + i%16)*8 + j%8.
+ * Each 16-row block is then contiguous, and every 64-wide step of it lists,
+ * for each half q, the eight consecutive elements lane L of a wavefront
+ * feeds the bf16 matrix core (row i%16 = L%16, elements 32q + 8(L/16) ..)
+ * in lane order, so the kernels load weights in whole 1 KB runs.
+ * d_src and d_dst are device buffers of n*k elements that must not overlap;
+ * the copy is enqueued on stream. DG_EINVAL if a pointer is NULL, the
+ * buffers overlap, or n % 16 != 0 or k % 64 != 0. A launch failure returns
+ * DG_EHIP. Needs no context. */
+dg_status dg_pack_weight(void *stream, const void *d_src, void *d_dst, int64_t n, int32_t k);
 
 /* Bytes of KV cache for ONE request slot:
  * n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2.

@@ -23,14 +23,31 @@ extern "C" {
  *   w        fp32 [rows][k]          softmax over the selected logits
  *   wslot    int32 [rows*k]          t*k + j of each expert slot (index into w)
  *   cnt      int32 [E]; off int32 [E+1]
- *   items    int32 [2][260]          work-item offsets of the grouped expert
- *                                    kernels (gate/up, then down) per group
+ *   items    int32 words             expert work list: per group (0 = shared
+ *                                    expert, 1+e = routed expert e) the item
+ *                                    and row-chunk offsets, the queue head,
+ *                                    the spin-timeout counter (word
+ *                                    DG_ITEMS_SPIN_TIMEOUTS) and per-chunk
+ *                                    completion counters
  *   perm     int32 [rows*k]          token of each expert slot
  *   slot     int32 [rows][k]         slot of each (token, choice)
  *   hid      bf16 [rows*k][F]        routed expert SwiGLU activations
  *   hid_s    bf16 [rows][Fs]         shared expert SwiGLU activations
  *   y        fp32 [rows*k][d]        routed expert outputs (weighted)
  *   stats    dg_row_stats [rows]     per-row LM-head statistics          */
+/* Word of the items buffer that counts expert-kernel waits which ran out of
+ * their poll budget instead of seeing their input published. A correct run
+ * leaves it unchanged; the library never resets it. */
+#define DG_ITEMS_SPIN_TIMEOUTS 409
+
+/* Running routing statistics in the items buffer (uint64 at these word
+ * indices, never reset by the library): the number of experts that received
+ * at least one row, summed over permutation calls, and the number of calls.
+ * Their ratio over an interval is the mean number of experts whose weights a
+ * layer had to stream. */
+#define DG_ITEMS_TOUCHED_TOTAL 410
+#define DG_ITEMS_PERMUTE_CALLS 412
+
 typedef struct dg_ws_layout {
   size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
       slot, hid, hid_s, y, lm_part, stats, ids, total;
@@ -72,8 +89,7 @@ enum {
   DG_STAGE_ROUTER,      /* router logits + top-k + softmax (fused) */
   DG_STAGE_TOPK,        /* top-k from given logits (test entry point only) */
   DG_STAGE_PERMUTE,     /* token -> expert permutation */
-  DG_STAGE_GATEUP,      /* grouped expert gate/up + SwiGLU (routed + shared) */
-  DG_STAGE_DOWN,        /* grouped expert down projection (routed + shared) */
+  DG_STAGE_EXPERTS,     /* grouped experts: gate/up + SwiGLU, then down (routed + shared) */
   DG_STAGE_COMBINE,     /* weighted combine + residual */
   DG_STAGE_LMHEAD,      /* LM head with fused vocabulary statistics */
   DG_STAGE_MERGE,       /* vocabulary statistics merge */

@@ -132,3 +132,16 @@ def test_argument_and_capacity_errors_launch_nothing(lib):
         assert lib.dg_reset(h, 9) == B.DG_EINVAL
     finally:
         lib.dg_destroy(h)
+
+
+def test_pack_weight_rejects_bad_arguments(lib):
+    # every check runs on the host before a launch: fake addresses are safe
+    ok_src, ok_dst = 0x100000, 0x900000
+    assert lib.dg_pack_weight(None, None, ok_dst, 16, 64) == B.DG_EINVAL
+    assert lib.dg_pack_weight(None, ok_src, None, 16, 64) == B.DG_EINVAL
+    assert lib.dg_pack_weight(None, ok_src, ok_dst, 24, 64) == B.DG_EINVAL   # n % 16
+    assert lib.dg_pack_weight(None, ok_src, ok_dst, 16, 96) == B.DG_EINVAL   # k % 64
+    assert lib.dg_pack_weight(None, ok_src, ok_dst, 0, 64) == B.DG_EINVAL
+    # 16 x 64 bf16 = 2048 bytes: destinations overlapping the source are refused
+    assert lib.dg_pack_weight(None, ok_src, ok_src + 2046, 16, 64) == B.DG_EINVAL
+    assert lib.dg_pack_weight(None, ok_src + 2046, ok_src, 16, 64) == B.DG_EINVAL

@@ -37,6 +37,33 @@ def test_synth_generator_identical_on_gpu_and_cpu():
     assert torch.equal(synth.make_prompt(999, 262144, 3), synth.make_prompt(999, 262144, 3, device="cuda").cpu())
 
 
+# ------------------------------------------------------------------------ weight layout
+
+def _fragment_major_reference(w):
+    """The packed layout by axis permutation: W[16nb + r][64ks + 32q + 8g + e]
+    goes to position (nb, ks, q, g, r, e)."""
+    n, k = w.shape
+    t = w.reshape(n // 16, 16, k // 64, 2, 4, 8)          # nb, r, ks, q, g, e
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 4, 1, 5)).reshape(n, k)
+
+
+@pytest.mark.parametrize("shape", [(16, 64), (48, 192), (3 * 704, 256), (4096, 2048)])
+def test_pack_weight_bit_exact(shape):
+    from block_discrete_diffusion_dg_amd.engine import pack_weight
+    say(f"[pack] shape={shape}")
+    w = synth.hashed_normal(shape, 11 + shape[0], 0.02, "cuda")
+    got = pack_weight(w).cpu().view(torch.int16).numpy()
+    ref = _fragment_major_reference(w.cpu().view(torch.int16).numpy())
+    assert np.array_equal(got, ref)
+    # spot-check the index formula of the header on a few elements
+    n, k = shape
+    wc = w.cpu().view(torch.int16).numpy()
+    for i, j in [(0, 0), (n - 1, k - 1), (17 % n, 33 % k), (n // 2, 63 % k)]:
+        idx = (i // 16) * 16 * k + (j // 64) * 1024 + ((j % 64) // 32) * 512 + \
+            (((j % 32) // 8) * 16 + i % 16) * 8 + j % 8
+        assert got.reshape(-1)[idx] == wc[i, j]
+
+
 # ------------------------------------------------------------------------ router
 
 def _router_logits(rows, E, seed):
@@ -55,10 +82,15 @@ def test_route_bit_exact(model, rows):
     say(f"[route] E={model.n_experts} k={model.top_k} rows={rows}")
     eng, _ = _zero_layer_engine(model, max_rows=max(rows, model.canvas))
     z = _router_logits(rows, model.n_experts, rows)
+    c0 = eng.moe_counters()
     out = eng.test_route(z.cuda())
     torch.cuda.synchronize()
+    c1 = eng.moe_counters()
     idx, w = om.route(z.double().numpy(), model.top_k)
     cnt, off, perm, slot = om.permutation(idx, model.n_experts)
+    # running statistics: one call, touching exactly the experts with rows
+    assert c1["permute_calls"] - c0["permute_calls"] == 1
+    assert c1["touched_total"] - c0["touched_total"] == int((cnt > 0).sum())
     assert np.array_equal(out["idx"].cpu().numpy(), idx)
     assert np.abs(out["w"].cpu().double().numpy() - w).max() < 2e-6
     assert np.array_equal(out["cnt"].cpu().numpy(), cnt)
@@ -232,3 +264,5 @@ def test_layer_parity(name, causal):
             e = idx_gpu[t, j]
             ref = w_gpu[t, j] * om.swiglu(u2[t:t + 1], lw["w_gate"][e], lw["w_up"][e], lw["w_down"][e])[0]
             assert max_rel(y[slot_gpu[t, j]], ref) <= REL_TOL, (t, j)
+    # every wait of the expert kernel saw its input published in time
+    assert eng.moe_counters()["spin_timeouts"] == 0

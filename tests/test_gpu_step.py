@@ -134,3 +134,4 @@ def test_step_is_deterministic_and_batch_matches_single():
     b = stats_fields(st1)
     assert max_rel(b["max_logit"], a["max_logit"]) < 1e-4
     assert torch.equal(a["argmax"], b["argmax"])
+    assert eng.moe_counters()["spin_timeouts"] == 0
