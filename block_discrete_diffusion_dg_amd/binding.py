@@ -58,7 +58,7 @@ class DGStepArgs(ctypes.Structure):
 
 
 WS_FIELDS = ("h", "u", "q", "attn_o", "attn_part", "attn_ml", "rope", "z", "idx", "w", "wslot",
-             "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "stats", "ids",
+             "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "stats", "ids", "ss", "zpart", "sync",
              "total")
 
 

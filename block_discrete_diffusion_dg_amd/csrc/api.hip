@@ -59,6 +59,9 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.lm_part = take(R * (size_t)lmhead_parts(c.vocab) * 16);
   L.stats = take(R * sizeof(dg_row_stats));
   L.ids = take(R * 4);
+  L.ss = take(R * (d / 64) * 4);
+  L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
+  L.sync = take(256 * 4);
   L.total = o;
   return L;
 }
@@ -80,8 +83,8 @@ const char* check_config(const dg_config& c) {
   if (c.max_requests <= 0) return "max_requests must be positive";
   if (c.max_rows < c.canvas || c.max_rows > DG_MAX_REQ * c.canvas)
     return "max_rows must lie in [canvas, 16*canvas]";
-  if ((size_t)c.max_rows * (((c.n_experts + 31) / 32) * 4 + c.top_k) > 57344)
-    return "max_rows * (4*ceil(n_experts/32) + top_k) must not exceed 56 KiB (routing tables in LDS)";
+  if (permute_lds_bytes(c.max_rows, c.n_experts, c.top_k) > 57344)
+    return "12 * n_experts * ceil(max_rows/64) must not exceed 56 KiB (routing tables in LDS)";
   if (c.max_ctx < 2 * c.canvas) return "max_ctx must hold at least two blocks";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.tau_first > 0.f) || !(c.tau_last > 0.f))
     return "rms_eps >= 0, rope_theta > 0 and temperatures > 0 required";
@@ -187,16 +190,17 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   bf16_t* u = c->buf<bf16_t>(L.u);
 
   STAGE(DG_STAGE_QKV, launch_qkv(s, u, rows, d, w.w_qkv, c->buf<bf16_t>(L.q), c->kv, l, g.n_q_heads,
-                                 g.n_kv_heads, g.head_dim, c->buf<float2>(L.rope), rt));
+                                 g.n_kv_heads, g.head_dim, c->buf<float2>(L.rope), rt, c->buf<int32_t>(L.sync)));
   if (kv_only) return;
   const int ns = attn_splits(rt, g.n_q_heads, g.n_kv_heads, g.max_rows);
   STAGE(DG_STAGE_ATTN, launch_attention(s, c->buf<bf16_t>(L.q), c->kv, l, rt, g.n_q_heads, g.n_kv_heads,
                                        g.head_dim, causal, ns, c->buf<float>(L.attn_part),
                                        c->buf<float2>(L.attn_ml), c->buf<bf16_t>(L.attn_o)));
-  STAGE(DG_STAGE_OPROJ, launch_resid(s, c->buf<bf16_t>(L.attn_o), rows, g.n_q_heads * g.head_dim, w.w_o, d, h));
-  STAGE(DG_STAGE_ROUTER, launch_norm_router_topk(s, h, w.moe_norm, rows, d, g.rms_eps, w.w_router, g.n_experts,
-                                                 g.top_k, u, c->buf<float>(L.z), c->buf<int32_t>(L.idx),
-                                                 c->buf<float>(L.w)));
+  STAGE(DG_STAGE_OPROJ, launch_resid(s, c->buf<bf16_t>(L.attn_o), rows, g.n_q_heads * g.head_dim, w.w_o, d, h,
+                                     c->buf<float>(L.ss)));
+  STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,
+                                       g.n_experts, g.top_k, u, c->buf<float>(L.z), c->buf<float>(L.zpart),
+                                       c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w)));
   int32_t* items = c->buf<int32_t>(L.items);
   const int ch = moe_rows_per_chunk(rows, g.n_experts, g.top_k);
   STAGE(DG_STAGE_PERMUTE, launch_permute(s, c->buf<int32_t>(L.idx), rows, g.n_experts, g.top_k, ch,

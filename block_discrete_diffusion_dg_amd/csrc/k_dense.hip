@@ -33,12 +33,14 @@ struct QkvArgs {
   int layer, Hq, Hkv, dh;
   const float2* rope;  // [rows][dh/2] (cos, sin)
   ReqTable rt;
+  int32_t* sync;  // router row-block counters, zeroed here for the layer's router
 };
 
 __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, int rows, int d,
                                                   const bf16_t* __restrict__ w, QkvArgs p) {
   using T = StreamTile<DMT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
+  if (blockIdx.x == 0 && p.sync) p.sync[threadIdx.x] = 0;
   const int dh = p.dh, half = dh >> 1;
   const int NT = (p.Hq + 2 * p.Hkv) * half / 64, MC = div_up(rows, T::CH);
   int nt, mc;
@@ -81,12 +83,15 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
     }
 }
 
-// h[row][col] += (A W^T)[row][col]
+// h[row][col] += (A W^T)[row][col]; with ss, also the sum over the
+// work-group's 64 columns of the updated h[row][col]^2 -> ss[nt][row] (the
+// MoE pre-norm then needs no second pass over whole rows).
 __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a, int rows, int K,
                                                     const bf16_t* __restrict__ w, int N,
-                                                    float* __restrict__ h) {
+                                                    float* __restrict__ h, float* __restrict__ ss) {
   using T = StreamTile<DMT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
+  __shared__ float red[4][T::CH];
   const int NT = N / 64, MC = div_up(rows, T::CH);
   int nt, mc;
   tile_coords(NT, MC, nt, mc);
@@ -100,22 +105,39 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + 16 * mt + 4 * grp + r;
-      if (row < rows) h[(int64_t)row * N + col] += acc[mt][r];
+      float sq = 0.f;
+      if (row < rows) {
+        const float v = h[(int64_t)row * N + col] + acc[mt][r];
+        h[(int64_t)row * N + col] = v;
+        sq = v * v;
+      }
+      // sum over the wave's 16 columns (lanes of the same group)
+      sq += __shfl_xor(sq, 1, WAVE);
+      sq += __shfl_xor(sq, 2, WAVE);
+      sq += __shfl_xor(sq, 4, WAVE);
+      sq += __shfl_xor(sq, 8, WAVE);
+      if (l16 == 0) red[wave][16 * mt + 4 * grp + r] = sq;
     }
+  if (!ss) return;
+  __syncthreads();
+  if (threadIdx.x < T::CH && row0 + (int)threadIdx.x < rows) {
+    const int i = threadIdx.x;
+    ss[(int64_t)nt * rows + row0 + i] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+  }
 }
 
 }  // namespace
 
 void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
                 const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
-                const ReqTable& rt) {
-  QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt};
+                const ReqTable& rt, int32_t* sync) {
+  QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt, sync};
   const int NT = (Hq + 2 * Hkv) * (dh / 2) / 64;
   const int MC = div_up(rows, StreamTile<DMT>::CH);
   hipLaunchKernelGGL(qkv_kernel, dim3(NT * MC), dim3(256), 0, s, u, rows, d, w, p);
 }
 
-void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h) {
+void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h, float* ss) {
   const int MC = div_up(rows, StreamTile<DMT>::CH);
-  hipLaunchKernelGGL(resid_kernel, dim3((N / 64) * MC), dim3(256), 0, s, a, rows, K, w, N, h);
+  hipLaunchKernelGGL(resid_kernel, dim3((N / 64) * MC), dim3(256), 0, s, a, rows, K, w, N, h, ss);
 }

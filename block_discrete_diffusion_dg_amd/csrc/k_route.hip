@@ -11,191 +11,254 @@ size_t permute_lds_bytes(int rows, int E, int k);
 
 namespace {
 
-// One wave selects the top-k (k <= 8) of E <= 256 logits, lane l holding
-// experts l, l+64, l+128, l+192 in v[0..3]: k rounds of a wave arg-max (ties
-// to the lower expert id) pick the experts in descending order; lane 0 writes
-// them and the softmax of the picked logits.
-__device__ __forceinline__ void wave_topk(const float (&v)[4], int E, int k, int lane,
-                                          int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  bool taken[4] = {false, false, false, false};
+// Top-k (k <= 8) of E <= 128 logits for each of RB = 16 rows: every 16-lane
+// group of the work-group's four waves takes one row, lane l16 holding the
+// logits of experts l16 + 16m (m < 8; experts past E read as -inf). Each of k
+// rounds takes the group's arg-max (lane-local over the 8 values, then four
+// xor steps inside the group; on equal values the lower expert id wins) and
+// retires it. The selection comes out in descending order; the group's first
+// lane then writes the experts and the softmax over the selected logits,
+// w_j = exp(z_(j) - z_(0)) / sum_i exp(z_(i) - z_(0)), summed in that order.
+// zl: LDS tile [16][E + 1]; rows at or past `rows` are skipped.
+constexpr int RB = 16;  // rows per block
+
+__device__ __forceinline__ void block_topk16(const float* zl, int E, int k, int t0, int rows, int32_t* __restrict__ idx,
+                             float* __restrict__ w) {
+  const int tid = threadIdx.x, r = tid >> 4, l16 = tid & 15;
+  const float* zr = zl + r * (E + 1);
+  float v[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int e = l16 + 16 * m;
+    v[m] = e < E ? zr[e] : -INFINITY;
+  }
   float sel[8];
   int sid[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j >= k) break;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    // lane-local: experts ascend with m, so a strict '>' keeps the lower id
+    float bv = v[0];
+    int bi = l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !taken[i]) argmax_merge(bv, bi, v[i], e);
+    for (int m = 1; m < 8; ++m)
+      if (v[m] > bv) {
+        bv = v[m];
+        bi = l16 + 16 * m;
+      }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, 16);
+      const int oi = __shfl_xor(bi, o, 16);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(bv, o, WAVE);
-      const int i2 = __shfl_xor(bi, o, WAVE);
-      argmax_merge(bv, bi, v2, i2);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (bi == lane + 64 * i) taken[i] = true;
+    for (int m = 0; m < 8; ++m)
+      if (bi == l16 + 16 * m) v[m] = -INFINITY;
     sel[j] = bv;
     sid[j] = bi;
   }
-  if (lane == 0) {
-    const float m = sel[0];
+  const int t = t0 + r;
+  if (l16 == 0 && t < rows) {
     float ex[8], sum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= k) break;
-      ex[j] = expf(sel[j] - m);
+      ex[j] = expf(sel[j] - sel[0]);
       sum += ex[j];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= k) break;
-      idx_out[j] = sid[j];
-      w_out[j] = ex[j] / sum;
+      idx[(int64_t)t * k + j] = sid[j];
+      w[(int64_t)t * k + j] = ex[j] / sum;
     }
   }
 }
 
-// Top-k from given router logits: one wave per token.
+// Top-k from given router logits: 16 rows per work-group.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int rows, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= rows) return;
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? z[(int64_t)t * E + e] : -INFINITY;
+  __shared__ float zl[RB * 129];
+  const int t0 = blockIdx.x * RB;
+  for (int i = threadIdx.x; i < RB * E; i += 256) {
+    const int r = i / E, t = min(t0 + r, rows - 1);
+    zl[r * (E + 1) + i % E] = z[(int64_t)t * E + i % E];
   }
-  wave_topk(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
+  __syncthreads();
+  block_topk16(zl, E, k, t0, rows, idx, w);
 }
 
-// MoE pre-norm, router logits and top-k for 8 token rows per work-group.
-//  1. RMSNorm: wave w normalises rows 2w and 2w+1; u goes to the workspace
-//     (the experts' input rows) and to an LDS tile (bf16, [8][d + 8]).
-//  2. z = u W_r^T on the matrix cores: wave w reduces over its quarter of d
-//     for all experts (8 subtiles of 16 experts, indices clamped to E-1; the
-//     A rows 8..15 repeat rows 0..7 and are discarded).
-//  3. z = sum of the four partial sums (fixed order); wave w selects the
-//     experts of rows 2w and 2w+1 (wave_topk).
-constexpr int RT_ROWS = 8;
+// MoE pre-norm, router logits and top-k. Work-group (row block rb of RB = 16
+// rows, K quarter ks) of a grid of ceil(rows/16) x 4:
+//  1. issues the loads of its router weight fragments (expert rows
+//     16*(2w+n) + l16 of wave w, clamped to E-1, over its quarter of d)
+//     before anything else: they depend on nothing;
+//  2. 1/rms of its rows from the output projection's per-64-column sums of
+//     squares (summed in a fixed order);
+//  3. u = bf16(h / rms * gain) on its quarter of d -> workspace (the experts'
+//     input rows) and an LDS tile;
+//  4. partial logits of its quarter on the matrix cores, written through to
+//     device-coherent memory, then counts itself in for the row block;
+//  5. the last of the four to arrive adds the four partials in quarter
+//     order (deterministic whatever the arrival order), stores z, resets the
+//     counter, and selects each row's experts (block_topk16).
+constexpr int RKS = 4;     // K quarters
+constexpr int RSTEPS = 8;  // 32-wide K steps whose weights are loaded at once
 
-__global__ __launch_bounds__(256) void norm_router_topk_kernel(
-    const float* __restrict__ h, const bf16_t* __restrict__ gain, int rows, int d, float eps,
-    const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
-    int32_t* __restrict__ idx, float* __restrict__ w) {
+__device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
+
+__global__ __launch_bounds__(256) void router_kernel(
+    const float* __restrict__ h, const float* __restrict__ ss, const bf16_t* __restrict__ gain, int rows, int d,
+    float eps, const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
+    float* __restrict__ zpart, int32_t* __restrict__ sync, int32_t* __restrict__ idx, float* __restrict__ w) {
   extern __shared__ __align__(16) char rt_lds[];
-  const int LDU = d + 8;
-  bf16_t* Us = reinterpret_cast<bf16_t*>(rt_lds);   // [8][LDU]
-  float* part = reinterpret_cast<float*>(rt_lds);   // after phase 2: [4][8][E], then z [8][E]
+  const int kq = d / RKS, LDA = kq + 8, nct = d / 64;
+  bf16_t* As = reinterpret_cast<bf16_t*>(rt_lds);                    // [RB][LDA]
+  float* zt = reinterpret_cast<float*>(rt_lds + RB * LDA * 2);       // [RB][E + 1]
+  float* sq = zt + RB * (E + 1);                                     // [RB][nct]
+  __shared__ float s_inv[RB];
+  __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int t0 = blockIdx.x * RT_ROWS;
+  const int rb = blockIdx.x / RKS, ks = blockIdx.x % RKS;
+  const int t0 = rb * RB, kb = ks * kq, nk = kq / 32;
+  // quarter stride in rows, a multiple of RB: every row block's partials
+  // fill whole 128-byte lines (E % 8 == 0), shared with no other block
+  const int zs = div_up(rows, RB) * RB;
 
-  for (int i = 0; i < 2; ++i) {
-    const int rr = wave * 2 + i, t = t0 + rr;
-    bf16_t* urow = Us + rr * LDU;
-    if (t < rows) {
-      const float* x = h + (int64_t)t * d;
-      float ss = 0.f;
-      for (int c = lane * 4; c < d; c += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(x + c);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  // 1. weight fragments of the first RSTEPS steps
+  const bf16_t* brow[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) brow[n] = wr + (int64_t)min(16 * (2 * wave + n) + l16, E - 1) * d + kb + 8 * grp;
+  u32x4 bf[RSTEPS][2];
+#pragma unroll
+  for (int st = 0; st < RSTEPS; ++st)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) bf[st][n] = ld16(brow[n] + min(st, nk - 1) * 32);
+
+  // 2. 1/rms per row: all partial sums loaded at once, added in tile order
+  for (int i = tid; i < RB * nct; i += 256) {
+    const int r = i / nct, ct = i % nct, t = t0 + r;
+    sq[i] = t < rows ? ss[(int64_t)ct * rows + t] : 0.f;
+  }
+  __syncthreads();
+  if (tid < RB) {
+    float acc = 0.f;
+    for (int ct = 0; ct < nct; ++ct) acc += sq[tid * nct + ct];
+    s_inv[tid] = 1.0f / sqrtf(acc / (float)d + eps);
+  }
+  __syncthreads();
+
+  // 3. normalised rows on this quarter (rows past the end are zero); loads of
+  // a batch of up to 8 float4 per thread are all issued before any use
+  for (int i0 = tid * 4; i0 < RB * kq; i0 += 8 * 1024) {
+    float4 hv[8];
+    u32x2 gv[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int i = i0 + b * 1024, r = i / kq, c = i % kq, t = min(t0 + r, rows - 1);
+      const bool ok = i < RB * kq;
+      hv[b] = *reinterpret_cast<const float4*>(h + (int64_t)t * d + kb + (ok ? c : 0));
+      gv[b] = *reinterpret_cast<const u32x2*>(gain + kb + (ok ? c : 0));
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int i = i0 + b * 1024, r = i / kq, c = i % kq, t = t0 + r;
+      if (i >= RB * kq) break;
+      u32x2 pk = {0u, 0u};
+      if (t < rows) {
+        const float inv = s_inv[r];
+        const float4 v = hv[b];
+        pk = u32x2{pack_bf16x2(v.x * inv * __uint_as_float(gv[b].x << 16),
+                               v.y * inv * __uint_as_float(gv[b].x & 0xffff0000u)),
+                   pack_bf16x2(v.z * inv * __uint_as_float(gv[b].y << 16),
+                               v.w * inv * __uint_as_float(gv[b].y & 0xffff0000u))};
+        *reinterpret_cast<u32x2*>(u + (int64_t)t * d + kb + c) = pk;
       }
-      ss = wave_sum(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-      for (int c = lane * 4; c < d; c += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(x + c);
-        const u32x2 pk = {pack_bf16x2(v.x * inv * bf2f(gain[c]), v.y * inv * bf2f(gain[c + 1])),
-                          pack_bf16x2(v.z * inv * bf2f(gain[c + 2]), v.w * inv * bf2f(gain[c + 3]))};
-        *reinterpret_cast<u32x2*>(u + (int64_t)t * d + c) = pk;
-        *reinterpret_cast<u32x2*>(urow + c) = pk;
-      }
-    } else {
-      for (int c = lane * 4; c < d; c += 256) *reinterpret_cast<u32x2*>(urow + c) = u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(As + r * LDA + c) = pk;
     }
   }
   __syncthreads();
 
-  const int kq = d / 4, kb = wave * kq;
-  const bf16_t* arow = Us + (l16 & 7) * LDU + kb + 8 * grp;
-  const bf16_t* brow[8];
+  // 4. partial logits: 16 rows x 32 experts per wave over the quarter
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int s0 = 0; s0 < nk; s0 += RSTEPS) {
+    if (s0 > 0) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n) brow[n] = wr + (int64_t)min(16 * n + l16, E - 1) * d + kb + 8 * grp;
-  f32x4 acc[8];
+      for (int st = 0; st < RSTEPS; ++st)
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Weight loads run two 32-wide steps ahead (three register sets, loop
-  // unrolled by three; steps past the end reload the last step and are
-  // multiplied by a zeroed A operand).
-  const int nk = kq / 32;
-  u32x4 b[3][8];
-  auto issue = [&](auto S, int st) {
-    constexpr int s = decltype(S)::value;
-    const int k0 = min(st, nk - 1) * 32;
+        for (int n = 0; n < 2; ++n) bf[st][n] = ld16(brow[n] + min(s0 + st, nk - 1) * 32);
+    }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) b[s][n] = ld16(brow[n] + k0);
-  };
-  auto compute = [&](auto S, int st) {
-    constexpr int s = decltype(S)::value;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const u32x4 a0 = ld16(arow + min(st, nk - 1) * 32);
-    const u32x4 a = st < nk ? a0 : zero;
+    for (int st = 0; st < RSTEPS; ++st) {
+      const u32x4 a0 = ld16(As + l16 * LDA + min(s0 + st, nk - 1) * 32 + 8 * grp);
+      const u32x4 a = s0 + st < nk ? a0 : zero;  // steps past the end add nothing
 #pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = mfma_bf16(a, b[s][n], acc[n]);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  issue(I0{}, 0);
-  issue(I1{}, 1);
-  for (int it = 0; it < nk; it += 3) {
-    issue(I2{}, it + 2);
-    compute(I0{}, it);
-    issue(I0{}, it + 3);
-    compute(I1{}, it + 1);
-    issue(I1{}, it + 4);
-    compute(I2{}, it + 2);
-  }
-  __syncthreads();  // the u tile is no longer read: reuse the LDS for partial sums
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int e = 16 * n + l16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = 4 * grp + r;  // rows 0..15 of the MFMA tile; 8..15 are repeats
-      if (rr < RT_ROWS && e < E) part[(wave * RT_ROWS + rr) * E + e] = acc[n][r];
+      for (int n = 0; n < 2; ++n) acc[n] = mfma_bf16(a, bf[st][n], acc[n]);
     }
   }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int e = 16 * (2 * wave + n) + l16;
+    if (e < E)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) zt[(4 * grp + r) * E + e] = acc[n][r];  // dense [RB][E] here
+  }
   __syncthreads();
-  float* zl = part + 4 * RT_ROWS * E;
-  for (int i = tid; i < RT_ROWS * E; i += 256) {
-    const float v = part[i] + part[RT_ROWS * E + i] + part[2 * RT_ROWS * E + i] + part[3 * RT_ROWS * E + i];
-    zl[i] = v;
+  for (int i = tid * 4; i < RB * E; i += 1024) {
     const int t = t0 + i / E;
-    if (t < rows) z[(int64_t)t * E + (i % E)] = v;
+    if (t < rows)
+      store16_coherent(zpart + ((int64_t)ks * zs + t) * E + i % E, *reinterpret_cast<const u32x4*>(zt + i));
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(sync + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == RKS - 1;
+    if (s_last) __hip_atomic_store(sync + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  for (int i = 0; i < 2; ++i) {
-    const int rr = wave * 2 + i, t = t0 + rr;
-    if (t >= rows) break;
-    float v[4];
+  if (!s_last) return;
+
+  // 5. the last arrival: z = ((p0 + p1) + p2) + p3, then top-k per row. The
+  // block's partial lines are read only here, after all four were written,
+  // and caches start the kernel invalidated: no cache holds a stale copy.
+  // (E <= 128: at most 8 entries per thread, every load issued before the sums)
+  float pv[8][RKS];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? zl[rr * E + e] : -INFINITY;
-    }
-    wave_topk(v, E, k, lane, idx + (int64_t)t * k, w + (int64_t)t * k);
+  for (int b = 0; b < 8; ++b) {
+    const int i = tid + 256 * b, t = min(t0 + i / E, rows - 1), e = i % E;
+    const bool ok = i < RB * E;
+#pragma unroll
+    for (int q = 0; q < RKS; ++q) pv[b][q] = ok ? zpart[((int64_t)q * zs + t) * E + e] : 0.f;
   }
+  __syncthreads();  // the dense staging view of zt is no longer read
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int i = tid + 256 * b, r = i / E, t = t0 + r, e = i % E;
+    if (i >= RB * E) break;
+    float v = 0.f;
+    if (t < rows) {
+      v = pv[b][0];
+#pragma unroll
+      for (int q = 1; q < RKS; ++q) v += pv[b][q];
+      z[(int64_t)t * E + e] = v;
+    }
+    zt[r * (E + 1) + e] = v;
+  }
+  __syncthreads();
+  block_topk16(zt, E, k, t0, rows, idx, w);
 }
 
 // Exclusive prefix sum of n <= 320 ints by one wave (5 consecutive per lane);
 // out[n] receives the total.
-__device__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int lane) {
+__device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int lane) {
   int local[5], acc = 0;
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
@@ -219,14 +282,18 @@ __device__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int 
   if (lane == 63) out[n] = inc;
 }
 
-// Single work-group of 1024 threads (16 waves).
-//  1. mark (token, expert) bits in LDS, keep the choices as bytes in LDS;
-//  2. cnt[e] = popcount of ballots over the token column of expert e;
-//  3. off = exclusive prefix sum of cnt; work-item offsets of the grouped
-//     expert kernels (E routed groups + the shared expert as group E, each
-//     cut into chunks of ch rows, times its column tiles);
-//  4. slot of (t, e) = off[e] + number of earlier tokens of e (ballot rank);
-//     widx[slot] = t*k + j locates the slot's routing weight w[t][j].
+// Single work-group of 1024 threads (16 waves); nb = ceil(rows / 64) token
+// blocks (nb <= 64).
+//  1. mask[e][b] = bit set of the tokens of block b that chose expert e
+//     (64-bit LDS atomic OR per (token, choice) pair);
+//  2. one wave per expert: popcounts of its masks, prefix over the blocks ->
+//     cnt[e] and the tokens of e in earlier blocks;
+//  3. off = exclusive prefix sum of cnt; base[e][b] = off[e] + earlier
+//     tokens; the work list of the expert kernel (groups: 0 = shared expert,
+//     1 + e = routed e) as exclusive item and row-chunk offsets;
+//  4. every pair (t, j) with expert e = idx[t][j] takes slot
+//     base[e][t/64] + popcount(mask[e][t/64] below t): tokens ascending
+//     inside an expert, three stores per pair (slot[t][j] coalesced).
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int rows, int E,
                                                        int k, int ch, int ft_routed, int ft_shared,
                                                        int dt, int32_t* __restrict__ cnt,
@@ -235,31 +302,33 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ slot,
                                                        int32_t* __restrict__ widx,
                                                        int32_t* __restrict__ items) {
-  extern __shared__ uint32_t dyn[];  // bits [rows][ceil(E/32)], then choices [rows*k] bytes
+  extern __shared__ __align__(8) char pm_lds[];
+  const int nb = (rows + 63) / 64;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(pm_lds);  // [E][nb]
+  int32_t* base = reinterpret_cast<int32_t*>(mask + (size_t)E * nb);       // [E][nb]
   __shared__ int32_t s_cnt[257];
   __shared__ int32_t s_off[258];
   __shared__ int32_t s_ngu[MOE_MAX_GROUPS], s_ndn[MOE_MAX_GROUPS], s_nch[MOE_MAX_GROUPS];
   __shared__ int32_t s_igu[MOE_MAX_GROUPS + 1], s_idn[MOE_MAX_GROUPS + 1], s_ich[MOE_MAX_GROUPS + 1];
-  const int words = (E + 31) / 32;
-  uint32_t* bits = dyn;
-  uint8_t* choice = reinterpret_cast<uint8_t*>(dyn + rows * words);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < rows * words; i += 1024) bits[i] = 0u;
+  const int pairs = rows * k;
+  for (int i = tid; i < E * nb; i += 1024) mask[i] = 0ull;
   __syncthreads();
-  for (int i = tid; i < rows * k; i += 1024) {
+  for (int i = tid; i < pairs; i += 1024) {
     const int t = i / k, e = idx[i];
-    choice[i] = (uint8_t)e;
-    atomicOr(&bits[t * words + (e >> 5)], 1u << (e & 31));
+    atomicOr(&mask[e * nb + (t >> 6)], 1ull << (t & 63));
   }
   __syncthreads();
   for (int e = wave; e < E; e += 16) {
-    int c = 0;
-    for (int t0 = 0; t0 < rows; t0 += 64) {
-      const int t = t0 + lane;
-      const bool bit = t < rows && ((bits[t * words + (e >> 5)] >> (e & 31)) & 1u);
-      c += __popcll(__ballot(bit));
+    const int c = lane < nb ? __popcll(mask[e * nb + lane]) : 0;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, WAVE);
+      if (lane >= o) inc += y;
     }
-    if (lane == 0) s_cnt[e] = c;
+    if (lane < nb) base[e * nb + lane] = inc - c;  // tokens of e in earlier blocks
+    if (lane == 63) s_cnt[e] = inc;
   }
   __syncthreads();
   // groups: 0 = shared expert (all rows), 1 + e = routed expert e
@@ -276,6 +345,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   if (wave == 2) wave_exclusive_scan(s_ndn, s_idn, E + 1, lane);
   if (wave == 3) wave_exclusive_scan(s_nch, s_ich, E + 1, lane);
   __syncthreads();
+  for (int i = tid; i < E * nb; i += 1024) base[i] += s_off[i / nb];
   for (int e = tid; e < E; e += 1024) {
     cnt[e] = s_cnt[e];
     off[e] = s_off[e];
@@ -298,40 +368,30 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     items[MOE_CHUNKS + g] = s_ich[g];
   }
   for (int c = tid; c < s_ich[E + 1]; c += 1024) items[MOE_DONE + c] = 0;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = wave; e < E; e += 16) {
-    int run = s_off[e];
-    for (int t0 = 0; t0 < rows; t0 += 64) {
-      const int t = t0 + lane;
-      const bool bit = t < rows && ((bits[t * words + (e >> 5)] >> (e & 31)) & 1u);
-      const uint64_t m = __ballot(bit);
-      if (bit) {
-        const int pos = run + __popcll(m & lt);
-        perm[pos] = t;
-        for (int j = 0; j < k; ++j)
-          if (choice[t * k + j] == e) {
-            slot[t * k + j] = pos;
-            widx[pos] = t * k + j;
-          }
-      }
-      run += __popcll(m);
-    }
+  __syncthreads();  // base is final
+  for (int i = tid; i < pairs; i += 1024) {
+    const int t = i / k, e = idx[i], b = t >> 6, l = t & 63;
+    const unsigned long long below = l == 0 ? 0ull : (mask[e * nb + b] << (64 - l));
+    const int pos = base[e * nb + b] + __popcll(below);
+    slot[i] = pos;
+    perm[pos] = t;
+    widx[pos] = i;
   }
 }
 
 }  // namespace
 
 void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t* idx, float* w) {
-  hipLaunchKernelGGL(topk_kernel, dim3(div_up(rows, 4)), dim3(256), 0, s, z, rows, E, k, idx, w);
+  hipLaunchKernelGGL(topk_kernel, dim3(div_up(rows, RB)), dim3(256), 0, s, z, rows, E, k, idx, w);
 }
 
-void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
-                             const bf16_t* wr, int E, int k, bf16_t* u, float* z, int32_t* idx, float* w) {
-  const size_t tile = (size_t)RT_ROWS * (d + 8) * sizeof(bf16_t);
-  const size_t sums = (size_t)5 * RT_ROWS * E * sizeof(float);
-  const size_t lds = tile > sums ? tile : sums;
-  hipLaunchKernelGGL(norm_router_topk_kernel, dim3(div_up(rows, RT_ROWS)), dim3(256), lds, s, h, gain, rows, d,
-                     eps, wr, E, k, u, z, idx, w);
+void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
+                   const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
+                   float* w) {
+  const int kq = d / RKS;
+  const size_t lds = (size_t)RB * (kq + 8) * 2 + (size_t)RB * (E + 1) * 4 + (size_t)RB * (d / 64) * 4;
+  hipLaunchKernelGGL(router_kernel, dim3(div_up(rows, RB) * RKS), dim3(256), lds, s, h, ss, gain, rows, d, eps, wr,
+                     E, k, u, z, zpart, sync, idx, w);
 }
 
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
@@ -342,6 +402,9 @@ void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, i
                      dt, cnt, off, perm, slot, widx, items);
 }
 
+// Dynamic LDS of the permutation kernel: mask (8 B) and base (4 B) per
+// (expert, 64-token block).
 size_t permute_lds_bytes(int rows, int E, int k) {
-  return (size_t)rows * ((E + 31) / 32) * 4 + (((size_t)rows * k + 3) & ~(size_t)3);
+  (void)k;
+  return (size_t)E * ((rows + 63) / 64) * 12;
 }

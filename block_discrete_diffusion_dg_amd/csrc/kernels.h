@@ -17,10 +17,13 @@ void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas,
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k);
 
 // k_dense.hip (weight-streaming dense projections)
+// launch_qkv also zeroes the router's row-block counters (sync, 256 words)
 void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
                 const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
-                const ReqTable& rt);
-void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h);
+                const ReqTable& rt, int32_t* sync);
+// h += a W^T; ss (optional) receives per-64-column partial sums of squares
+// of the updated rows, [N/64][rows]
+void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h, float* ss);
 
 // k_gemm.hip (LM head: LDS-tiled GEMM with fused vocabulary statistics)
 void launch_gemm_lmhead(hipStream_t s, int mt, const bf16_t* a, int rows, int K, const bf16_t* embed,
@@ -36,8 +39,9 @@ void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int laye
 
 // k_route.hip
 void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t* idx, float* w);
-void launch_norm_router_topk(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
-                             const bf16_t* wr, int E, int k, bf16_t* u, float* z, int32_t* idx, float* w);
+void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
+                   const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
+                   float* w);
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
                     int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
                     int32_t* widx, int32_t* items);

@@ -57,7 +57,9 @@ typedef enum {
  * n_q_heads a multiple of n_kv_heads; (n_q_heads*head_dim) and
  * (n_kv_heads*head_dim) multiples of 128; n_experts <= 128 and a multiple
  * of 8; top_k <= 8; d_expert and d_shared multiples of 64; vocab a multiple
- * of 256; canvas a multiple of 16, at most 1024.
+ * of 256; canvas a multiple of 16, at most 1024; canvas <= max_rows <=
+ * 16*canvas and 12 * n_experts * ceil(max_rows/64) <= 57344 (routing tables
+ * held in LDS: max_rows <= 2368 for 128 experts).
  * tau_first / tau_last: temperature at the first / last step, falling
  * linearly (explainer §3.3: 0.8 -> 0.4). */
 typedef struct dg_config {

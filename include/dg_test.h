@@ -34,7 +34,12 @@ extern "C" {
  *   hid      bf16 [rows*k][F]        routed expert SwiGLU activations
  *   hid_s    bf16 [rows][Fs]         shared expert SwiGLU activations
  *   y        fp32 [rows*k][d]        routed expert outputs (weighted)
- *   stats    dg_row_stats [rows]     per-row LM-head statistics          */
+ *   stats    dg_row_stats [rows]     per-row LM-head statistics
+ *   ss       fp32 [d/64][rows]       partial sums of squares of h per
+ *                                    64-column tile (output projection)
+ *   zpart    fp32 [4][rows16][E]     router logits per quarter of d
+ *                                    (rows16 = rows rounded up to 16)
+ *   sync     int32 [256]             router row-block arrival counters   */
 /* Word of the items buffer that counts expert-kernel waits which ran out of
  * their poll budget instead of seeing their input published. A correct run
  * leaves it unchanged; the library never resets it. */
@@ -50,7 +55,7 @@ extern "C" {
 
 typedef struct dg_ws_layout {
   size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
-      slot, hid, hid_s, y, lm_part, stats, ids, total;
+      slot, hid, hid_s, y, lm_part, stats, ids, ss, zpart, sync, total;
 } dg_ws_layout;
 
 dg_status dg_workspace_layout(const dg_config *cfg, dg_ws_layout *out);
