@@ -80,7 +80,6 @@ def cpu_baseline(eng, hw, cfg, canvas_ids, prefix, n_layers_sample, step, n_step
         blas_threads = 0
     cores = len(os.sched_getaffinity(0))
     req = om.Request(cfg, prefix + cfg.canvas)
-    kv = eng.kv_view()
     x = canvas_ids.astype(np.int64)
     t0 = time.perf_counter()
     h = om.f64(hw.embed[x])
@@ -88,8 +87,9 @@ def cpu_baseline(eng, hw, cfg, canvas_ids, prefix, n_layers_sample, step, n_step
     t_layers = 0.0
     for l in range(n_layers_sample):
         lw = hw.layer(l)
-        ck = om.f64(kv[0, l, 0, :, :prefix].permute(1, 0, 2).cpu())
-        cv = om.f64(kv[0, l, 1, :, :prefix].permute(1, 0, 2).cpu())
+        k_rows, v_rows = eng.cache_rows(0, l, 0, prefix)
+        ck = om.f64(k_rows.permute(1, 0, 2).cpu())
+        cv = om.f64(v_rows.permute(1, 0, 2).cpu())
         t0 = time.perf_counter()
         h, _, _ = om.layer_forward(h, lw, cfg, ck, cv, prefix, False)
         t_layers += time.perf_counter() - t0

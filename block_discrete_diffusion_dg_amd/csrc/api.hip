@@ -42,7 +42,8 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.q = take(R * qd * 2);
   L.attn_o = take(R * qd * 2);
   L.attn_part = take((size_t)DG_ATTN_SPLITS * R * qd * 4);
-  L.attn_ml = take((size_t)DG_ATTN_SPLITS * R * c.n_q_heads * 8);
+  const size_t groups = attn_groups_bound(c.max_rows, c.n_q_heads, c.n_kv_heads);
+  L.attn_ml = take((size_t)DG_ATTN_SPLITS * groups * 64 * 8);
   L.rope = take(R * (c.head_dim / 2) * 8);
   L.z = take(R * E * 4);
   L.idx = take(R * k * 4);
@@ -61,7 +62,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.ids = take(R * 4);
   L.ss = take(R * (d / 64) * 4);
   L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
-  L.sync = take(256 * 4);
+  L.sync = take((256 + groups) * 4);  // router row blocks, then attention groups
   L.total = o;
   return L;
 }
@@ -85,7 +86,7 @@ const char* check_config(const dg_config& c) {
     return "max_rows must lie in [canvas, 16*canvas]";
   if (permute_lds_bytes(c.max_rows, c.n_experts, c.top_k) > 57344)
     return "12 * n_experts * ceil(max_rows/64) must not exceed 56 KiB (routing tables in LDS)";
-  if (c.max_ctx < 2 * c.canvas) return "max_ctx must hold at least two blocks";
+  if (c.max_ctx < 2 * c.canvas || c.max_ctx % 32) return "max_ctx must be a multiple of 32 holding at least two blocks";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.tau_first > 0.f) || !(c.tau_last > 0.f))
     return "rms_eps >= 0, rope_theta > 0 and temperatures > 0 required";
   return nullptr;
@@ -190,12 +191,14 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   bf16_t* u = c->buf<bf16_t>(L.u);
 
   STAGE(DG_STAGE_QKV, launch_qkv(s, u, rows, d, w.w_qkv, c->buf<bf16_t>(L.q), c->kv, l, g.n_q_heads,
-                                 g.n_kv_heads, g.head_dim, c->buf<float2>(L.rope), rt, c->buf<int32_t>(L.sync)));
+                                 g.n_kv_heads, g.head_dim, c->buf<float2>(L.rope), rt, c->buf<int32_t>(L.sync),
+                                 256 + attn_groups_bound(g.max_rows, g.n_q_heads, g.n_kv_heads)));
   if (kv_only) return;
   const int ns = attn_splits(rt, g.n_q_heads, g.n_kv_heads, g.max_rows);
   STAGE(DG_STAGE_ATTN, launch_attention(s, c->buf<bf16_t>(L.q), c->kv, l, rt, g.n_q_heads, g.n_kv_heads,
                                        g.head_dim, causal, ns, c->buf<float>(L.attn_part),
-                                       c->buf<float2>(L.attn_ml), c->buf<bf16_t>(L.attn_o)));
+                                       c->buf<float2>(L.attn_ml), c->buf<int32_t>(L.sync) + 256,
+                                       c->buf<bf16_t>(L.attn_o)));
   STAGE(DG_STAGE_OPROJ, launch_resid(s, c->buf<bf16_t>(L.attn_o), rows, g.n_q_heads * g.head_dim, w.w_o, d, h,
                                      c->buf<float>(L.ss)));
   STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,

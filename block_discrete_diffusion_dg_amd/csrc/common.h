@@ -57,16 +57,14 @@ struct KvGeom {
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (bf16_t)(b >> 16);
-}
+// fp32 -> bf16, round to nearest even: the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32), two values per instruction in pack_bf16x2.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // D = A(16x32) * B(32x16) + C on the gfx950 bf16 matrix core.

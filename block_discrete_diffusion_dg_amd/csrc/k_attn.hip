@@ -3,16 +3,30 @@
 // h = g*rep .. g*rep+rep-1 read kv head g). Denoising uses no mask inside the
 // block; the causal encoder (commit / prefill) masks keys after the query.
 //
-// Flash-style with split keys: a work-group takes 64 query vectors of one
-// (request, kv head) and one contiguous range of 64-key tiles, keeps an
-// online softmax, and writes an unnormalised partial output with its running
-// max and sum; a merge kernel combines the splits.
-//
-// The wave computes S^T = K Q^T (16 queries x 64 keys per tile) so that the
-// score accumulators are already laid out as the B operand of O^T = V^T P^T:
-// the lane holding query column q has keys {32kk + 4g + r} and
-// {32kk + 16 + 4g + r} of k-step kk, which is the same key set the A operand
-// (V^T, staged transposed in LDS) supplies for that lane group.
+// A work-group takes 64 query vectors of one (request, kv head), 16 per wave,
+// and one contiguous range of 64-key tiles (a split of the keys), keeping an
+// online softmax per query. Operands come straight from the KV cache:
+//   S^T = K Q^T: the A operand is 16 keys x 32 dims of K, row-major in the
+//     cache (16 contiguous bytes per lane), the B operand the wave's queries.
+//   O^T = V^T P^T: the score accumulators already sit in the B-operand layout
+//     (the lane holding query q has keys {4g+r} and {16+4g+r} of each 32-key
+//     step); the cache stores V in that same key grouping (see v_index), so
+//     the A operand is again 16 contiguous bytes per lane.
+// A tile's 32 operand fragments (1 KB each) are copied global -> LDS by the
+// asynchronous load-to-LDS path into one of two distinct LDS buffers: lane L
+// of a copy lands at byte 16*L of its fragment, so each wave later reads a
+// fragment with one linear, conflict-free LDS load, and the four waves share
+// one copy of the tile. The next tile's copy is issued as soon as the current
+// tile is in place; because the two buffers are distinct objects, reading one
+// never waits for the copy into the other.
+// Softmax work is kept off the common path: keys are masked only on tiles
+// that reach past the cache length or (causal) past a query's position, the
+// running output is rescaled only when some query's maximum moved, and the
+// denominator comes from the matrix cores (see lacc).
+// With several splits, each work-group writes its unnormalised output and
+// (max, sum) through to device-coherent memory and counts itself in; the last
+// of the (request, kv head, query block) to arrive merges the splits in split
+// order (deterministic), writes the bf16 output and resets the counter.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,17 +34,24 @@ namespace {
 
 constexpr int KT = 64;  // keys per tile
 
-template <int DH>
-__global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q, KvGeom kv, int layer,
-                                                   ReqTable rt, int Hq, int Hkv, int causal,
-                                                   int nsplit, float scale_log2,
-                                                   float* __restrict__ opart,
-                                                   float2* __restrict__ ml) {
-  constexpr int LDKs = DH + 8;
-  constexpr int LDV = KT + 8;
-  __shared__ __align__(16) bf16_t Ks[KT * LDKs];
-  __shared__ __align__(16) bf16_t Vt[DH * LDV];
+__device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store8_coherent(void* dst, u32x2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
 
+template <int DH>
+__global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q, KvGeom kv, int layer, ReqTable rt,
+                                                   int Hq, int Hkv, int causal, int nsplit, float scale_log2,
+                                                   float* __restrict__ opart, float2* __restrict__ ml,
+                                                   int32_t* __restrict__ sync, bf16_t* __restrict__ out) {
+  constexpr int NS = DH / 32;  // 32-dim steps of QK^T
+  constexpr int ND = DH / 16;  // 16-dim output subtiles
+  constexpr int CHUNKS = 4 * NS + 2 * ND;
+  __shared__ __align__(16) u32x4 tbA[CHUNKS][64];  // two distinct buffers: a copy into
+  __shared__ __align__(16) u32x4 tbB[CHUNKS][64];  // one never delays reads of the other
+  __shared__ int s_last;
   const int rep = Hq / Hkv;
   const int n = rt.rows_per_req;
   const int rows_total = rt.n_req * n;
@@ -39,6 +60,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   int b = blockIdx.x;
   const int split = b % nsplit;
   b /= nsplit;
+  const int group = b;  // (request, kv head, query block)
   const int qb = b % qblocks;
   b /= qblocks;
   const int g = b % Hkv;
@@ -58,131 +80,228 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   const int qh = g * rep + (qvalid ? qv % rep : 0);
   const int row = r * n + qi;
 
-  u32x4 qf[DH / 32];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int s = 0; s < DH / 32; ++s)
-    qf[s] = qvalid ? ld16(q + ((int64_t)row * Hq + qh) * DH + 32 * s + 8 * grp) : zero;
+  u32x4 qf[NS];
 
-  f32x4 oacc[DH / 16];
+  f32x4 oacc[ND];
 #pragma unroll
-  for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < ND; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running maximum of scale_log2 * score
 
   const int slot = rt.slot[r];
   const bf16_t* Kp = kv.k_plane(slot, layer, g);
   const bf16_t* Vp = kv.v_plane(slot, layer, g);
   const int qlimit = P + qi;  // causal: keys at positions <= P + qi
 
-  for (int tile = t0; tile < t1; ++tile) {
-    const int k0 = tile * KT;
-    __syncthreads();
+  // Fragments of a tile: K subtile ks (16 keys) x dim step st at ks*NS + st,
+  // then V block kk (32 keys) x dim subtile dt at 4*NS + kk*ND + dt. Wave w
+  // copies chunks w + 4j. Both planes advance by KT*DH elements per tile, so
+  // interior tiles only offset the addresses of the first tile; the tile that
+  // reaches past nk clamps: K rows to the last key (finite; their scores are
+  // masked), V blocks to the last block holding keys (entries past nk are
+  // zeroed before use).
+  constexpr int CPW = CHUNKS / 4;  // chunks per wave
+  const bf16_t* cbase[CPW];
 #pragma unroll
-    for (int i = 0; i < DH / 32; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
-      // keys past nk re-read the last key (finite values; their scores are masked)
-      const int kr = min(k0 + key, nk - 1);
-      const u32x4 kk = ld16(Kp + (int64_t)kr * DH + dc);
-      const u32x4 vv = ld16(Vp + (int64_t)kr * DH + dc);
-      *reinterpret_cast<u32x4*>(Ks + key * LDKs + dc) = kk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(dc + 2 * e) * LDV + key] = (bf16_t)(vv[e] & 0xffffu);
-        Vt[(dc + 2 * e + 1) * LDV + key] = (bf16_t)(vv[e] >> 16);
-      }
+  for (int j = 0; j < CPW; ++j) {
+    const int c = wave + 4 * j;
+    if (c < 4 * NS) {
+      cbase[j] = Kp + (int64_t)(16 * (c / NS) + l16) * DH + 32 * (c % NS) + 8 * grp;
+    } else {
+      const int kk = (c - 4 * NS) / ND, dt = (c - 4 * NS) % ND;
+      cbase[j] = Vp + ((int64_t)(kk * 4 + grp) * DH + 16 * dt + l16) * 8;
     }
-    __syncthreads();
+  }
+  auto copy_tile = [&](int tile, u32x4 (&tb)[CHUNKS][64]) {
+    const int k0 = tile * KT;
+    const bool edge = k0 + KT > nk;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int c = wave + 4 * j;
+      const bf16_t* src = cbase[j] + (int64_t)k0 * DH;
+      if (edge) {
+        if (c < 4 * NS) {
+          const int key = min(k0 + 16 * (c / NS) + l16, nk - 1);
+          src = Kp + (int64_t)key * DH + 32 * (c % NS) + 8 * grp;
+        } else {
+          const int kk = (c - 4 * NS) / ND, dt = (c - 4 * NS) % ND;
+          const int blk = min((k0 + 32 * kk) >> 5, (nk - 1) >> 5);
+          src = Vp + (((int64_t)blk * 4 + grp) * DH + 16 * dt + l16) * 8;
+        }
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tb[c][0], 16, 0, 0);
+    }
+  };
+  // smallest query position of the wave: causal masking is needed only on
+  // tiles reaching past it
+  const int qi_lo = min((qb * 64 + wave * 16) / rep, n - 1);
+  // the denominator runs on the matrix cores: an all-ones A operand turns the
+  // probabilities of the PV product into their column sums
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 
+  auto compute_tile = [&](int tile, const u32x4 (&tb)[CHUNKS][64]) {
+    const int k0 = tile * KT;
     f32x4 s[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < DH / 32; ++st) {
-        const u32x4 kf = ld16(Ks + (16 * ks + l16) * LDKs + 32 * st + 8 * grp);
-        s[ks] = mfma_bf16(kf, qf[st], s[ks]);
-      }
+      for (int st = 0; st < NS; ++st) s[ks] = mfma_bf16(tb[ks * NS + st][lane], qf[st], s[ks]);
     }
-    float tmax = -INFINITY;
+    if (k0 + KT > nk || (causal && k0 + KT - 1 > P + qi_lo)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = k0 + 16 * ks + 4 * grp + rr;
-        float v = s[ks][rr] * scale_log2;
-        if (key >= nk || (causal && key > qlimit)) v = -INFINITY;
-        s[ks][rr] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = k0 + 16 * ks + 4 * grp + rr;
+          if (key >= nk || (causal && key > qlimit)) s[ks][rr] = -INFINITY;
+        }
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
+                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
-    const float m_new = fmaxf(m_run, tmax);
+    // running maximum in the scaled log2 domain (scale > 0 keeps the order)
+    const float m_new = fmaxf(m_run, tmax * scale_log2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    l_run *= alpha;
+    // alpha == 1 exactly when the maximum did not move: skip the rescale
+    // when that holds for every query of the wave
+    if (__ballot(m_new != m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      lacc *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] *= alpha;
+    }
     m_run = m_new;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float pv = exp2f(s[ks][rr] - m_use);
-        s[ks][rr] = pv;
-        l_run += pv;
-      }
+      for (int rr = 0; rr < 4; ++rr) s[ks][rr] = __builtin_amdgcn_exp2f(fmaf(s[ks][rr], scale_log2, -m_use));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const u32x4 pf = {pack_bf16x2(s[2 * kk][0], s[2 * kk][1]), pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
                         pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
                         pack_bf16x2(s[2 * kk + 1][2], s[2 * kk + 1][3])};
+      u32x4 vf[ND];
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
-        const bf16_t* vr = Vt + (16 * dt + l16) * LDV + 32 * kk + 4 * grp;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16);
-        const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
-        oacc[dt] = mfma_bf16(vf, pf, oacc[dt]);
+      for (int dt = 0; dt < ND; ++dt) vf[dt] = tb[4 * NS + kk * ND + dt][lane];
+      if (k0 + KT > nk) {
+        // keys past nk: V entries may be unwritten cache rows (any bit
+        // pattern); zero them so that 0 * V stays 0
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = k0 + 32 * kk + (e >> 2) * 16 + 4 * grp + (e & 3);
+          const uint32_t keep = key < nk ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) vf[dt][e >> 1] &= keep;
+        }
       }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma_bf16(vf[dt], pf, oacc[dt]);
+      lacc = mfma_bf16(ones, pf, lacc);
+    }
+  };
+
+  if (t0 < t1) copy_tile(t0, tbA);
+  // the query fragments load while the first tile is in flight
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    qf[s] = qvalid ? ld16(q + ((int64_t)row * Hq + qh) * DH + 32 * s + 8 * grp) : zero;
+  for (int tile = t0; tile < t1; tile += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the tile have landed
+    __syncthreads();                // ... and every other wave's; buffer B is free
+    if (tile + 1 < t1) copy_tile(tile + 1, tbB);
+    compute_tile(tile, tbA);
+    if (tile + 1 >= t1) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 2 < t1) copy_tile(tile + 2, tbA);
+    compute_tile(tile + 1, tbB);
+  }
+
+  const float l_tot = lacc[0];  // every row of the ones-product holds the column sum
+  // lane (grp, l16) holds output dims 16dt + 4grp + 0..3 of query column l16
+  if (nsplit == 1) {
+    if (qvalid) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* op = out + ((int64_t)row * Hq + qh) * DH;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+        *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * grp) =
+            u32x2{pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv), pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
+    }
+    return;
+  }
+  {
+    const int64_t base = ((int64_t)split * rows_total + row) * Hq + qh;
+    if (qvalid) {
+      float* op = opart + base * DH;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) store16_coherent(op + 16 * dt + 4 * grp, __builtin_bit_cast(u32x4, oacc[dt]));
+      // (max, sum) group-major, [group][split][64 queries]: a group's entries
+      // fill whole lines that no other group touches
+      if (grp == 0)
+        store8_coherent(ml + ((int64_t)group * nsplit + split) * 64 + wave * 16 + l16,
+                        u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)});
     }
   }
-
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, WAVE);
-  l_tot += __shfl_xor(l_tot, 32, WAVE);
-  if (qvalid) {
-    const int64_t base = ((int64_t)split * rows_total + row) * Hq + qh;
-    float* op = opart + base * DH;
-#pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) op[16 * dt + 4 * grp + rr] = oacc[dt][rr];
-    if (grp == 0) ml[base] = float2{m_run, l_tot};
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(sync + group, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == nsplit - 1;
+    if (s_last) __hip_atomic_store(sync + group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
-
-// out[row][h*DH + d] = sum_s 2^(m_s - M) O_s[d] / sum_s 2^(m_s - M) l_s
-template <int DH>
-__global__ void attn_merge_kernel(const float* __restrict__ opart, const float2* __restrict__ ml,
-                                  int rows_total, int Hq, int nsplit, bf16_t* __restrict__ out) {
-  const int rh = blockIdx.x;  // row * Hq + h
-  const int d = threadIdx.x;
+  __syncthreads();
+  if (!s_last || !qvalid) return;
+  // merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, split order.
+  // The group's partial lines are read only here, after every split wrote
+  // them, and caches start the kernel invalidated: no stale copies.
+  constexpr int MAXS = DG_ATTN_SPLITS;
+  float2 mls[MAXS];
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[(int64_t)s * rows_total * Hq + rh].x);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 v = ml[(int64_t)s * rows_total * Hq + rh];
-    if (v.x == -INFINITY) continue;
-    const float w = exp2f(v.x - M);
-    num += w * opart[((int64_t)s * rows_total * Hq + rh) * DH + d];
-    den += w * v.y;
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp) {
+    if (sp >= nsplit) break;
+    mls[sp] = ml[((int64_t)group * nsplit + sp) * 64 + wave * 16 + l16];
+    M = fmaxf(M, mls[sp].x);
   }
-  out[(int64_t)rh * DH + d] = f2bf(num / den);
+  float num[ND][4], den = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) num[dt][rr] = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp) {
+    if (sp >= nsplit) break;
+    if (mls[sp].x == -INFINITY) continue;
+    const float wgt = exp2f(mls[sp].x - M);
+    den += wgt * mls[sp].y;
+    const float* op = opart + (((int64_t)sp * rows_total + row) * Hq + qh) * DH;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const float4 v = *reinterpret_cast<const float4*>(op + 16 * dt + 4 * grp);
+      num[dt][0] += wgt * v.x;
+      num[dt][1] += wgt * v.y;
+      num[dt][2] += wgt * v.z;
+      num[dt][3] += wgt * v.w;
+    }
+  }
+  const float inv = 1.0f / den;
+  bf16_t* op = out + ((int64_t)row * Hq + qh) * DH;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * grp) =
+        u32x2{pack_bf16x2(num[dt][0] * inv, num[dt][1] * inv), pack_bf16x2(num[dt][2] * inv, num[dt][3] * inv)};
 }
 
 }  // namespace
 
+// Splits of the key range: enough work-groups to cover the GPU about once
+// (256 compute units), at most DG_ATTN_SPLITS, at least one tile per split.
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
   (void)max_rows;
   const int rep = Hq / Hkv;
@@ -190,28 +309,25 @@ int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
   int max_pos = 0;
   for (int r = 0; r < rt.n_req; ++r) max_pos = max(max_pos, rt.pos0[r]);
   const int tiles = div_up(max_pos + rt.rows_per_req, KT);
-  int ns = div_up(1024, base);
+  int ns = div_up(256, base);
   ns = min(ns, DG_ATTN_SPLITS);
   ns = min(ns, tiles);
   return max(ns, 1);
 }
 
-void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer,
-                      const ReqTable& rt, int Hq, int Hkv, int dh, int causal, int nsplit,
-                      float* opart, float2* ml, bf16_t* out) {
+// (request, kv head, query block) groups of a call of at most max_rows rows:
+// sum_r Hkv * ceil(n_r * rep / 64) <= max_rows * Hq / 64 + DG_MAX_REQ * Hkv.
+int attn_groups_bound(int max_rows, int Hq, int Hkv) { return div_up(max_rows * Hq, 64) + DG_MAX_REQ * Hkv; }
+
+void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer, const ReqTable& rt, int Hq,
+                      int Hkv, int dh, int causal, int nsplit, float* opart, float2* ml, int32_t* sync, bf16_t* out) {
   const int rep = Hq / Hkv;
   const int blocks = rt.n_req * Hkv * div_up(rt.rows_per_req * rep, 64) * nsplit;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
-  const int rows_total = rt.n_req * rt.rows_per_req;
-  if (dh == 128) {
-    hipLaunchKernelGGL(attn_kernel<128>, dim3(blocks), dim3(256), 0, s, q, kv, layer, rt, Hq, Hkv,
-                       causal, nsplit, scale_log2, opart, ml);
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(rows_total * Hq), dim3(128), 0, s, opart, ml,
-                       rows_total, Hq, nsplit, out);
-  } else {
-    hipLaunchKernelGGL(attn_kernel<64>, dim3(blocks), dim3(256), 0, s, q, kv, layer, rt, Hq, Hkv,
-                       causal, nsplit, scale_log2, opart, ml);
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(rows_total * Hq), dim3(64), 0, s, opart, ml,
-                       rows_total, Hq, nsplit, out);
-  }
+  if (dh == 128)
+    hipLaunchKernelGGL(attn_kernel<128>, dim3(blocks), dim3(256), 0, s, q, kv, layer, rt, Hq, Hkv, causal, nsplit,
+                       scale_log2, opart, ml, sync, out);
+  else
+    hipLaunchKernelGGL(attn_kernel<64>, dim3(blocks), dim3(256), 0, s, q, kv, layer, rt, Hq, Hkv, causal, nsplit,
+                       scale_log2, opart, ml, sync, out);
 }

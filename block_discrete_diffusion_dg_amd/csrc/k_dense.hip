@@ -33,14 +33,16 @@ struct QkvArgs {
   int layer, Hq, Hkv, dh;
   const float2* rope;  // [rows][dh/2] (cos, sin)
   ReqTable rt;
-  int32_t* sync;  // router row-block counters, zeroed here for the layer's router
+  int32_t* sync;  // arrival counters of the layer's router and attention, zeroed here
+  int n_sync;
 };
 
 __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, int rows, int d,
                                                   const bf16_t* __restrict__ w, QkvArgs p) {
   using T = StreamTile<DMT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
-  if (blockIdx.x == 0 && p.sync) p.sync[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && p.sync)
+    for (int i = threadIdx.x; i < p.n_sync; i += 256) p.sync[i] = 0;
   const int dh = p.dh, half = dh >> 1;
   const int NT = (p.Hq + 2 * p.Hkv) * half / 64, MC = div_up(rows, T::CH);
   int nt, mc;
@@ -67,19 +69,23 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
         x1 = y1;
         x2 = y2;
       }
-      bf16_t* dst;
-      if (head < p.Hq) {
-        dst = p.q + (int64_t)row * p.Hq * dh + (int64_t)head * dh;
-      } else {
+      if (head < p.Hq + p.Hkv) {
+        bf16_t* dst;
+        if (head < p.Hq) {
+          dst = p.q + (int64_t)row * p.Hq * dh + (int64_t)head * dh;
+        } else {
+          const int rq = row / p.rt.rows_per_req, i = row % p.rt.rows_per_req;
+          dst = p.kv.k_plane(p.rt.slot[rq], p.layer, head - p.Hq) + (int64_t)(p.rt.pos0[rq] + i) * dh;
+        }
+        dst[j] = f2bf(x1);
+        dst[j + half] = f2bf(x2);
+      } else {  // V: matrix-core operand order inside 32-key blocks
         const int rq = row / p.rt.rows_per_req, i = row % p.rt.rows_per_req;
-        const int pos = p.rt.pos0[rq] + i;
-        const int slot = p.rt.slot[rq];
-        dst = (head < p.Hq + p.Hkv ? p.kv.k_plane(slot, p.layer, head - p.Hq)
-                                   : p.kv.v_plane(slot, p.layer, head - p.Hq - p.Hkv)) +
-              (int64_t)pos * dh;
+        const int64_t pos = p.rt.pos0[rq] + i;
+        bf16_t* vp = p.kv.v_plane(p.rt.slot[rq], p.layer, head - p.Hq - p.Hkv);
+        vp[v_index(pos, j, dh)] = f2bf(x1);
+        vp[v_index(pos, j + half, dh)] = f2bf(x2);
       }
-      dst[j] = f2bf(x1);
-      dst[j + half] = f2bf(x2);
     }
 }
 
@@ -130,8 +136,8 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
 
 void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
                 const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
-                const ReqTable& rt, int32_t* sync) {
-  QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt, sync};
+                const ReqTable& rt, int32_t* sync, int n_sync) {
+  QkvArgs p{q, kv, layer, Hq, Hkv, dh, rope, rt, sync, n_sync};
   const int NT = (Hq + 2 * Hkv) * (dh / 2) / 64;
   const int MC = div_up(rows, StreamTile<DMT>::CH);
   hipLaunchKernelGGL(qkv_kernel, dim3(NT * MC), dim3(256), 0, s, u, rows, d, w, p);

@@ -17,10 +17,11 @@ void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas,
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k);
 
 // k_dense.hip (weight-streaming dense projections)
-// launch_qkv also zeroes the router's row-block counters (sync, 256 words)
+// launch_qkv also zeroes the n_sync arrival counters of the layer's router
+// and attention kernels
 void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w, bf16_t* q,
                 const KvGeom& kv, int layer, int Hq, int Hkv, int dh, const float2* rope,
-                const ReqTable& rt, int32_t* sync);
+                const ReqTable& rt, int32_t* sync, int n_sync);
 // h += a W^T; ss (optional) receives per-64-column partial sums of squares
 // of the updated rows, [N/64][rows]
 void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h, float* ss);
@@ -33,9 +34,16 @@ int lmhead_parts(int V);
 
 // k_attn.hip
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows);
-void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer,
-                      const ReqTable& rt, int Hq, int Hkv, int dh, int causal, int nsplit,
-                      float* opart, float2* ml, bf16_t* out);
+int attn_groups_bound(int max_rows, int Hq, int Hkv);
+// V planes of the KV cache hold each 32-key block in matrix-core operand
+// order: key o of the block, dim c at element ((o%16)/4 * dh + c) * 8 +
+// (o/16)*4 + o%4 of the block (32*dh elements).
+__host__ __device__ __forceinline__ int64_t v_index(int64_t pos, int c, int dh) {
+  const int o = (int)(pos & 31);
+  return (pos >> 5) * 32 * dh + ((int64_t)((o & 15) >> 2) * dh + c) * 8 + (o >> 4) * 4 + (o & 3);
+}
+void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer, const ReqTable& rt, int Hq,
+                      int Hkv, int dh, int causal, int nsplit, float* opart, float2* ml, int32_t* sync, bf16_t* out);
 
 // k_route.hip
 void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t* idx, float* w);

@@ -38,6 +38,27 @@ def pack_weight(t: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def v_to_cache_order(v: torch.Tensor) -> torch.Tensor:
+    """V rows [..., n, dh] (n % 32 == 0) -> the cache's element order: inside
+    each 32-key block, key o = 16*half + 4*g + r and dim c sit at
+    (g*dh + c)*8 + 4*half + r. Returns [..., n, dh]-shaped storage."""
+    *lead, n, dh = v.shape
+    assert n % 32 == 0, n
+    nl = len(lead)
+    t = v.reshape(*lead, n // 32, 2, 4, 4, dh)  # blk, half, g, r, c
+    t = t.permute(*range(nl), nl, nl + 2, nl + 4, nl + 1, nl + 3)  # blk, g, c, half, r
+    return t.reshape(*lead, n, dh)
+
+
+def v_from_cache_order(raw: torch.Tensor) -> torch.Tensor:
+    """Inverse of v_to_cache_order: [..., n, dh] cache storage -> V rows."""
+    *lead, n, dh = raw.shape
+    nl = len(lead)
+    t = raw.reshape(*lead, n // 32, 4, dh, 2, 4)  # blk, g, c, half, r
+    t = t.permute(*range(nl), nl, nl + 3, nl + 1, nl + 4, nl + 2)  # blk, half, g, r, c
+    return t.reshape(*lead, n, dh)
+
+
 class Engine:
     """One context: weights (bf16, on the GPU), KV cache and workspace tensors.
 
@@ -109,8 +130,26 @@ class Engine:
             msg = self.lib.dg_last_error(self.ctx).decode() if getattr(self, "ctx", None) else ""
             raise B.DGError(status, msg)
 
+    def cache_rows(self, slot: int, layer: int, lo: int, hi: int):
+        """K and V rows [lo, hi) of one slot and layer, each [kv_head][hi-lo][head_dim]
+        bf16 on the device (V converted from the cache's block order)."""
+        kv = self.kv_view()
+        k = kv[slot, layer, 0, :, lo:hi]
+        b0, b1 = lo // 32 * 32, -(-hi // 32) * 32
+        v = v_from_cache_order(kv[slot, layer, 1, :, b0:b1])[:, lo - b0:hi - b0]
+        return k, v
+
+    def set_cache_rows(self, slot: int, layer: int, k: torch.Tensor, v: torch.Tensor):
+        """Write K and V rows [0, n) of one slot and layer (n % 32 == 0), each
+        [kv_head][n][head_dim] bf16, in the cache's layout."""
+        n = k.shape[1]
+        kv = self.kv_view()
+        kv[slot, layer, 0, :, :n] = k.to(kv.device)
+        kv[slot, layer, 1, :, :n] = v_to_cache_order(v.to(kv.device))
+
     def kv_view(self) -> torch.Tensor:
-        """[slot][layer][K|V][kv_head][max_ctx][head_dim] bf16 view of the cache."""
+        """[slot][layer][K|V][kv_head][max_ctx][head_dim] bf16 view of the raw
+        cache; V planes are in block operand order (v_from_cache_order)."""
         c = self.cfg
         return self.kv[:self.kv_bytes].view(torch.bfloat16).view(
             self.max_requests, c.n_layers, 2, c.n_kv_heads, self.max_ctx, c.head_dim)

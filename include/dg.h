@@ -66,7 +66,7 @@ typedef struct dg_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim;
   int32_t n_experts, top_k, d_expert, d_shared, vocab;
   int32_t canvas;        /* C: tokens per block (explainer §3.2: 256) */
-  int32_t max_ctx;       /* KV rows per request and layer */
+  int32_t max_ctx;       /* KV rows per request and layer (multiple of 32) */
   int32_t max_requests;  /* number of request slots in the KV cache */
   int32_t max_rows;      /* largest number of rows one call processes */
   float rms_eps, rope_theta, tau_first, tau_last;
@@ -145,8 +145,14 @@ dg_status dg_pack_weight(void *stream, const void *d_src, void *d_dst, int64_t n
 
 /* Bytes of KV cache for ONE request slot:
  * n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2.
- * Layout of the whole cache: [req][layer][K|V][kv_head][max_ctx][head_dim]
- * bf16, K stored after RoPE. */
+ * Layout of the whole cache: [req][layer][K|V][kv_head] planes of
+ * max_ctx * head_dim bf16 each. A K plane is row-major [max_ctx][head_dim],
+ * K stored after RoPE. A V plane is cut into blocks of 32 positions
+ * (max_ctx % 32 == 0); inside block b, position 32b + o (o = 16*h + 4*g + r,
+ * h < 2, g < 4, r < 4) and dim c sit at element
+ *   32*head_dim*b + (g*head_dim + c)*8 + 4*h + r,
+ * so the eight values one matrix-core lane multiplies (positions
+ * {4g..4g+3, 16+4g..16+4g+3} of the block, one dim) are contiguous. */
 size_t dg_kv_cache_bytes(const dg_config *cfg);
 
 /* Bytes of device workspace needed for calls of up to cfg->max_rows rows. */

@@ -65,7 +65,8 @@ def test_buffer_sizes(lib):
 
 @pytest.mark.parametrize("field,value", [("head_dim", 96), ("d_model", 1000), ("n_experts", 136),
                                          ("top_k", 9), ("vocab", 1000), ("canvas", 24),
-                                         ("max_rows", 100), ("n_q_heads", 12), ("max_ctx", 300)])
+                                         ("max_rows", 100), ("n_q_heads", 12), ("max_ctx", 300),
+                                         ("max_ctx", 4096 + 16)])
 def test_unsupported_shapes_rejected(lib, field, value):
     c = _cfg(**{field: value})
     assert lib.dg_workspace_bytes(ctypes.byref(c)) == 0

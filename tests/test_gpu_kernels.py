@@ -187,19 +187,15 @@ def test_init_canvas_matches_philox():
 # ------------------------------------------------------------------------ one layer
 
 def _fill_prefix(eng, cfg, P, seed=7, slot=0, layer=0):
-    kv = eng.kv_view()
     k = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), seed, layer, "k", "cuda")
     v = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), seed, layer, "v", "cuda")
-    kv[slot, layer, 0, :, :P] = k
-    kv[slot, layer, 1, :, :P] = v
+    eng.set_cache_rows(slot, layer, k, v)
     eng.set_cache_len(slot, P)
 
 
 def _cache_rows(eng, slot, layer, lo, hi):
-    kv = eng.kv_view()
-    k = kv[slot, layer, 0, :, lo:hi].permute(1, 0, 2).contiguous().cpu()
-    v = kv[slot, layer, 1, :, lo:hi].permute(1, 0, 2).contiguous().cpu()
-    return k, v
+    k, v = eng.cache_rows(slot, layer, lo, hi)
+    return k.permute(1, 0, 2).contiguous().cpu(), v.permute(1, 0, 2).contiguous().cpu()
 
 
 @pytest.mark.parametrize("name,causal", [("tiny", False), ("tiny", True), ("one_layer", False),

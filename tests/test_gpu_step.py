@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 
 def _oracle_request(eng, cfg, slot, length):
     req = om.Request(cfg, eng.max_ctx)
-    kv = eng.kv_view()
     for l in range(cfg.n_layers):
-        req.k[l, :length] = om.f64(kv[slot, l, 0, :, :length].permute(1, 0, 2).cpu())
-        req.v[l, :length] = om.f64(kv[slot, l, 1, :, :length].permute(1, 0, 2).cpu())
+        k, v = eng.cache_rows(slot, l, 0, length)
+        req.k[l, :length] = om.f64(k.permute(1, 0, 2).cpu())
+        req.v[l, :length] = om.f64(v.permute(1, 0, 2).cpu())
     req.length = length
     return req
 
@@ -91,7 +91,8 @@ def test_prefill_chunking_and_commit_are_causally_consistent():
     cfg = synth.TINY
     C = cfg.canvas
     n = 3 * C + 7  # ragged: several chunks of max_rows=C rows plus a tail
-    eng, hw = make_engine(cfg, max_ctx=n + C + 2 * C, max_requests=3, max_rows=C)
+    max_ctx = -(-(n + 3 * C) // 32) * 32  # capacity: a multiple of 32 positions
+    eng, hw = make_engine(cfg, max_ctx=max_ctx, max_requests=3, max_rows=C)
     ids = synth.make_prompt(n + C, cfg.vocab, 9).cuda()
     eng.prefill(0, ids)                       # whole sequence, chunked by the library
     eng.prefill(1, ids[:n].contiguous())      # prefix only ...
