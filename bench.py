@@ -219,6 +219,11 @@ def main():
     kinds, per_step = algorithmic_model(cfg, P, rows, touched)
     t_roof = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in per_step.values())
     b_ex, f_ex = algorithmic_model(cfg, P, rows, touched_staged)[0]["experts"]
+    # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+    # plain copy), only while the kernel's sources match the recorded hash
+    from block_discrete_diffusion_dg_amd.profiles import traffic_for
+    traffic = traffic_for("moe_experts", f"moe_experts_{wl.name}_traffic")
+    traffic = round(traffic) if traffic is not None else None
     ex_launch_ms = stages["experts"][0] / max(1, stages["experts"][1])
     achieved = b_ex / (ex_launch_ms * 1e-3)
     steps_per_s = 1e3 / ms
@@ -248,7 +253,7 @@ def main():
                      "bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                      "bytes_per_launch": round(b_ex), "avg_launch_ms": round(ex_launch_ms, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,
         "commit_ms": round(commit_ms, 3),
