@@ -15,6 +15,10 @@
 namespace {
 
 constexpr int DMT = 2;  // rows per chunk = 32
+// These launches give about one work-group per compute unit and little
+// matrix-core work per K-step, so each keeps its weights and its token rows
+// five steps ahead instead of relying on other work-groups to hide latency.
+constexpr int DENSE_DW = 5;
 
 __device__ __forceinline__ void tile_coords(int NT, int MC, int& nt, int& mc) {
   const int b = blockIdx.x;
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
   const int64_t r0 = (int64_t)head * dh + pw % half;  // first row of the wave's block
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 a0[DMT], a1[DMT];
-  stream_tile<DMT, true>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
+  stream_tile<DMT, true, DENSE_DW, DENSE_DW>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
   const bool rotate = head < p.Hq + p.Hkv;
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
   const int col0 = nt * 64 + wave * 16, col = col0 + l16;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 acc[DMT], unused[DMT];
-  stream_tile<DMT, false>(a, K, nullptr, row0, nrows, w + (int64_t)col0 * K, nullptr, K, acc, unused, lds);
+  stream_tile<DMT, false, DENSE_DW, DENSE_DW>(a, K, nullptr, row0, nrows, w + (int64_t)col0 * K, nullptr, K, acc, unused, lds);
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
 #pragma unroll

@@ -12,14 +12,12 @@
 // is 2 KB in the exact order the lanes consume it, so every weight load of a
 // wave is one fully used, contiguous 1 KB request.
 //
-// Pipeline: K advances in steps of BK = 64. Loads run two steps ahead of the
-// matrix cores: while step it is multiplied, the loads of steps it+1 and
-// it+2 are in flight (three register sets for the weights and for the A
-// staging; a double-buffered LDS tile for A, shared by the four waves). The
-// loop is unrolled by three so every register set has a static index; steps
-// past the end reload the last step (in-bounds, branch-free) and their
-// weight operands are zeroed, so the matrix-core instructions never sit under
-// control flow.
+// Pipeline: K advances in steps of BK = 64. The A rows are loaded DA steps
+// ahead (DA + 1 register sets, then a double-buffered LDS tile shared by the
+// four waves) and the weights DW steps ahead (DW + 1 register sets). The loop is
+// unrolled so every register set has a static index; steps past the end
+// reload the last step (in-bounds, branch-free) and their weight operands are
+// zeroed, so the matrix-core instructions never sit under control flow.
 //
 // Reduction-index assignment per K-step: MFMA step q in {0,1}, lane group g
 // uses k0 + 32q + 8g .. +7 for both operands.
@@ -56,7 +54,17 @@ __host__ __device__ __forceinline__ int64_t pack_index(int64_t n, int64_t k, int
 // A + map(row0 + i) * lda with map = rowmap or identity. Rows past nrows
 // repeat the chunk's first row; their accumulators are meaningless and must
 // not be stored. K % 64 == 0.
-template <int MT, bool GATED>
+// DW / DA: weight loads run DW steps ahead (DW + 1 register sets), A-row
+// loads DA steps ahead (DA + 1 sets). Deeper pipelines keep more bytes in
+// flight per work-group, which matters when few work-groups share a compute
+// unit or when a step has little matrix-core work to hide latency behind.
+template <int A_, int B_>
+struct Lcm {
+  static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+  static constexpr int value = A_ / gcd(A_, B_) * B_;
+};
+
+template <int MT, bool GATED, int DW = 2, int DA = 2>
 __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
                                             const int32_t* __restrict__ rowmap, int row0, int nrows,
                                             const bf16_t* __restrict__ w0,
@@ -64,6 +72,8 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
                                             f32x4 (&acc0)[MT], f32x4 (&acc1)[MT], bf16_t* lds) {
   using T = StreamTile<MT>;
   constexpr int BK = T::BK, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
+  constexpr int NW = DW + 1, NA = DA + 1, U = Lcm<NW, NA>::value;
+  static_assert(DW >= 2 && DA >= 2, "loads run at least two steps ahead");
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
 
 #pragma unroll
@@ -83,36 +93,37 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
   const bf16_t* wl0 = w0 + lane * 8;
   const bf16_t* wl1 = GATED ? w1 + lane * 8 : nullptr;
 
-  u32x4 ra[3][ACH];
-  u32x4 b0[3][2], b1[3][2];
+  u32x4 ra[NA][ACH];
+  u32x4 b0[NW][2], b1[NW][2];
 
-  // A loads first, then weights: the wait for A of the next step (in-order
-  // completion) then never waits on weights issued after it.
-  auto issue = [&](auto S, int st) {
-    constexpr int s = decltype(S)::value;
+  // Loads of step st (clamped to the last step) into register sets sa / sw.
+  // A loads go first in each step, so the wait for the next step's A rows
+  // (in-order completion) never waits on weights issued after them.
+  auto issue_a = [&](int sa, int st) {
     const int k0 = min(st, nk - 1) * BK;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[s][i] = ld16(arow[i] + k0);
+    for (int i = 0; i < ACH; ++i) ra[sa][i] = ld16(arow[i] + k0);
+  };
+  auto issue_w = [&](int sw, int st) {
+    const int k0 = min(st, nk - 1) * BK;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      b0[s][q] = ld16(wl0 + k0 * 16 + q * 512);
-      if (GATED) b1[s][q] = ld16(wl1 + k0 * 16 + q * 512);
+      b0[sw][q] = ld16(wl0 + k0 * 16 + q * 512);
+      if (GATED) b1[sw][q] = ld16(wl1 + k0 * 16 + q * 512);
     }
   };
-  auto stage = [&](auto S, int buf) {
-    constexpr int s = decltype(S)::value;
+  auto stage = [&](int sa, int buf) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(lds + buf * CH * LDA + aoff[i]) = ra[s][i];
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(lds + buf * CH * LDA + aoff[i]) = ra[sa][i];
   };
-  auto compute = [&](auto S, int buf, int st) {
-    constexpr int s = decltype(S)::value;
+  auto compute = [&](int sw, int buf, int st) {
     const bool live = st < nk;  // past the end: weight operands zeroed
     const bf16_t* As = lds + buf * CH * LDA;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const u32x4 bq0 = live ? b0[s][q] : zero;
-      const u32x4 bq1 = live ? b1[s][q] : zero;
+      const u32x4 bq0 = live ? b0[sw][q] : zero;
+      const u32x4 bq1 = live ? b1[sw][q] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 a = ld16(As + (16 * mt + l16) * LDA + 32 * q + 8 * grp);
@@ -121,30 +132,29 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
       }
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
 
-  issue(I0{}, 0);
-  issue(I1{}, 1);
-  stage(I0{}, 0);
+#pragma unroll
+  for (int j = 0; j < (DA > DW ? DA : DW); ++j) {
+    if (j < DA) issue_a(j, j);
+    if (j < DW) issue_w(j, j);
+  }
+  stage(0, 0);
   __syncthreads();
-  // Step it multiplies LDS buffer it&1 with weight set it%3. Before it, the
-  // loads of step it+2 are issued into set (it+2)%3; after it, step it+1's A
-  // (set (it+1)%3) moves into LDS buffer (it+1)&1, last read by step it-1.
-  for (int it = 0; it < nk; it += 3) {
-    issue(I2{}, it + 2);
-    compute(I0{}, it & 1, it);
-    stage(I1{}, (it + 1) & 1);
-    __syncthreads();
-    issue(I0{}, it + 3);
-    compute(I1{}, (it + 1) & 1, it + 1);
-    stage(I2{}, it & 1);
-    __syncthreads();
-    issue(I1{}, it + 4);
-    compute(I2{}, it & 1, it + 2);
-    stage(I0{}, (it + 1) & 1);
-    __syncthreads();
+  // Step st multiplies LDS buffer st&1 with weight set st%NW. Before it, the
+  // A rows of step st+DA and the weights of step st+DW are issued; after it,
+  // step st+1's A rows move into LDS buffer (st+1)&1, last read by step st-1.
+  // The loop is unrolled by U (a multiple of both set counts) so every set
+  // index is a compile-time constant.
+  for (int it = 0; it < nk; it += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int st = it + j;
+      issue_a((j + DA) % NA, st + DA);
+      issue_w((j + DW) % NW, st + DW);
+      compute(j % NW, (it + j) & 1, st);
+      stage((j + 1) % NA, (st + 1) & 1);
+      __syncthreads();
+    }
   }
 }
 
