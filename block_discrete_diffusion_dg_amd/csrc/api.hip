@@ -257,10 +257,9 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   const float tau = tau_for(g, a->step, a->n_steps);
   const int k_s = (int)(((int64_t)a->step * g.canvas) / a->n_steps);
   dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
-  const int mt = rows >= 256 ? 8 : 2;
-  STAGE(DG_STAGE_LMHEAD, launch_gemm_lmhead(s, mt, c->buf<bf16_t>(L.u), rows, g.d_model, c->embed, g.vocab,
-                                           a->d_canvas, tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
-                                           (int)(sizeof(dg_row_stats) / sizeof(float))));
+  STAGE(DG_STAGE_LMHEAD, launch_lmhead(s, c->buf<bf16_t>(L.u), rows, g.d_model, c->embed, g.vocab, a->d_canvas,
+                                      tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
+                                      (int)(sizeof(dg_row_stats) / sizeof(float))));
   STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats));
   STAGE(DG_STAGE_SAMPLER, launch_sampler(s, stats, a->n_req, g.canvas, g.vocab, a->d_canvas, a->d_committed,
                                          a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats));

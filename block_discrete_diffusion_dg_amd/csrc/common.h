@@ -102,3 +102,18 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
 }
 
 __host__ __device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
+
+// Work-group id -> (column tile nt, row chunk mc) for a grid of NT * MC
+// work-groups. When NT is a multiple of 8, the row chunks of one column tile
+// get ids 8 apart: dispatch is round-robin over the 8 XCDs, so they run on
+// the same XCD and share its L2 copy of the tile's weights.
+__device__ __forceinline__ void xcd_tile_coords(int NT, int MC, int& nt, int& mc) {
+  const int b = blockIdx.x;
+  if ((NT & 7) == 0) {
+    mc = (b >> 3) % MC;
+    nt = (b & 7) + 8 * (b / (8 * MC));
+  } else {
+    mc = b % MC;
+    nt = b / MC;
+  }
+}

@@ -20,17 +20,6 @@ constexpr int DMT = 2;  // rows per chunk = 32
 // five steps ahead instead of relying on other work-groups to hide latency.
 constexpr int DENSE_DW = 5;
 
-__device__ __forceinline__ void tile_coords(int NT, int MC, int& nt, int& mc) {
-  const int b = blockIdx.x;
-  if ((NT & 7) == 0) {
-    mc = (b >> 3) % MC;
-    nt = (b & 7) + 8 * (b / (8 * MC));
-  } else {
-    mc = b % MC;
-    nt = b / MC;
-  }
-}
-
 struct QkvArgs {
   bf16_t* q;  // [rows][Hq*dh]
   KvGeom kv;
@@ -50,7 +39,7 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
   const int dh = p.dh, half = dh >> 1;
   const int NT = (p.Hq + 2 * p.Hkv) * half / 64, MC = div_up(rows, T::CH);
   int nt, mc;
-  tile_coords(NT, MC, nt, mc);
+  xcd_tile_coords(NT, MC, nt, mc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
   const int pw = nt * 64 + wave * 16;  // the wave's first pair
   const int head = pw / half, j = pw % half + l16;
@@ -104,7 +93,7 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
   __shared__ float red[4][T::CH];
   const int NT = N / 64, MC = div_up(rows, T::CH);
   int nt, mc;
-  tile_coords(NT, MC, nt, mc);
+  xcd_tile_coords(NT, MC, nt, mc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
   const int col0 = nt * 64 + wave * 16, col = col0 + l16;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);

@@ -11,7 +11,9 @@
 namespace {
 
 // h[row] = E[ids[row]] in fp32 and u[row] = bf16(RMSNorm(h[row]) * gain).
-// Ids outside [0, V) are clamped (no fault).
+// E is fragment-major (it is also the LM head's streamed matrix): 8
+// consecutive elements of a row are contiguous, so the row is gathered in
+// 16-byte pieces through pack_index. Ids outside [0, V) are clamped (no fault).
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ ids,
                                                     const bf16_t* __restrict__ E, int d, int V,
                                                     float* __restrict__ h,
@@ -21,11 +23,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const int row = blockIdx.x, tid = threadIdx.x;
   int id = ids[row];
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  const bf16_t* src = E + (int64_t)id * d;
   float* dst = h + (int64_t)row * d;
   float ss = 0.f;
   for (int c = tid * 8; c < d; c += 256 * 8) {
-    const u32x4 v = ld16(src + c);
+    const u32x4 v = ld16(E + pack_index(id, c, d));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float a = __uint_as_float(v[j] << 16), b = __uint_as_float(v[j] & 0xffff0000u);
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   __syncthreads();
   const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
   for (int c = tid * 8; c < d; c += 256 * 8) {
-    const u32x4 v = ld16(src + c);
+    const u32x4 v = ld16(E + pack_index(id, c, d));
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -1,7 +1,7 @@
 // Vocabulary statistics merge and the confidence sampler.
 //
 // The LM-head kernel leaves, per row, one (max, sum of exp, argmax) partial
-// for every 64-column slice of the vocabulary. The merge rescales the sums to
+// for every 256-column tile of the vocabulary. The merge rescales the sums to
 // the global max (online log-sum-exp) and keeps the lowest index among equal
 // maxima. The sampler then, per request (one work-group, one thread per
 // canvas position):

@@ -26,10 +26,9 @@ void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w
 // of the updated rows, [N/64][rows]
 void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h, float* ss);
 
-// k_gemm.hip (LM head: LDS-tiled GEMM with fused vocabulary statistics)
-void launch_gemm_lmhead(hipStream_t s, int mt, const bf16_t* a, int rows, int K, const bf16_t* embed,
-                        int V, const int32_t* held, float tau, float4* part, float* held_logit,
-                        int held_stride);
+// k_lmhead.hip (LM head with fused vocabulary statistics; embed fragment-major)
+void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
+                   const int32_t* held, float tau, float4* part, float* held_logit, int held_stride);
 int lmhead_parts(int V);
 
 // k_attn.hip

@@ -47,13 +47,15 @@ __host__ __device__ __forceinline__ int64_t pack_index(int64_t n, int64_t k, int
          (kk & 7);
 }
 
-// acc0[mt][r] (and acc1 when GATED) = sum_k A[row][k] * W[n][k] for
-// row = row0 + 16*mt + 4*(lane/16) + r of the chunk and n = the lane's weight
-// row: lane l16 of the wave's 16-row block(s) w0 (w1), packed fragment-major
-// (w0 = packed matrix + 16*K * block index). A row i of the chunk is
+// acc[nb][mt][r] = sum_k A[row][k] * W_nb[n][k] for row = row0 + 16*mt +
+// 4*(lane/16) + r of the chunk and n = the lane's weight row: lane l16 of the
+// wave's nb-th 16-row block w[nb], packed fragment-major (a block is the
+// packed matrix + 16*K * block index). A row i of the chunk is
 // A + map(row0 + i) * lda with map = rowmap or identity. Rows past nrows
 // repeat the chunk's first row; their accumulators are meaningless and must
 // not be stored. K % 64 == 0.
+// NB blocks per wave: each A fragment read from LDS feeds NB products (a
+// SwiGLU gate/up pair, a RoPE rotate-half pair, or several output blocks).
 // DW / DA: weight loads run DW steps ahead (DW + 1 register sets), A-row
 // loads DA steps ahead (DA + 1 sets). Deeper pipelines keep more bytes in
 // flight per work-group, which matters when few work-groups share a compute
@@ -64,12 +66,11 @@ struct Lcm {
   static constexpr int value = A_ / gcd(A_, B_) * B_;
 };
 
-template <int MT, bool GATED, int DW = 2, int DA = 2>
-__device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
-                                            const int32_t* __restrict__ rowmap, int row0, int nrows,
-                                            const bf16_t* __restrict__ w0,
-                                            const bf16_t* __restrict__ w1, int K,
-                                            f32x4 (&acc0)[MT], f32x4 (&acc1)[MT], bf16_t* lds) {
+template <int MT, int NB, int DW = 2, int DA = 2>
+__device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int lda,
+                                              const int32_t* __restrict__ rowmap, int row0, int nrows,
+                                              const bf16_t* const (&w)[NB], int K, f32x4 (&acc)[NB][MT],
+                                              bf16_t* lds) {
   using T = StreamTile<MT>;
   constexpr int BK = T::BK, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
   constexpr int NW = DW + 1, NA = DA + 1, U = Lcm<NW, NA>::value;
@@ -77,7 +78,9 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
 
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bf16_t* arow[ACH];
   int aoff[ACH];
@@ -90,11 +93,12 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     aoff[i] = r * LDA + kc;
   }
   const int nk = K / BK;
-  const bf16_t* wl0 = w0 + lane * 8;
-  const bf16_t* wl1 = GATED ? w1 + lane * 8 : nullptr;
+  const bf16_t* wl[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wl[nb] = w[nb] + lane * 8;
 
   u32x4 ra[NA][ACH];
-  u32x4 b0[NW][2], b1[NW][2];
+  u32x4 b[NW][NB][2];
 
   // Loads of step st (clamped to the last step) into register sets sa / sw.
   // A loads go first in each step, so the wait for the next step's A rows
@@ -107,10 +111,9 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
   auto issue_w = [&](int sw, int st) {
     const int k0 = min(st, nk - 1) * BK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      b0[sw][q] = ld16(wl0 + k0 * 16 + q * 512);
-      if (GATED) b1[sw][q] = ld16(wl1 + k0 * 16 + q * 512);
-    }
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b[sw][nb][q] = ld16(wl[nb] + k0 * 16 + q * 512);
   };
   auto stage = [&](int sa, int buf) {
 #pragma unroll
@@ -122,13 +125,14 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const u32x4 bq0 = live ? b0[sw][q] : zero;
-      const u32x4 bq1 = live ? b1[sw][q] : zero;
+      u32x4 bq[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bq[nb] = live ? b[sw][nb][q] : zero;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 a = ld16(As + (16 * mt + l16) * LDA + 32 * q + 8 * grp);
-        acc0[mt] = mfma_bf16(a, bq0, acc0[mt]);
-        if (GATED) acc1[mt] = mfma_bf16(a, bq1, acc1[mt]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb][mt] = mfma_bf16(a, bq[nb], acc[nb][mt]);
       }
     }
   };
@@ -155,6 +159,32 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
       stage((j + 1) % NA, (st + 1) & 1);
       __syncthreads();
     }
+  }
+}
+
+// One weight row per lane (acc0), or with GATED two (acc0 from w0, acc1 from
+// w1): the single-block and paired forms of stream_tile_n.
+template <int MT, bool GATED, int DW = 2, int DA = 2>
+__device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
+                                            const int32_t* __restrict__ rowmap, int row0, int nrows,
+                                            const bf16_t* __restrict__ w0,
+                                            const bf16_t* __restrict__ w1, int K,
+                                            f32x4 (&acc0)[MT], f32x4 (&acc1)[MT], bf16_t* lds) {
+  if constexpr (GATED) {
+    const bf16_t* const w[2] = {w0, w1};
+    f32x4 acc[2][MT];
+    stream_tile_n<MT, 2, DW, DA>(A, lda, rowmap, row0, nrows, w, K, acc, lds);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc0[mt] = acc[0][mt];
+      acc1[mt] = acc[1][mt];
+    }
+  } else {
+    const bf16_t* const w[1] = {w0};
+    f32x4 acc[1][MT];
+    stream_tile_n<MT, 1, DW, DA>(A, lda, rowmap, row0, nrows, w, K, acc, lds);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc[0][mt];
   }
 }
 

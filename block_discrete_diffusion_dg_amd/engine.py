@@ -62,9 +62,10 @@ def v_from_cache_order(raw: torch.Tensor) -> torch.Tensor:
 class Engine:
     """One context: weights (bf16, on the GPU), KV cache and workspace tensors.
 
-    `layers` holds row-major tensors (the synth/oracle convention); the
-    streamed projection matrices are repacked on the GPU into the library's
-    fragment-major layout, and only the packed copies are kept."""
+    `layers` and `embed` hold row-major tensors (the synth/oracle
+    convention); the streamed matrices (projections, experts, embedding) are
+    repacked on the GPU into the library's fragment-major layout, and only the
+    packed copies are kept."""
 
     def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
                  embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
@@ -83,6 +84,7 @@ class Engine:
         c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
         c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
         self.c_cfg = c
+        embed = pack_weight(embed)  # the tied LM head streams it fragment-major
         self._keep = [embed, final_norm]
         arr = (B.DGLayerWeights * max(1, len(layers)))()
         for i, lw in enumerate(layers):

@@ -22,9 +22,10 @@
  *     masks. The library never allocates device memory; it keeps the raw
  *     pointers given to dg_create, which must stay valid until dg_destroy.
  *     The dg_ctx itself is host memory owned by the library.
- *   - Weights are bf16 in the [out][in] convention (y = x W^T). Norm gains,
- *     the router and the embedding are row-major; the streamed projection
- *     matrices are in the fragment-major layout made by dg_pack_weight.
+ *   - Weights are bf16 in the [out][in] convention (y = x W^T). Norm gains
+ *     and the router are row-major; the streamed matrices (projections,
+ *     experts, and the embedding, which is also the LM head) are in the
+ *     fragment-major layout made by dg_pack_weight.
  *   - Every call validates its arguments and the cache capacity before it
  *     enqueues anything; on DG_EINVAL / DG_ECAPACITY nothing has been
  *     launched and no state changed. Work is enqueued asynchronously on the
@@ -86,7 +87,8 @@ typedef struct dg_layer_weights {
   const void *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
 } dg_layer_weights;
 
-/* embed [V][d] is also the LM head (tied); final_norm [d];
+/* embed [V][d] is also the LM head (tied), fragment-major (dg_pack_weight
+ * of the row-major [V][d] matrix); final_norm [d];
  * layers: host array of n_layers entries (copied by dg_create). */
 typedef struct dg_weights {
   const void *embed, *final_norm;
