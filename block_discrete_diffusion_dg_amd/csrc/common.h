@@ -87,6 +87,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Reductions over the 16 lanes of each DPP row (lanes 16j .. 16j+15) on
+// the DPP network, with no LDS round trip: butterflies inside each quad
+// (lane ^ 1, lane ^ 2), then the half-row mirror (lane i <-> 7 - i within 8)
+// and the row mirror (i <-> 15 - i). Every lane of the row ends with the same
+// result: each step combines two equal-sized partial results, and the
+// operation is commutative.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_movf(float v) {
+  return __int_as_float(dpp_mov<CTRL>(__float_as_int(v)));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_movf<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_movf<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_movf<DPP_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_movf<DPP_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_movf<DPP_XOR1>(v);
+  v += dpp_movf<DPP_XOR2>(v);
+  v += dpp_movf<DPP_HALF_MIRROR>(v);
+  return v + dpp_movf<DPP_MIRROR>(v);
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_mov<DPP_XOR1>(v));
+  v = min(v, dpp_mov<DPP_XOR2>(v));
+  v = min(v, dpp_mov<DPP_HALF_MIRROR>(v));
+  return min(v, dpp_mov<DPP_MIRROR>(v));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

@@ -110,11 +110,8 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
         h[(int64_t)row * N + col] = v;
         sq = v * v;
       }
-      // sum over the wave's 16 columns (lanes of the same group)
-      sq += __shfl_xor(sq, 1, WAVE);
-      sq += __shfl_xor(sq, 2, WAVE);
-      sq += __shfl_xor(sq, 4, WAVE);
-      sq += __shfl_xor(sq, 8, WAVE);
+      // sum over the wave's 16 columns (the lanes of one DPP row)
+      sq = row16_sum(sq);
       if (l16 == 0) red[wave][16 * mt + 4 * grp + r] = sq;
     }
   if (!ss) return;

@@ -51,33 +51,35 @@ __global__ __launch_bounds__(256) void lmhead_kernel(const bf16_t* __restrict__ 
 
   // Per row (16mt + 4grp + r of the chunk), over the wave's 64 columns
   // (16nb + l16): max, the smallest column holding it, and sum exp2((L - max) k2).
+  // All rows are reduced first (independent chains on the DPP network), then
+  // the held-token logits are picked out.
+  float m[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      m[mt][r] = row16_max(fmaxf(fmaxf(acc[0][mt][r], acc[1][mt][r]), fmaxf(acc[2][mt][r], acc[3][mt][r])));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = 16 * mt + 4 * grp + r;
-      float m = fmaxf(fmaxf(acc[0][mt][r], acc[1][mt][r]), fmaxf(acc[2][mt][r], acc[3][mt][r]));
-      m = fmaxf(m, __shfl_xor(m, 1, WAVE));
-      m = fmaxf(m, __shfl_xor(m, 2, WAVE));
-      m = fmaxf(m, __shfl_xor(m, 4, WAVE));
-      m = fmaxf(m, __shfl_xor(m, 8, WAVE));
       int ix = 0x7fffffff;
       float z = 0.f;
 #pragma unroll
       for (int nb = LM_NB - 1; nb >= 0; --nb) {
         const float v = acc[nb][mt][r];
-        if (v == m) ix = c0 + 16 * nb + l16;
-        z += __builtin_amdgcn_exp2f((v - m) * k2);
+        if (v == m[mt][r]) ix = c0 + 16 * nb + l16;
+        z += __builtin_amdgcn_exp2f((v - m[mt][r]) * k2);
       }
-      ix = min(ix, __shfl_xor(ix, 1, WAVE));
-      ix = min(ix, __shfl_xor(ix, 2, WAVE));
-      ix = min(ix, __shfl_xor(ix, 4, WAVE));
-      ix = min(ix, __shfl_xor(ix, 8, WAVE));
-      z += __shfl_xor(z, 1, WAVE);
-      z += __shfl_xor(z, 2, WAVE);
-      z += __shfl_xor(z, 4, WAVE);
-      z += __shfl_xor(z, 8, WAVE);
-      if (l16 == 0) red[wave][rl] = float4{m, z, __int_as_float(ix), 0.f};
+      ix = row16_min(ix);
+      z = row16_sum(z);
+      if (l16 == 0) red[wave][16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), 0.f};
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rl = 16 * mt + 4 * grp + r;
       const int hc = s_held[rl] - c0;
       if (hc >= 0 && hc < 64 && (hc & 15) == l16) {
         float hv = acc[0][mt][r];

@@ -59,7 +59,7 @@ __device__ __forceinline__ int next_item(int32_t* counter, int* s_slot) {
 }
 
 template <int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void moe_experts_kernel(MoeArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2 : 3))) void moe_experts_kernel(MoeArgs p) {
   using T = StreamTile<MT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
   __shared__ int32_t s_gu[MOE_MAX_GROUPS + 1], s_dn[MOE_MAX_GROUPS + 1], s_ch[MOE_MAX_GROUPS + 1];
