@@ -34,6 +34,10 @@ namespace {
 
 constexpr int KT = 64;  // keys per tile
 
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (the lgkm and export counters are not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
 }
@@ -49,22 +53,35 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   constexpr int NS = DH / 32;  // 32-dim steps of QK^T
   constexpr int ND = DH / 16;  // 16-dim output subtiles
   constexpr int CHUNKS = 4 * NS + 2 * ND;
-  __shared__ __align__(16) u32x4 tbA[CHUNKS][64];  // two distinct buffers: a copy into
-  __shared__ __align__(16) u32x4 tbB[CHUNKS][64];  // one never delays reads of the other
+  // a ring of distinct buffers: a copy into one never delays reads of another
+  __shared__ __align__(16) u32x4 tb0[CHUNKS][64];
+  __shared__ __align__(16) u32x4 tb1[CHUNKS][64];
+  __shared__ __align__(16) u32x4 tb2[CHUNKS][64];
+  __shared__ __align__(16) u32x4 tb3[CHUNKS][64];
   __shared__ int s_last;
   const int rep = Hq / Hkv;
   const int n = rt.rows_per_req;
   const int rows_total = rt.n_req * n;
   const int nqv = n * rep;
   const int qblocks = div_up(nqv, 64);
-  int b = blockIdx.x;
-  const int split = b % nsplit;
-  b /= nsplit;
-  const int group = b;  // (request, kv head, query block)
-  const int qb = b % qblocks;
-  b /= qblocks;
-  const int g = b % Hkv;
-  const int r = b / Hkv;
+  // Work-group id -> (key range c = (request, kv head, split), query block).
+  // The query blocks of one key range read the same K/V tiles, so they get
+  // ids that are equal modulo 8: dispatch is round-robin over the 8 XCDs,
+  // so they share one XCD's L2 copy of those tiles (fetched from HBM once).
+  // Ranges go in runs of 8: run cb holds ranges 8cb .. 8cb+width-1, ordered
+  // query block major.
+  const int C = rt.n_req * Hkv * nsplit;
+  int c, qb;
+  {
+    const int b = blockIdx.x, run = 8 * qblocks;
+    const int cb = b / run, rem = b % run, width = min(8, C - 8 * cb);
+    qb = rem / width;
+    c = 8 * cb + rem % width;
+  }
+  const int split = c % nsplit;
+  const int g = (c / nsplit) % Hkv;
+  const int r = c / (nsplit * Hkv);
+  const int group = (r * Hkv + g) * qblocks + qb;  // (request, kv head, query block)
 
   const int P = rt.pos0[r];
   const int nk = P + n;
@@ -141,13 +158,28 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
 
   auto compute_tile = [&](int tile, const u32x4 (&tb)[CHUNKS][64]) {
     const int k0 = tile * KT;
+    // Every operand fragment of the tile is read from LDS up front, in the
+    // order of use, so the reads overlap each other and the products (a read
+    // followed at once by its product would stall on every fragment). The
+    // score products then run dim-step outer, key-subtile inner: four
+    // independent accumulation chains.
+    u32x4 kf[NS][4], vf[2][ND];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[st][ks] = tb[ks * NS + st][lane];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) vf[kk][dt] = tb[4 * NS + kk * ND + dt][lane];
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 s[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < 4; ++ks) s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NS; ++st) s[ks] = mfma_bf16(tb[ks * NS + st][lane], qf[st], s[ks]);
-    }
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) s[ks] = mfma_bf16(kf[st][ks], qf[st], s[ks]);
     if (k0 + KT > nk || (causal && k0 + KT - 1 > P + qi_lo)) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -184,9 +216,6 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
       const u32x4 pf = {pack_bf16x2(s[2 * kk][0], s[2 * kk][1]), pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
                         pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
                         pack_bf16x2(s[2 * kk + 1][2], s[2 * kk + 1][3])};
-      u32x4 vf[ND];
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) vf[dt] = tb[4 * NS + kk * ND + dt][lane];
       if (k0 + KT > nk) {
         // keys past nk: V entries may be unwritten cache rows (any bit
         // pattern); zero them so that 0 * V stays 0
@@ -195,31 +224,63 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
           const int key = k0 + 32 * kk + (e >> 2) * 16 + 4 * grp + (e & 3);
           const uint32_t keep = key < nk ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt) vf[dt][e >> 1] &= keep;
+          for (int dt = 0; dt < ND; ++dt) vf[kk][dt][e >> 1] &= keep;
         }
       }
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma_bf16(vf[dt], pf, oacc[dt]);
+      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma_bf16(vf[kk][dt], pf, oacc[dt]);
       lacc = mfma_bf16(ones, pf, lacc);
     }
   };
 
-  if (t0 < t1) copy_tile(t0, tbA);
-  // the query fragments load while the first tile is in flight
+  // Tiles t0 .. t1-1 cycle through the ring; tile t + 3 is copied while
+  // tile t is computed. Before tile t, this wave waits only for its own
+  // copies of tile t (the copies of up to two later tiles stay in flight:
+  // they complete in issue order), then the barrier makes every wave's
+  // copies visible and ensures buffer (t + 3) % 4, read by tile t - 1, is
+  // free. The barrier carries no fence: a release fence would wait for every
+  // outstanding copy. The empty memory-clobbering statements keep the
+  // compiler from moving LDS accesses across it.
+  if (t0 < t1) copy_tile(t0, tb0);
+  if (t0 + 1 < t1) copy_tile(t0 + 1, tb1);
+  if (t0 + 2 < t1) copy_tile(t0 + 2, tb2);
+  // the query fragments load while the first tiles are in flight; then
+  // everything is waited for once, so that inside the loop only tile copies
+  // are ever outstanding (the compiler would otherwise order the first use
+  // of the query registers after every copy in flight)
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     qf[s] = qvalid ? ld16(q + ((int64_t)row * Hq + qh) * DH + 32 * s + 8 * grp) : zero;
-  for (int tile = t0; tile < t1; tile += 2) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the tile have landed
-    __syncthreads();                // ... and every other wave's; buffer B is free
-    if (tile + 1 < t1) copy_tile(tile + 1, tbB);
-    compute_tile(tile, tbA);
+  __builtin_amdgcn_s_waitcnt(0);
+  auto ring_sync = [&](int tile) {
+    const int later = min(t1 - 1 - tile, 2);  // tiles issued after this one
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPW));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  for (int tile = t0; tile < t1; tile += 4) {
+    ring_sync(tile);
+    if (tile + 3 < t1) copy_tile(tile + 3, tb3);
+    compute_tile(tile, tb0);
     if (tile + 1 >= t1) break;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tile + 2 < t1) copy_tile(tile + 2, tbA);
-    compute_tile(tile + 1, tbB);
+    ring_sync(tile + 1);
+    if (tile + 4 < t1) copy_tile(tile + 4, tb0);
+    compute_tile(tile + 1, tb1);
+    if (tile + 2 >= t1) break;
+    ring_sync(tile + 2);
+    if (tile + 5 < t1) copy_tile(tile + 5, tb1);
+    compute_tile(tile + 2, tb2);
+    if (tile + 3 >= t1) break;
+    ring_sync(tile + 3);
+    if (tile + 6 < t1) copy_tile(tile + 6, tb2);
+    compute_tile(tile + 3, tb3);
   }
 
   const float l_tot = lacc[0];  // every row of the ones-product holds the column sum

@@ -227,17 +227,19 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
 
 }  // namespace
 
-// Rows per work item: 64-row chunks once experts average at least 8 rows,
+// Rows per work item. Every chunk of an expert streams all of that expert's
+// weights, so a hot expert cut into many small chunks multiplies its weight
+// traffic: 128-row chunks once experts average at least 16 rows, 64 from 8,
 // else 32 (tiny batches).
 int moe_rows_per_chunk(int rows, int E, int k) {
-  return rows * k >= 8 * E ? 64 : 32;
+  return rows * k >= 16 * E ? 128 : rows * k >= 8 * E ? 64 : 32;
 }
 
 // Chunks over all groups: sum_e ceil(cnt_e / ch) + ceil(rows / ch) is at most
-// rows*k/ch + E + rows/ch + 1.
+// rows*k/ch + E + rows/ch + 1; bounded with the smallest chunk size, so that
+// it holds for every call of at most `rows` rows.
 int moe_chunk_bound(int rows, int E, int k) {
-  const int ch = moe_rows_per_chunk(rows, E, k);
-  return div_up(rows * k, ch) + E + div_up(rows, ch) + 1;
+  return div_up(rows * k, 32) + E + div_up(rows, 32) + 1;
 }
 
 // Persistent grid: as many work-groups as the GPU holds at once (queried
@@ -256,7 +258,7 @@ static int resident_blocks(Kernel kernel, int& cache) {
   }
   return cache;
 }
-static int g_resident[2];  // MT=4, MT=2
+static int g_resident[3];  // MT=8, MT=4, MT=2
 
 void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, int Fs, int E, int k,
                         const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
@@ -264,11 +266,15 @@ void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, 
                         const bf16_t* wd, const bf16_t* sg, const bf16_t* su, const bf16_t* sd, bf16_t* hid,
                         bf16_t* hid_s, float* y, float* ys) {
   MoeArgs p{u, rows, d, F, Fs, E, perm, cnt, off, wts, widx, items, wg, wu, wd, sg, su, sd, hid, hid_s, y, ys};
-  if (moe_rows_per_chunk(rows, E, k) == 64)
-    hipLaunchKernelGGL(moe_experts_kernel<4>, dim3(resident_blocks(moe_experts_kernel<4>, g_resident[0])),
+  const int ch = moe_rows_per_chunk(rows, E, k);
+  if (ch == 128)
+    hipLaunchKernelGGL(moe_experts_kernel<8>, dim3(resident_blocks(moe_experts_kernel<8>, g_resident[0])),
+                       dim3(256), 0, s, p);
+  else if (ch == 64)
+    hipLaunchKernelGGL(moe_experts_kernel<4>, dim3(resident_blocks(moe_experts_kernel<4>, g_resident[1])),
                        dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(moe_experts_kernel<2>, dim3(resident_blocks(moe_experts_kernel<2>, g_resident[1])),
+    hipLaunchKernelGGL(moe_experts_kernel<2>, dim3(resident_blocks(moe_experts_kernel<2>, g_resident[2])),
                        dim3(256), 0, s, p);
 }
 
