@@ -43,7 +43,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.attn_o = take(R * qd * 2);
   L.attn_part = take((size_t)DG_ATTN_SPLITS * R * qd * 4);
   const size_t groups = attn_groups_bound(c.max_rows, c.n_q_heads, c.n_kv_heads);
-  L.attn_ml = take((size_t)DG_ATTN_SPLITS * groups * 64 * 8);
+  L.attn_ml = take((size_t)DG_ATTN_SPLITS * groups * attn_group_queries() * 8);
   L.rope = take(R * (c.head_dim / 2) * 8);
   L.z = take(R * E * 4);
   L.idx = take(R * k * 4);

@@ -3,9 +3,12 @@
 // h = g*rep .. g*rep+rep-1 read kv head g). Denoising uses no mask inside the
 // block; the causal encoder (commit / prefill) masks keys after the query.
 //
-// A work-group takes 64 query vectors of one (request, kv head), 16 per wave,
-// and one contiguous range of 64-key tiles (a split of the keys), keeping an
-// online softmax per query. Operands come straight from the KV cache:
+// A work-group takes 64*QB query vectors of one (request, kv head), QB
+// blocks of 16 per wave, and one contiguous range of 64-key tiles (a split of
+// the keys), keeping an online softmax per query. Each K/V fragment a wave
+// reads from LDS feeds the products of all of its query blocks. (QB = 2
+// halves the LDS traffic per query but measured slower here: it halves the
+// work-groups, and their registers allow one per compute unit.) Operands come straight from the KV cache:
 //   S^T = K Q^T: the A operand is 16 keys x 32 dims of K, row-major in the
 //     cache (16 contiguous bytes per lane), the B operand the wave's queries.
 //   O^T = V^T P^T: the score accumulators already sit in the B-operand layout
@@ -18,7 +21,9 @@
 // fragment with one linear, conflict-free LDS load, and the four waves share
 // one copy of the tile. The next tile's copy is issued as soon as the current
 // tile is in place; because the two buffers are distinct objects, reading one
-// never waits for the copy into the other.
+// never waits for the copy into the other. (A deeper ring of copies measured
+// no faster: the tile's LDS reads and softmax, not the copy, set the pace,
+// and 64 KB of LDS leaves room for two work-groups per compute unit.)
 // Softmax work is kept off the common path: keys are masked only on tiles
 // that reach past the cache length or (causal) past a query's position, the
 // running output is rescaled only when some query's maximum moved, and the
@@ -33,10 +38,9 @@
 namespace {
 
 constexpr int KT = 64;  // keys per tile
+constexpr int QB = 1;   // 16-query blocks per wave
+constexpr int ATTN_QWG = 64 * QB;  // query vectors per work-group
 
-// s_waitcnt immediate: wait until at most n vector-memory operations of this
-// wave are outstanding (the lgkm and export counters are not waited on).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
@@ -53,17 +57,16 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   constexpr int NS = DH / 32;  // 32-dim steps of QK^T
   constexpr int ND = DH / 16;  // 16-dim output subtiles
   constexpr int CHUNKS = 4 * NS + 2 * ND;
-  // a ring of distinct buffers: a copy into one never delays reads of another
-  __shared__ __align__(16) u32x4 tb0[CHUNKS][64];
-  __shared__ __align__(16) u32x4 tb1[CHUNKS][64];
-  __shared__ __align__(16) u32x4 tb2[CHUNKS][64];
-  __shared__ __align__(16) u32x4 tb3[CHUNKS][64];
+  constexpr int QPW = 16 * QB;  // query vectors per wave
+  // two distinct buffers: a copy into one never delays reads of the other
+  __shared__ __align__(16) u32x4 tbA[CHUNKS][64];
+  __shared__ __align__(16) u32x4 tbB[CHUNKS][64];
   __shared__ int s_last;
   const int rep = Hq / Hkv;
   const int n = rt.rows_per_req;
   const int rows_total = rt.n_req * n;
   const int nqv = n * rep;
-  const int qblocks = div_up(nqv, 64);
+  const int qblocks = div_up(nqv, ATTN_QWG);
   // Work-group id -> (key range c = (request, kv head, split), query block).
   // The query blocks of one key range read the same K/V tiles, so they get
   // ids that are equal modulo 8: dispatch is round-robin over the 8 XCDs,
@@ -91,23 +94,34 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   const int t1 = min(tiles, t0 + per);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int qv = qb * 64 + wave * 16 + l16;
-  const bool qvalid = qv < nqv;
-  const int qi = qvalid ? qv / rep : 0;
-  const int qh = g * rep + (qvalid ? qv % rep : 0);
-  const int row = r * n + qi;
-
-  u32x4 qf[NS];
-
-  f32x4 oacc[ND];
+  // query block j of the wave: query vectors qb*QWG + wave*QPW + 16j + l16
+  bool qvalid[QB];
+  int qh[QB], row[QB], qlimit[QB];
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running maximum of scale_log2 * score
+  for (int j = 0; j < QB; ++j) {
+    const int qv = qb * ATTN_QWG + wave * QPW + 16 * j + l16;
+    qvalid[j] = qv < nqv;
+    const int qi = qvalid[j] ? qv / rep : 0;
+    qh[j] = g * rep + (qvalid[j] ? qv % rep : 0);
+    row[j] = r * n + qi;
+    qlimit[j] = P + qi;  // causal: keys at positions <= P + qi
+  }
+
+  u32x4 qf[QB][NS];
+  f32x4 oacc[QB][ND];
+  f32x4 lacc[QB];
+  float m_run[QB];  // running maximum of scale_log2 * score
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) oacc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+  }
 
   const int slot = rt.slot[r];
   const bf16_t* Kp = kv.k_plane(slot, layer, g);
   const bf16_t* Vp = kv.v_plane(slot, layer, g);
-  const int qlimit = P + qi;  // causal: keys at positions <= P + qi
 
   // Fragments of a tile: K subtile ks (16 keys) x dim step st at ks*NS + st,
   // then V block kk (32 keys) x dim subtile dt at 4*NS + kk*ND + dt. Wave w
@@ -119,195 +133,173 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   constexpr int CPW = CHUNKS / 4;  // chunks per wave
   const bf16_t* cbase[CPW];
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int c = wave + 4 * j;
-    if (c < 4 * NS) {
-      cbase[j] = Kp + (int64_t)(16 * (c / NS) + l16) * DH + 32 * (c % NS) + 8 * grp;
+  for (int jc = 0; jc < CPW; ++jc) {
+    const int ch = wave + 4 * jc;
+    if (ch < 4 * NS) {
+      cbase[jc] = Kp + (int64_t)(16 * (ch / NS) + l16) * DH + 32 * (ch % NS) + 8 * grp;
     } else {
-      const int kk = (c - 4 * NS) / ND, dt = (c - 4 * NS) % ND;
-      cbase[j] = Vp + ((int64_t)(kk * 4 + grp) * DH + 16 * dt + l16) * 8;
+      const int kk = (ch - 4 * NS) / ND, dt = (ch - 4 * NS) % ND;
+      cbase[jc] = Vp + ((int64_t)(kk * 4 + grp) * DH + 16 * dt + l16) * 8;
     }
   }
   auto copy_tile = [&](int tile, u32x4 (&tb)[CHUNKS][64]) {
     const int k0 = tile * KT;
     const bool edge = k0 + KT > nk;
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int c = wave + 4 * j;
-      const bf16_t* src = cbase[j] + (int64_t)k0 * DH;
+    for (int jc = 0; jc < CPW; ++jc) {
+      const int ch = wave + 4 * jc;
+      const bf16_t* src = cbase[jc] + (int64_t)k0 * DH;
       if (edge) {
-        if (c < 4 * NS) {
-          const int key = min(k0 + 16 * (c / NS) + l16, nk - 1);
-          src = Kp + (int64_t)key * DH + 32 * (c % NS) + 8 * grp;
+        if (ch < 4 * NS) {
+          const int key = min(k0 + 16 * (ch / NS) + l16, nk - 1);
+          src = Kp + (int64_t)key * DH + 32 * (ch % NS) + 8 * grp;
         } else {
-          const int kk = (c - 4 * NS) / ND, dt = (c - 4 * NS) % ND;
+          const int kk = (ch - 4 * NS) / ND, dt = (ch - 4 * NS) % ND;
           const int blk = min((k0 + 32 * kk) >> 5, (nk - 1) >> 5);
           src = Vp + (((int64_t)blk * 4 + grp) * DH + 16 * dt + l16) * 8;
         }
       }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tb[c][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&tb[ch][0], 16, 0, 0);
     }
   };
   // smallest query position of the wave: causal masking is needed only on
   // tiles reaching past it
-  const int qi_lo = min((qb * 64 + wave * 16) / rep, n - 1);
+  const int qi_lo = min((qb * ATTN_QWG + wave * QPW) / rep, n - 1);
   // the denominator runs on the matrix cores: an all-ones A operand turns the
   // probabilities of the PV product into their column sums
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 
   auto compute_tile = [&](int tile, const u32x4 (&tb)[CHUNKS][64]) {
     const int k0 = tile * KT;
-    // Every operand fragment of the tile is read from LDS up front, in the
-    // order of use, so the reads overlap each other and the products (a read
-    // followed at once by its product would stall on every fragment). The
-    // score products then run dim-step outer, key-subtile inner: four
-    // independent accumulation chains.
-    u32x4 kf[NS][4], vf[2][ND];
+    // Fragments are read from LDS at their use; the compiler schedules the
+    // reads. (Forcing all 32 reads ahead of the products costs the registers
+    // that let two work-groups share a compute unit, and measured no faster.)
+    f32x4 s[QB][4];
 #pragma unroll
-    for (int st = 0; st < NS; ++st)
+    for (int j = 0; j < QB; ++j)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[st][ks] = tb[ks * NS + st][lane];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) vf[kk][dt] = tb[4 * NS + kk * ND + dt][lane];
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 s[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < NS; ++st)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s[ks] = mfma_bf16(kf[st][ks], qf[st], s[ks]);
-    if (k0 + KT > nk || (causal && k0 + KT - 1 > P + qi_lo)) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = k0 + 16 * ks + 4 * grp + rr;
-          if (key >= nk || (causal && key > qlimit)) s[ks][rr] = -INFINITY;
-        }
-    }
-    float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                             fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
-    // running maximum in the scaled log2 domain (scale > 0 keeps the order)
-    const float m_new = fmaxf(m_run, tmax * scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    // alpha == 1 exactly when the maximum did not move: skip the rescale
-    // when that holds for every query of the wave
-    if (__ballot(m_new != m_run) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      lacc *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) oacc[dt] *= alpha;
-    }
-    m_run = m_new;
+      for (int ks = 0; ks < 4; ++ks) s[j][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) s[ks][rr] = __builtin_amdgcn_exp2f(fmaf(s[ks][rr], scale_log2, -m_use));
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 kf = tb[ks * NS + st][lane];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 pf = {pack_bf16x2(s[2 * kk][0], s[2 * kk][1]), pack_bf16x2(s[2 * kk][2], s[2 * kk][3]),
-                        pack_bf16x2(s[2 * kk + 1][0], s[2 * kk + 1][1]),
-                        pack_bf16x2(s[2 * kk + 1][2], s[2 * kk + 1][3])};
-      if (k0 + KT > nk) {
-        // keys past nk: V entries may be unwritten cache rows (any bit
-        // pattern); zero them so that 0 * V stays 0
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = k0 + 32 * kk + (e >> 2) * 16 + 4 * grp + (e & 3);
-          const uint32_t keep = key < nk ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) vf[kk][dt][e >> 1] &= keep;
-        }
+        for (int j = 0; j < QB; ++j) s[j][ks] = mfma_bf16(kf, qf[j][st], s[j][ks]);
       }
+    const bool v_edge = k0 + KT > nk;
+    const bool mask = v_edge || (causal && k0 + KT - 1 > P + qi_lo);
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) oacc[dt] = mfma_bf16(vf[kk][dt], pf, oacc[dt]);
-      lacc = mfma_bf16(ones, pf, lacc);
+    for (int j = 0; j < QB; ++j) {
+      if (mask) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int key = k0 + 16 * ks + 4 * grp + rr;
+            if (key >= nk || (causal && key > qlimit[j])) s[j][ks][rr] = -INFINITY;
+          }
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(s[j][0][0], s[j][0][1]), fmaxf(s[j][0][2], s[j][0][3])),
+                         fmaxf(fmaxf(s[j][1][0], s[j][1][1]), fmaxf(s[j][1][2], s[j][1][3])));
+      tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[j][2][0], s[j][2][1]), fmaxf(s[j][2][2], s[j][2][3])),
+                               fmaxf(fmaxf(s[j][3][0], s[j][3][1]), fmaxf(s[j][3][2], s[j][3][3]))));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
+      // running maximum in the scaled log2 domain (scale > 0 keeps the order)
+      const float m_new = fmaxf(m_run[j], tmax * scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      // alpha == 1 exactly when the maximum did not move: skip the rescale
+      // when that holds for every query of the block
+      if (__ballot(m_new != m_run[j]) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_use);
+        lacc[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) oacc[j][dt] *= alpha;
+      }
+      m_run[j] = m_new;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          s[j][ks][rr] = __builtin_amdgcn_exp2f(fmaf(s[j][ks][rr], scale_log2, -m_use));
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 pf = {pack_bf16x2(s[j][2 * kk][0], s[j][2 * kk][1]),
+                          pack_bf16x2(s[j][2 * kk][2], s[j][2 * kk][3]),
+                          pack_bf16x2(s[j][2 * kk + 1][0], s[j][2 * kk + 1][1]),
+                          pack_bf16x2(s[j][2 * kk + 1][2], s[j][2 * kk + 1][3])};
+        u32x4 vf[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vf[dt] = tb[4 * NS + kk * ND + dt][lane];
+        if (v_edge) {
+          // keys past nk: V entries may be unwritten cache rows (any bit
+          // pattern); zero them so that 0 * V stays 0
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = k0 + 32 * kk + (e >> 2) * 16 + 4 * grp + (e & 3);
+            const uint32_t keep = key < nk ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) vf[dt][e >> 1] &= keep;
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) oacc[j][dt] = mfma_bf16(vf[dt], pf, oacc[j][dt]);
+        lacc[j] = mfma_bf16(ones, pf, lacc[j]);
+      }
     }
   };
 
-  // Tiles t0 .. t1-1 cycle through the ring; tile t + 3 is copied while
-  // tile t is computed. Before tile t, this wave waits only for its own
-  // copies of tile t (the copies of up to two later tiles stay in flight:
-  // they complete in issue order), then the barrier makes every wave's
-  // copies visible and ensures buffer (t + 3) % 4, read by tile t - 1, is
-  // free. The barrier carries no fence: a release fence would wait for every
-  // outstanding copy. The empty memory-clobbering statements keep the
-  // compiler from moving LDS accesses across it.
-  if (t0 < t1) copy_tile(t0, tb0);
-  if (t0 + 1 < t1) copy_tile(t0 + 1, tb1);
-  if (t0 + 2 < t1) copy_tile(t0 + 2, tb2);
-  // the query fragments load while the first tiles are in flight; then
-  // everything is waited for once, so that inside the loop only tile copies
-  // are ever outstanding (the compiler would otherwise order the first use
-  // of the query registers after every copy in flight)
+  // Tiles alternate between the two buffers: the copy of tile t + 1 is
+  // issued as soon as tile t is in place (every wave waited for its own
+  // copies, then the barrier) and overlaps the products of tile t.
+  if (t0 < t1) copy_tile(t0, tbA);
+  // the query fragments load while the first tile is in flight
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qf[s] = qvalid ? ld16(q + ((int64_t)row * Hq + qh) * DH + 32 * s + 8 * grp) : zero;
-  __builtin_amdgcn_s_waitcnt(0);
-  auto ring_sync = [&](int tile) {
-    const int later = min(t1 - 1 - tile, 2);  // tiles issued after this one
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPW));
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  for (int tile = t0; tile < t1; tile += 4) {
-    ring_sync(tile);
-    if (tile + 3 < t1) copy_tile(tile + 3, tb3);
-    compute_tile(tile, tb0);
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      qf[j][st] = qvalid[j] ? ld16(q + ((int64_t)row[j] * Hq + qh[j]) * DH + 32 * st + 8 * grp) : zero;
+  for (int tile = t0; tile < t1; tile += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the tile have landed
+    __syncthreads();                // ... and every other wave's; buffer B is free
+    if (tile + 1 < t1) copy_tile(tile + 1, tbB);
+    compute_tile(tile, tbA);
     if (tile + 1 >= t1) break;
-    ring_sync(tile + 1);
-    if (tile + 4 < t1) copy_tile(tile + 4, tb0);
-    compute_tile(tile + 1, tb1);
-    if (tile + 2 >= t1) break;
-    ring_sync(tile + 2);
-    if (tile + 5 < t1) copy_tile(tile + 5, tb1);
-    compute_tile(tile + 2, tb2);
-    if (tile + 3 >= t1) break;
-    ring_sync(tile + 3);
-    if (tile + 6 < t1) copy_tile(tile + 6, tb2);
-    compute_tile(tile + 3, tb3);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 2 < t1) copy_tile(tile + 2, tbA);
+    compute_tile(tile + 1, tbB);
   }
 
-  const float l_tot = lacc[0];  // every row of the ones-product holds the column sum
   // lane (grp, l16) holds output dims 16dt + 4grp + 0..3 of query column l16
+  // of each block; every row of the ones-product holds the column sum
   if (nsplit == 1) {
-    if (qvalid) {
-      const float inv = 1.0f / l_tot;
-      bf16_t* op = out + ((int64_t)row * Hq + qh) * DH;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      if (!qvalid[j]) continue;
+      const float inv = 1.0f / lacc[j][0];
+      bf16_t* op = out + ((int64_t)row[j] * Hq + qh[j]) * DH;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
         *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * grp) =
-            u32x2{pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv), pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv)};
+            u32x2{pack_bf16x2(oacc[j][dt][0] * inv, oacc[j][dt][1] * inv),
+                  pack_bf16x2(oacc[j][dt][2] * inv, oacc[j][dt][3] * inv)};
     }
     return;
   }
-  {
-    const int64_t base = ((int64_t)split * rows_total + row) * Hq + qh;
-    if (qvalid) {
-      float* op = opart + base * DH;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) store16_coherent(op + 16 * dt + 4 * grp, __builtin_bit_cast(u32x4, oacc[dt]));
-      // (max, sum) group-major, [group][split][64 queries]: a group's entries
-      // fill whole lines that no other group touches
-      if (grp == 0)
-        store8_coherent(ml + ((int64_t)group * nsplit + split) * 64 + wave * 16 + l16,
-                        u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)});
-    }
+  for (int j = 0; j < QB; ++j) {
+    if (!qvalid[j]) continue;
+    float* op = opart + (((int64_t)split * rows_total + row[j]) * Hq + qh[j]) * DH;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) store16_coherent(op + 16 * dt + 4 * grp, __builtin_bit_cast(u32x4, oacc[j][dt]));
+    // (max, sum) group-major, [group][split][ATTN_QWG queries]: a group's
+    // entries fill whole lines that no other group touches
+    if (grp == 0)
+      store8_coherent(ml + ((int64_t)group * nsplit + split) * ATTN_QWG + wave * QPW + 16 * j + l16,
+                      u32x2{__float_as_uint(m_run[j]), __float_as_uint(lacc[j][0])});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -317,46 +309,50 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
     if (s_last) __hip_atomic_store(sync + group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (!s_last || !qvalid) return;
+  if (!s_last) return;
   // merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, split order.
   // The group's partial lines are read only here, after every split wrote
   // them, and caches start the kernel invalidated: no stale copies.
   constexpr int MAXS = DG_ATTN_SPLITS;
-  float2 mls[MAXS];
-  float M = -INFINITY;
 #pragma unroll
-  for (int sp = 0; sp < MAXS; ++sp) {
-    if (sp >= nsplit) break;
-    mls[sp] = ml[((int64_t)group * nsplit + sp) * 64 + wave * 16 + l16];
-    M = fmaxf(M, mls[sp].x);
-  }
-  float num[ND][4], den = 0.f;
+  for (int j = 0; j < QB; ++j) {
+    if (!qvalid[j]) continue;
+    float2 mls[MAXS];
+    float M = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) num[dt][rr] = 0.f;
-#pragma unroll
-  for (int sp = 0; sp < MAXS; ++sp) {
-    if (sp >= nsplit) break;
-    if (mls[sp].x == -INFINITY) continue;
-    const float wgt = exp2f(mls[sp].x - M);
-    den += wgt * mls[sp].y;
-    const float* op = opart + (((int64_t)sp * rows_total + row) * Hq + qh) * DH;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const float4 v = *reinterpret_cast<const float4*>(op + 16 * dt + 4 * grp);
-      num[dt][0] += wgt * v.x;
-      num[dt][1] += wgt * v.y;
-      num[dt][2] += wgt * v.z;
-      num[dt][3] += wgt * v.w;
+    for (int sp = 0; sp < MAXS; ++sp) {
+      if (sp >= nsplit) break;
+      mls[sp] = ml[((int64_t)group * nsplit + sp) * ATTN_QWG + wave * QPW + 16 * j + l16];
+      M = fmaxf(M, mls[sp].x);
     }
-  }
-  const float inv = 1.0f / den;
-  bf16_t* op = out + ((int64_t)row * Hq + qh) * DH;
+    float num[ND][4], den = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * grp) =
-        u32x2{pack_bf16x2(num[dt][0] * inv, num[dt][1] * inv), pack_bf16x2(num[dt][2] * inv, num[dt][3] * inv)};
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) num[dt][rr] = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < MAXS; ++sp) {
+      if (sp >= nsplit) break;
+      if (mls[sp].x == -INFINITY) continue;
+      const float wgt = exp2f(mls[sp].x - M);
+      den += wgt * mls[sp].y;
+      const float* op = opart + (((int64_t)sp * rows_total + row[j]) * Hq + qh[j]) * DH;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const float4 v = *reinterpret_cast<const float4*>(op + 16 * dt + 4 * grp);
+        num[dt][0] += wgt * v.x;
+        num[dt][1] += wgt * v.y;
+        num[dt][2] += wgt * v.z;
+        num[dt][3] += wgt * v.w;
+      }
+    }
+    const float inv = 1.0f / den;
+    bf16_t* op = out + ((int64_t)row[j] * Hq + qh[j]) * DH;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * grp) =
+          u32x2{pack_bf16x2(num[dt][0] * inv, num[dt][1] * inv), pack_bf16x2(num[dt][2] * inv, num[dt][3] * inv)};
+  }
 }
 
 }  // namespace
@@ -366,7 +362,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
   (void)max_rows;
   const int rep = Hq / Hkv;
-  const int base = rt.n_req * Hkv * div_up(rt.rows_per_req * rep, 64);
+  const int base = rt.n_req * Hkv * div_up(rt.rows_per_req * rep, ATTN_QWG);
   int max_pos = 0;
   for (int r = 0; r < rt.n_req; ++r) max_pos = max(max_pos, rt.pos0[r]);
   const int tiles = div_up(max_pos + rt.rows_per_req, KT);
@@ -377,13 +373,15 @@ int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
 }
 
 // (request, kv head, query block) groups of a call of at most max_rows rows:
-// sum_r Hkv * ceil(n_r * rep / 64) <= max_rows * Hq / 64 + DG_MAX_REQ * Hkv.
-int attn_groups_bound(int max_rows, int Hq, int Hkv) { return div_up(max_rows * Hq, 64) + DG_MAX_REQ * Hkv; }
+// sum_r Hkv * ceil(n_r * rep / QWG) <= max_rows * Hq / QWG + DG_MAX_REQ * Hkv.
+int attn_groups_bound(int max_rows, int Hq, int Hkv) { return div_up(max_rows * Hq, ATTN_QWG) + DG_MAX_REQ * Hkv; }
+
+int attn_group_queries() { return ATTN_QWG; }
 
 void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int layer, const ReqTable& rt, int Hq,
                       int Hkv, int dh, int causal, int nsplit, float* opart, float2* ml, int32_t* sync, bf16_t* out) {
   const int rep = Hq / Hkv;
-  const int blocks = rt.n_req * Hkv * div_up(rt.rows_per_req * rep, 64) * nsplit;
+  const int blocks = rt.n_req * Hkv * div_up(rt.rows_per_req * rep, ATTN_QWG) * nsplit;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)dh);
   if (dh == 128)
     hipLaunchKernelGGL(attn_kernel<128>, dim3(blocks), dim3(256), 0, s, q, kv, layer, rt, Hq, Hkv, causal, nsplit,

@@ -34,6 +34,7 @@ int lmhead_parts(int V);
 // k_attn.hip
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows);
 int attn_groups_bound(int max_rows, int Hq, int Hkv);
+int attn_group_queries();  // query vectors per (request, kv head, query block) group
 // V planes of the KV cache hold each 32-key block in matrix-core operand
 // order: key o of the block, dim c at element ((o%16)/4 * dh + c) * 8 +
 // (o/16)*4 + o%4 of the block (32*dh elements).
