@@ -198,14 +198,21 @@ def _cache_rows(eng, slot, layer, lo, hi):
     return k.permute(1, 0, 2).contiguous().cpu(), v.permute(1, 0, 2).contiguous().cpu()
 
 
-@pytest.mark.parametrize("name,causal", [("tiny", False), ("tiny", True), ("one_layer", False),
-                                         ("one_layer", True)])
-def test_layer_parity(name, causal):
+# (workload, causal, prefix, rows): the workloads' own layer shapes, plus the
+# full-width layer with a 32,768-token prefix (the long-context workload's
+# attention) and with 2,048 rows in one call (the batch workload's tokens per
+# step: ~128 rows per expert, several 128-row chunks for hot experts).
+@pytest.mark.parametrize("name,causal,P,C", [("tiny", False, None, None), ("tiny", True, None, None),
+                                             ("one_layer", False, None, None), ("one_layer", True, None, None),
+                                             ("one_layer", False, 32768, None),
+                                             ("one_layer", False, None, 2048)])
+def test_layer_parity(name, causal, P, C):
     wl = synth.WORKLOADS[name]
     cfg = dataclasses.replace(wl.model, n_layers=1)
-    P, C = wl.prefix, cfg.canvas
-    say(f"[layer] {name} causal={causal} P={P} C={C}")
-    eng, hw = make_engine(cfg, max_ctx=P + 2 * C)
+    P = P or wl.prefix
+    C = C or cfg.canvas
+    say(f"[layer] {name} causal={causal} P={P} rows={C}")
+    eng, hw = make_engine(cfg, max_ctx=P + 2 * C, max_rows=C)
     _fill_prefix(eng, cfg, P)
     h = synth.make_hidden(C, cfg.d_model, 21)
     h_dev = h.cuda()
