@@ -226,6 +226,26 @@ def main():
     traffic = round(traffic) if traffic is not None else None
     ex_launch_ms = stages["experts"][0] / max(1, stages["experts"][1])
     achieved = b_ex / (ex_launch_ms * 1e-3)
+    # every kernel class against its own roof: algorithmic bytes and flops per
+    # launch over the launch's measured duration
+    kinds_staged = dict(algorithmic_model(cfg, P, rows, touched_staged)[0])
+    kinds_staged["lmhead"] = per_step["lmhead"]
+    kernels = {}
+    for name, (b, f) in kinds_staged.items():
+        if name not in stages or not stages[name][1]:
+            continue
+        t = stages[name][0] / stages[name][1] * 1e-3
+        hbm = b / HBM_PEAK >= f / MFMA_BF16_PEAK
+        kernels[name] = {"bound": "hbm" if hbm else "mfma",
+                         "achieved": round((b / t / 1e9) if hbm else (f / t / 1e12), 1),
+                         "unit": "GB/s" if hbm else "TFLOP/s",
+                         "peak": HBM_PEAK / 1e9 if hbm else MFMA_BF16_PEAK / 1e12,
+                         "frac": round(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) / t, 4),
+                         "bytes_per_launch": round(b), "flops_per_launch": round(f),
+                         "avg_launch_ms": round(t * 1e3, 4)}
+    lm_traffic = traffic_for("lmhead", f"lmhead_{wl.name}_traffic")
+    if "lmhead" in kernels:
+        kernels["lmhead"]["traffic"] = round(lm_traffic) if lm_traffic is not None else None
     steps_per_s = 1e3 / ms
     out = {
         "metric": METRIC,
@@ -254,6 +274,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
                      "bytes_per_launch": round(b_ex), "avg_launch_ms": round(ex_launch_ms, 4),
                      "traffic": traffic},
+        "kernel_rooflines": kernels,
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,
         "commit_ms": round(commit_ms, 3),
