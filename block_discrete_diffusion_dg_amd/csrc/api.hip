@@ -18,6 +18,10 @@ static_assert(MOE_SPIN_TIMEOUTS == DG_ITEMS_SPIN_TIMEOUTS && MOE_TOUCHED_TOTAL =
 
 namespace {
 
+// Arrival counters of the router: one per 16-row block, plus one for the
+// permutation run by the last block to finish.
+int router_sync_words(int max_rows) { return div_up(max_rows, 16) + 1; }
+
 struct LayerW {
   const bf16_t *attn_norm, *w_qkv, *w_o, *moe_norm, *w_router;
   const bf16_t *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
@@ -62,7 +66,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.ids = take(R * 4);
   L.ss = take(R * (d / 64) * 4);
   L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
-  L.sync = take((256 + groups) * 4);  // router row blocks, then attention groups
+  L.sync = take((router_sync_words(c.max_rows) + groups) * 4);  // router row blocks, then attention groups
   L.total = o;
   return L;
 }
@@ -180,6 +184,14 @@ namespace {
 // the layer's attention pre-norm of h; on exit (unless kv_only) h is updated
 // and, when next_gain is given, u holds RMSNorm(h) * next_gain for whatever
 // consumes the rows next (the following layer or the LM head).
+RouterPermute permute_outputs(dg_ctx* c, int rows) {
+  const dg_config& g = c->cfg;
+  const dg_ws_layout& L = c->lay;
+  return RouterPermute{moe_rows_per_chunk(rows, g.n_experts, g.top_k), g.d_expert / 64, g.d_shared / 64,
+                       g.d_model / 128, c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<int32_t>(L.perm),
+                       c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), c->buf<int32_t>(L.items)};
+}
+
 void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, bool kv_only,
                const bf16_t* next_gain) {
   const dg_config& g = c->cfg;
@@ -190,26 +202,23 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   float* h = c->buf<float>(L.h);
   bf16_t* u = c->buf<bf16_t>(L.u);
 
+  const int rsync = router_sync_words(g.max_rows);
   STAGE(DG_STAGE_QKV, launch_qkv(s, u, rows, d, w.w_qkv, c->buf<bf16_t>(L.q), c->kv, l, g.n_q_heads,
                                  g.n_kv_heads, g.head_dim, c->buf<float2>(L.rope), rt, c->buf<int32_t>(L.sync),
-                                 256 + attn_groups_bound(g.max_rows, g.n_q_heads, g.n_kv_heads)));
+                                 rsync + attn_groups_bound(g.max_rows, g.n_q_heads, g.n_kv_heads)));
   if (kv_only) return;
   const int ns = attn_splits(rt, g.n_q_heads, g.n_kv_heads, g.max_rows);
   STAGE(DG_STAGE_ATTN, launch_attention(s, c->buf<bf16_t>(L.q), c->kv, l, rt, g.n_q_heads, g.n_kv_heads,
                                        g.head_dim, causal, ns, c->buf<float>(L.attn_part),
-                                       c->buf<float2>(L.attn_ml), c->buf<int32_t>(L.sync) + 256,
+                                       c->buf<float2>(L.attn_ml), c->buf<int32_t>(L.sync) + rsync,
                                        c->buf<bf16_t>(L.attn_o)));
   STAGE(DG_STAGE_OPROJ, launch_resid(s, c->buf<bf16_t>(L.attn_o), rows, g.n_q_heads * g.head_dim, w.w_o, d, h,
                                      c->buf<float>(L.ss)));
+  int32_t* items = c->buf<int32_t>(L.items);
+  const RouterPermute rp = permute_outputs(c, rows);
   STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,
                                        g.n_experts, g.top_k, u, c->buf<float>(L.z), c->buf<float>(L.zpart),
-                                       c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w)));
-  int32_t* items = c->buf<int32_t>(L.items);
-  const int ch = moe_rows_per_chunk(rows, g.n_experts, g.top_k);
-  STAGE(DG_STAGE_PERMUTE, launch_permute(s, c->buf<int32_t>(L.idx), rows, g.n_experts, g.top_k, ch,
-                                         g.d_expert / 64, g.d_shared / 64, d / 128, c->buf<int32_t>(L.cnt),
-                                         c->buf<int32_t>(L.off), c->buf<int32_t>(L.perm),
-                                         c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot), items));
+                                       c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w), &rp));
   float* y = c->buf<float>(L.y);
   float* ys = y + (size_t)g.max_rows * g.top_k * d;
   STAGE(DG_STAGE_EXPERTS,
@@ -509,10 +518,7 @@ dg_status dg_test_route(dg_ctx* c, void* stream, const float* d_z, int32_t rows,
   const dg_ws_layout& L = c->lay;
   const int E = g.n_experts, k = g.top_k;
   launch_topk(s, d_z, rows, E, k, c->buf<int32_t>(L.idx), c->buf<float>(L.w));
-  launch_permute(s, c->buf<int32_t>(L.idx), rows, E, k, moe_rows_per_chunk(rows, E, k), g.d_expert / 64,
-                 g.d_shared / 64, g.d_model / 128, c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off),
-                 c->buf<int32_t>(L.perm), c->buf<int32_t>(L.slot), c->buf<int32_t>(L.wslot),
-                 c->buf<int32_t>(L.items));
+  launch_permute(s, c->buf<int32_t>(L.idx), rows, E, k, permute_outputs(c, rows));
   auto cp = [&](void* dst, size_t off, size_t bytes) {
     if (dst) (void)hipMemcpyAsync(dst, c->ws + off, bytes, hipMemcpyDeviceToDevice, s);
   };

@@ -4,6 +4,8 @@
 // wave-level prefix sum.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -22,8 +24,10 @@ namespace {
 // zl: LDS tile [16][E + 1]; rows at or past `rows` are skipped.
 constexpr int RB = 16;  // rows per block
 
+// With `coherent`, the expert ids are stored at agent scope (written through
+// to memory), for a reader on another XCD within the same launch.
 __device__ __forceinline__ void block_topk16(const float* zl, int E, int k, int t0, int rows, int32_t* __restrict__ idx,
-                             float* __restrict__ w) {
+                             float* __restrict__ w, bool coherent = false) {
   const int tid = threadIdx.x, r = tid >> 4, l16 = tid & 15;
   const float* zr = zl + r * (E + 1);
   float v[8];
@@ -73,7 +77,10 @@ __device__ __forceinline__ void block_topk16(const float* zl, int E, int k, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= k) break;
-      idx[(int64_t)t * k + j] = sid[j];
+      if (coherent)
+        __hip_atomic_store(idx + (int64_t)t * k + j, sid[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        idx[(int64_t)t * k + j] = sid[j];
       w[(int64_t)t * k + j] = ex[j] / sum;
     }
   }
@@ -90,6 +97,157 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
   }
   __syncthreads();
   block_topk16(zl, E, k, t0, rows, idx, w);
+}
+
+// Exclusive prefix sum of n <= 320 ints by one wave (5 consecutive per lane);
+// out[n] receives the total.
+__device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int lane) {
+  int local[5], acc = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = lane * 5 + i;
+    local[i] = e < n ? in[e] : 0;
+    acc += local[i];
+  }
+  int inc = acc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, WAVE);
+    if (lane >= o) inc += y;
+  }
+  int run = inc - acc;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int e = lane * 5 + i;
+    if (e < n) out[e] = run;
+    run += local[i];
+  }
+  if (lane == 63) out[n] = inc;
+}
+
+// Token -> expert permutation and the expert kernel's work list, by one
+// work-group of any size that is a multiple of 256 threads (at least 4
+// waves); nb = ceil(rows / 64) token blocks (nb <= 64):
+//  1. mask[e][b] = bit set of the tokens of block b that chose expert e
+//     (64-bit LDS atomic OR per (token, choice) pair);
+//  2. one thread per expert: popcounts of its masks, running sum over the
+//     blocks -> cnt[e] and the tokens of e in earlier blocks;
+//  3. off = exclusive prefix sum of cnt; base[e][b] = off[e] + earlier
+//     tokens; the work list of the expert kernel (groups: 0 = shared expert,
+//     1 + e = routed e) as exclusive item and row-chunk offsets;
+//  4. every pair (t, j) with expert e = idx[t][j] takes slot
+//     base[e][t/64] + popcount(mask[e][t/64] below t): tokens ascending
+//     inside an expert, three stores per pair (slot[t][j] coalesced).
+// With `coherent`, idx is read at agent scope (it was written in the same
+// launch, possibly on another XCD). lds: permute_lds_bytes(rows, E, k).
+struct PermuteArgs {
+  const int32_t* idx;
+  int rows, E, k, ch, ft_routed, ft_shared, dt;
+  int32_t *cnt, *off, *perm, *slot, *widx, *items;
+};
+
+__device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, bool coherent) {
+  const int rows = a.rows, E = a.E, k = a.k;
+  const int nb = (rows + 63) / 64;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(lds);  // [E][nb]
+  int32_t* base = reinterpret_cast<int32_t*>(mask + (size_t)E * nb);     // [E][nb]
+  __shared__ int32_t s_cnt[257];
+  __shared__ int32_t s_off[258];
+  __shared__ int32_t s_ngu[MOE_MAX_GROUPS], s_ndn[MOE_MAX_GROUPS], s_nch[MOE_MAX_GROUPS];
+  __shared__ int32_t s_igu[MOE_MAX_GROUPS + 1], s_idn[MOE_MAX_GROUPS + 1], s_ich[MOE_MAX_GROUPS + 1];
+  const int nt = blockDim.x, nw = nt >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int pairs = rows * k;
+  auto load_idx = [&](int i) {
+    return i >= pairs ? 0
+                      : coherent ? __hip_atomic_load(a.idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : a.idx[i];
+  };
+  // expert ids are loaded PB per thread at a time, all issued before any use
+  constexpr int PB = 8;
+  for (int i = tid; i < E * nb; i += nt) mask[i] = 0ull;
+  __syncthreads();
+  for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
+    int ev[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int i = i0 + j * nt, t = i / k;
+      if (i < pairs) atomicOr(&mask[ev[j] * nb + (t >> 6)], 1ull << (t & 63));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {  // one thread per expert, over its nb masks
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      base[e * nb + b] = run;  // tokens of e in earlier blocks
+      run += __popcll(mask[e * nb + b]);
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  // groups: 0 = shared expert (all rows), 1 + e = routed expert e
+  for (int g = tid; g <= E; g += nt) {
+    const int n = g == 0 ? rows : s_cnt[g - 1];
+    const int nmc = (n + a.ch - 1) / a.ch;
+    s_nch[g] = nmc;
+    s_ngu[g] = nmc * (g == 0 ? a.ft_shared : a.ft_routed);
+    s_ndn[g] = nmc * a.dt;
+  }
+  __syncthreads();
+  if (wave == 0) wave_exclusive_scan(s_cnt, s_off, E, lane);
+  if (wave == 1) wave_exclusive_scan(s_ngu, s_igu, E + 1, lane);
+  if (wave == 2) wave_exclusive_scan(s_ndn, s_idn, E + 1, lane);
+  if (wave == 3) wave_exclusive_scan(s_nch, s_ich, E + 1, lane);
+  __syncthreads();
+  for (int i = tid; i < E * nb; i += nt) base[i] += s_off[i / nb];
+  for (int e = tid; e < E; e += nt) {
+    a.cnt[e] = s_cnt[e];
+    a.off[e] = s_off[e];
+  }
+  if (tid == 0) {
+    a.off[E] = s_off[E];
+    a.items[MOE_QUEUE] = 0;
+  }
+  if (wave == 4 % nw) {  // running statistics: experts touched per call
+    int touched = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) touched += __popcll(__ballot(e0 + lane < E && s_cnt[e0 + lane] > 0));
+    if (lane == 0) {
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.items + MOE_TOUCHED_TOTAL), (unsigned long long)touched);
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.items + MOE_PERMUTE_CALLS), 1ull);
+    }
+  }
+  for (int g = tid; g <= E + 1; g += nt) {
+    a.items[MOE_ITEMS_GU + g] = s_igu[g];
+    a.items[MOE_ITEMS_DN + g] = s_idn[g];
+    a.items[MOE_CHUNKS + g] = s_ich[g];
+  }
+  for (int c = tid; c < s_ich[E + 1]; c += nt) a.items[MOE_DONE + c] = 0;
+  __syncthreads();  // base is final
+  for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
+    int ev[PB];
+#pragma unroll
+    for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      const int i = i0 + j * nt;
+      if (i >= pairs) break;
+      const int t = i / k, e = ev[j], b = t >> 6, l = t & 63;
+      const unsigned long long below = l == 0 ? 0ull : (mask[e * nb + b] << (64 - l));
+      const int pos = base[e * nb + b] + __popcll(below);
+      a.slot[i] = pos;
+      a.perm[pos] = t;
+      a.widx[pos] = i;
+    }
+  }
+}
+
+// The permutation as a launch of its own (1024 threads), from top-k results
+// of an earlier launch.
+__global__ __launch_bounds__(1024) void permute_kernel(PermuteArgs a) {
+  extern __shared__ __align__(8) char pm_lds[];
+  permute_block(a, pm_lds, false);
 }
 
 // MoE pre-norm, router logits and top-k. Work-group (row block rb of RB = 16
@@ -116,7 +274,8 @@ __device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
 __global__ __launch_bounds__(256) void router_kernel(
     const float* __restrict__ h, const float* __restrict__ ss, const bf16_t* __restrict__ gain, int rows, int d,
     float eps, const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
-    float* __restrict__ zpart, int32_t* __restrict__ sync, int32_t* __restrict__ idx, float* __restrict__ w) {
+    float* __restrict__ zpart, int32_t* __restrict__ sync, int32_t* __restrict__ idx, float* __restrict__ w,
+    PermuteArgs pa, int do_permute) {
   extern __shared__ __align__(16) char rt_lds[];
   const int kq = d / RKS, LDA = kq + 8, nct = d / 64;
   bf16_t* As = reinterpret_cast<bf16_t*>(rt_lds);                    // [RB][LDA]
@@ -253,130 +412,23 @@ __global__ __launch_bounds__(256) void router_kernel(
     zt[r * (E + 1) + e] = v;
   }
   __syncthreads();
-  block_topk16(zt, E, k, t0, rows, idx, w);
-}
+  block_topk16(zt, E, k, t0, rows, idx, w, do_permute != 0);
+  if (!do_permute) return;
 
-// Exclusive prefix sum of n <= 320 ints by one wave (5 consecutive per lane);
-// out[n] receives the total.
-__device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* out, int n, int lane) {
-  int local[5], acc = 0;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int e = lane * 5 + i;
-    local[i] = e < n ? in[e] : 0;
-    acc += local[i];
-  }
-  int inc = acc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o, WAVE);
-    if (lane >= o) inc += y;
-  }
-  int run = inc - acc;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int e = lane * 5 + i;
-    if (e < n) out[e] = run;
-    run += local[i];
-  }
-  if (lane == 63) out[n] = inc;
-}
-
-// Single work-group of 1024 threads (16 waves); nb = ceil(rows / 64) token
-// blocks (nb <= 64).
-//  1. mask[e][b] = bit set of the tokens of block b that chose expert e
-//     (64-bit LDS atomic OR per (token, choice) pair);
-//  2. one wave per expert: popcounts of its masks, prefix over the blocks ->
-//     cnt[e] and the tokens of e in earlier blocks;
-//  3. off = exclusive prefix sum of cnt; base[e][b] = off[e] + earlier
-//     tokens; the work list of the expert kernel (groups: 0 = shared expert,
-//     1 + e = routed e) as exclusive item and row-chunk offsets;
-//  4. every pair (t, j) with expert e = idx[t][j] takes slot
-//     base[e][t/64] + popcount(mask[e][t/64] below t): tokens ascending
-//     inside an expert, three stores per pair (slot[t][j] coalesced).
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int rows, int E,
-                                                       int k, int ch, int ft_routed, int ft_shared,
-                                                       int dt, int32_t* __restrict__ cnt,
-                                                       int32_t* __restrict__ off,
-                                                       int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ slot,
-                                                       int32_t* __restrict__ widx,
-                                                       int32_t* __restrict__ items) {
-  extern __shared__ __align__(8) char pm_lds[];
-  const int nb = (rows + 63) / 64;
-  unsigned long long* mask = reinterpret_cast<unsigned long long*>(pm_lds);  // [E][nb]
-  int32_t* base = reinterpret_cast<int32_t*>(mask + (size_t)E * nb);       // [E][nb]
-  __shared__ int32_t s_cnt[257];
-  __shared__ int32_t s_off[258];
-  __shared__ int32_t s_ngu[MOE_MAX_GROUPS], s_ndn[MOE_MAX_GROUPS], s_nch[MOE_MAX_GROUPS];
-  __shared__ int32_t s_igu[MOE_MAX_GROUPS + 1], s_idn[MOE_MAX_GROUPS + 1], s_ich[MOE_MAX_GROUPS + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int pairs = rows * k;
-  for (int i = tid; i < E * nb; i += 1024) mask[i] = 0ull;
+  // 6. the last row block to finish runs the permutation over all rows: its
+  // expert ids were written through to memory and waited for before the
+  // block counted itself in, and the permutation reads them at agent scope
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int i = tid; i < pairs; i += 1024) {
-    const int t = i / k, e = idx[i];
-    atomicOr(&mask[e * nb + (t >> 6)], 1ull << (t & 63));
-  }
-  __syncthreads();
-  for (int e = wave; e < E; e += 16) {
-    const int c = lane < nb ? __popcll(mask[e * nb + lane]) : 0;
-    int inc = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o, WAVE);
-      if (lane >= o) inc += y;
-    }
-    if (lane < nb) base[e * nb + lane] = inc - c;  // tokens of e in earlier blocks
-    if (lane == 63) s_cnt[e] = inc;
-  }
-  __syncthreads();
-  // groups: 0 = shared expert (all rows), 1 + e = routed expert e
-  for (int g = tid; g <= E; g += 1024) {
-    const int n = g == 0 ? rows : s_cnt[g - 1];
-    const int nmc = (n + ch - 1) / ch;
-    s_nch[g] = nmc;
-    s_ngu[g] = nmc * (g == 0 ? ft_shared : ft_routed);
-    s_ndn[g] = nmc * dt;
-  }
-  __syncthreads();
-  if (wave == 0) wave_exclusive_scan(s_cnt, s_off, E, lane);
-  if (wave == 1) wave_exclusive_scan(s_ngu, s_igu, E + 1, lane);
-  if (wave == 2) wave_exclusive_scan(s_ndn, s_idn, E + 1, lane);
-  if (wave == 3) wave_exclusive_scan(s_nch, s_ich, E + 1, lane);
-  __syncthreads();
-  for (int i = tid; i < E * nb; i += 1024) base[i] += s_off[i / nb];
-  for (int e = tid; e < E; e += 1024) {
-    cnt[e] = s_cnt[e];
-    off[e] = s_off[e];
-  }
+  const int nrb = div_up(rows, RB);
   if (tid == 0) {
-    off[E] = s_off[E];
-    items[MOE_QUEUE] = 0;
+    const int prev = __hip_atomic_fetch_add(sync + nrb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == nrb - 1;
+    if (s_last) __hip_atomic_store(sync + nrb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (wave == 4) {  // running statistics: experts touched per call
-    int touched = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) touched += __popcll(__ballot(e0 + lane < E && s_cnt[e0 + lane] > 0));
-    if (lane == 0) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(items + MOE_TOUCHED_TOTAL), (unsigned long long)touched);
-      atomicAdd(reinterpret_cast<unsigned long long*>(items + MOE_PERMUTE_CALLS), 1ull);
-    }
-  }
-  for (int g = tid; g <= E + 1; g += 1024) {
-    items[MOE_ITEMS_GU + g] = s_igu[g];
-    items[MOE_ITEMS_DN + g] = s_idn[g];
-    items[MOE_CHUNKS + g] = s_ich[g];
-  }
-  for (int c = tid; c < s_ich[E + 1]; c += 1024) items[MOE_DONE + c] = 0;
-  __syncthreads();  // base is final
-  for (int i = tid; i < pairs; i += 1024) {
-    const int t = i / k, e = idx[i], b = t >> 6, l = t & 63;
-    const unsigned long long below = l == 0 ? 0ull : (mask[e * nb + b] << (64 - l));
-    const int pos = base[e * nb + b] + __popcll(below);
-    slot[i] = pos;
-    perm[pos] = t;
-    widx[pos] = i;
-  }
+  __syncthreads();
+  if (!s_last) return;
+  permute_block(pa, rt_lds, true);
 }
 
 }  // namespace
@@ -387,19 +439,24 @@ void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t*
 
 void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
                    const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
-                   float* w) {
+                   float* w, const RouterPermute* perm) {
   const int kq = d / RKS;
-  const size_t lds = (size_t)RB * (kq + 8) * 2 + (size_t)RB * (E + 1) * 4 + (size_t)RB * (d / 64) * 4;
+  size_t lds = (size_t)RB * (kq + 8) * 2 + (size_t)RB * (E + 1) * 4 + (size_t)RB * (d / 64) * 4;
+  PermuteArgs pa{idx, rows, E, k, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (perm) {
+    pa = PermuteArgs{idx, rows, E, k, perm->ch, perm->ft_routed, perm->ft_shared, perm->dt, perm->cnt, perm->off,
+                     perm->perm, perm->slot, perm->widx, perm->items};
+    lds = std::max(lds, permute_lds_bytes(rows, E, k));
+  }
   hipLaunchKernelGGL(router_kernel, dim3(div_up(rows, RB) * RKS), dim3(256), lds, s, h, ss, gain, rows, d, eps, wr,
-                     E, k, u, z, zpart, sync, idx, w);
+                     E, k, u, z, zpart, sync, idx, w, pa, perm ? 1 : 0);
 }
 
-void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
-                    int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
-                    int32_t* widx, int32_t* items) {
+void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, const RouterPermute& p) {
   const size_t lds = permute_lds_bytes(rows, E, k);
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, idx, rows, E, k, ch, ft_routed, ft_shared,
-                     dt, cnt, off, perm, slot, widx, items);
+  const PermuteArgs pa{idx, rows, E, k, p.ch, p.ft_routed, p.ft_shared, p.dt, p.cnt, p.off, p.perm, p.slot,
+                       p.widx, p.items};
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, pa);
 }
 
 // Dynamic LDS of the permutation kernel: mask (8 B) and base (4 B) per

@@ -47,12 +47,19 @@ void launch_attention(hipStream_t s, const bf16_t* q, const KvGeom& kv, int laye
 
 // k_route.hip
 void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t* idx, float* w);
+// Outputs of the token -> expert permutation and the expert kernel's work
+// list (see k_route.hip).
+struct RouterPermute {
+  int ch, ft_routed, ft_shared, dt;  // chunk rows; gate/up tiles (routed, shared); down tiles
+  int32_t *cnt, *off, *perm, *slot, *widx, *items;
+};
+// Router (MoE pre-norm, logits, top-k); with perm, the last row block to
+// finish also runs the permutation (sync needs div_up(rows, 16) + 1 words).
 void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
                    const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
-                   float* w);
-void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, int ch, int ft_routed,
-                    int ft_shared, int dt, int32_t* cnt, int32_t* off, int32_t* perm, int32_t* slot,
-                    int32_t* widx, int32_t* items);
+                   float* w, const RouterPermute* perm);
+// The permutation as a launch of its own, from expert ids of an earlier launch.
+void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, const RouterPermute& p);
 size_t permute_lds_bytes(int rows, int E, int k);
 
 // k_moe.hip
