@@ -252,9 +252,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(PermuteArgs a) {
 
 // MoE pre-norm, router logits and top-k. Work-group (row block rb of RB = 16
 // rows, K quarter ks) of a grid of ceil(rows/16) x 4:
-//  1. issues the loads of its router weight fragments (expert rows
-//     16*(2w+n) + l16 of wave w, clamped to E-1, over its quarter of d)
-//     before anything else: they depend on nothing;
+//  1. issues every load that depends on nothing at once, in order of use:
+//     the sums of squares of its rows, its quarter of the hidden-state rows
+//     and norm gains, and its router weight fragments (expert rows
+//     16*(2w+n) + l16 of wave w, clamped to E-1, over its quarter of d);
 //  2. 1/rms of its rows from the output projection's per-64-column sums of
 //     squares (summed in a fixed order);
 //  3. u = bf16(h / rms * gain) on its quarter of d -> workspace (the experts'
@@ -263,9 +264,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(PermuteArgs a) {
 //     device-coherent memory, then counts itself in for the row block;
 //  5. the last of the four to arrive adds the four partials in quarter
 //     order (deterministic whatever the arrival order), stores z, resets the
-//     counter, and selects each row's experts (block_topk16).
+//     counter, and selects each row's experts (block_topk16);
+//  6. (with the permutation) the last row block to finish runs it.
 constexpr int RKS = 4;     // K quarters
-constexpr int RSTEPS = 8;  // 32-wide K steps whose weights are loaded at once
+constexpr int RSTEPS = 16;  // 32-wide K steps whose weights are loaded at once (a quarter of d = 2048)
 
 __device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
@@ -290,7 +292,28 @@ __global__ __launch_bounds__(256) void router_kernel(
   // fill whole 128-byte lines (E % 8 == 0), shared with no other block
   const int zs = div_up(rows, RB) * RB;
 
-  // 1. weight fragments of the first RSTEPS steps
+  // 1. every load that depends on nothing is issued first, in the order of
+  // use (completion is in order): the output projection's sums of squares of
+  // the block's rows, its first batch of hidden-state values and norm gains,
+  // then the router weight fragments of the first RSTEPS steps
+  float sqv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 256 * j, r = i / nct, ct = i % nct, t = t0 + r;
+    sqv[j] = (i < RB * nct && t < rows) ? ss[(int64_t)ct * rows + t] : 0.f;
+  }
+  float4 hv[8];
+  u32x2 gv[8];
+  auto load_h = [&](int i0) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int i = i0 + b * 1024, r = i / kq, c = i % kq, t = min(t0 + r, rows - 1);
+      const bool ok = i < RB * kq;
+      hv[b] = *reinterpret_cast<const float4*>(h + (int64_t)t * d + kb + (ok ? c : 0));
+      gv[b] = *reinterpret_cast<const u32x2*>(gain + kb + (ok ? c : 0));
+    }
+  };
+  load_h(tid * 4);
   const bf16_t* brow[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) brow[n] = wr + (int64_t)min(16 * (2 * wave + n) + l16, E - 1) * d + kb + 8 * grp;
@@ -300,8 +323,11 @@ __global__ __launch_bounds__(256) void router_kernel(
 #pragma unroll
     for (int n = 0; n < 2; ++n) bf[st][n] = ld16(brow[n] + min(st, nk - 1) * 32);
 
-  // 2. 1/rms per row: all partial sums loaded at once, added in tile order
-  for (int i = tid; i < RB * nct; i += 256) {
+  // 2. 1/rms per row: the partial sums added in tile order
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (tid + 256 * j < RB * nct) sq[tid + 256 * j] = sqv[j];
+  for (int i = tid + 512; i < RB * nct; i += 256) {  // d > 2048: the remaining sums
     const int r = i / nct, ct = i % nct, t = t0 + r;
     sq[i] = t < rows ? ss[(int64_t)ct * rows + t] : 0.f;
   }
@@ -313,18 +339,10 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
   __syncthreads();
 
-  // 3. normalised rows on this quarter (rows past the end are zero); loads of
-  // a batch of up to 8 float4 per thread are all issued before any use
+  // 3. normalised rows on this quarter (rows past the end are zero), in
+  // batches of 8 float4 per thread (the first already loaded)
   for (int i0 = tid * 4; i0 < RB * kq; i0 += 8 * 1024) {
-    float4 hv[8];
-    u32x2 gv[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int i = i0 + b * 1024, r = i / kq, c = i % kq, t = min(t0 + r, rows - 1);
-      const bool ok = i < RB * kq;
-      hv[b] = *reinterpret_cast<const float4*>(h + (int64_t)t * d + kb + (ok ? c : 0));
-      gv[b] = *reinterpret_cast<const u32x2*>(gain + kb + (ok ? c : 0));
-    }
+    if (i0 != tid * 4) load_h(i0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const int i = i0 + b * 1024, r = i / kq, c = i % kq, t = t0 + r;
