@@ -81,12 +81,6 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
-}
-
 // Reductions over the 16 lanes of each DPP row (lanes 16j .. 16j+15) on
 // the DPP network, with no LDS round trip: butterflies inside each quad
 // (lane ^ 1, lane ^ 2), then the half-row mirror (lane i <-> 7 - i within 8)
@@ -121,9 +115,41 @@ __device__ __forceinline__ int row16_min(int v) {
   return min(v, dpp_mov<DPP_MIRROR>(v));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Combine the four rows (lanes l, l ^ 16, l ^ 32, l ^ 48) with the gfx950
+// row-swap instructions (VALU, no LDS round trip): with both operands the
+// same register, v_permlane32_swap leaves each lane holding its own value
+// and that of lane l ^ 32 (in some order), v_permlane16_swap the same for
+// l ^ 16. The operation must be commutative; every lane ends with the same
+// result.
+__device__ __forceinline__ float xrow_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return xrow_sum(row16_sum(v)); }
+__device__ __forceinline__ float wave_max(float v) { return xrow_max(row16_max(v)); }
+
+// Inclusive prefix sum over the wave on the DPP network: shifts by 1, 2, 4, 8
+// inside each 16-lane row (lanes shifted in from before the row start read
+// 0), then the last lane of row 0 / row 2 is added to row 1 / row 3 and the
+// last lane of row 1 to rows 2 and 3.
+constexpr int DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118, DPP_BCAST15 = 0x142,
+              DPP_BCAST31 = 0x143;
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_SHR1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_SHR2, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_SHR4, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_SHR8, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_BCAST15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, DPP_BCAST31, 0xc, 0xf, false);
   return v;
 }
 

@@ -204,8 +204,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
                          fmaxf(fmaxf(s[j][1][0], s[j][1][1]), fmaxf(s[j][1][2], s[j][1][3])));
       tmax = fmaxf(tmax, fmaxf(fmaxf(fmaxf(s[j][2][0], s[j][2][1]), fmaxf(s[j][2][2], s[j][2][3])),
                                fmaxf(fmaxf(s[j][3][0], s[j][3][1]), fmaxf(s[j][3][2], s[j][3][3]))));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
+      tmax = xrow_max(tmax);  // the other key groups of the query
       // running maximum in the scaled log2 domain (scale > 0 keeps the order)
       const float m_new = fmaxf(m_run[j], tmax * scale_log2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;

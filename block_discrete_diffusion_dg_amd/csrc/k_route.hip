@@ -50,15 +50,18 @@ __device__ __forceinline__ void block_topk16(const float* zl, int E, int k, int 
         bv = v[m];
         bi = l16 + 16 * m;
       }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 16);
-      const int oi = __shfl_xor(bi, o, 16);
+    // across the 16 lanes of the row on the DPP network; the merge is a
+    // maximum under a total order, so every lane ends with the row's winner
+    auto merge = [&](float ov, int oi) {
       if (ov > bv || (ov == bv && oi < bi)) {
         bv = ov;
         bi = oi;
       }
-    }
+    };
+    merge(dpp_movf<DPP_XOR1>(bv), dpp_mov<DPP_XOR1>(bi));
+    merge(dpp_movf<DPP_XOR2>(bv), dpp_mov<DPP_XOR2>(bi));
+    merge(dpp_movf<DPP_HALF_MIRROR>(bv), dpp_mov<DPP_HALF_MIRROR>(bi));
+    merge(dpp_movf<DPP_MIRROR>(bv), dpp_mov<DPP_MIRROR>(bi));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
       if (bi == l16 + 16 * m) v[m] = -INFINITY;
@@ -109,12 +112,7 @@ __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* 
     local[i] = e < n ? in[e] : 0;
     acc += local[i];
   }
-  int inc = acc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o, WAVE);
-    if (lane >= o) inc += y;
-  }
+  const int inc = wave_inclusive_scan(acc);
   int run = inc - acc;
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
