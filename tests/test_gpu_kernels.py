@@ -198,20 +198,25 @@ def _cache_rows(eng, slot, layer, lo, hi):
     return k.permute(1, 0, 2).contiguous().cpu(), v.permute(1, 0, 2).contiguous().cpu()
 
 
-# (workload, causal, prefix, rows): the workloads' own layer shapes, plus the
-# full-width layer with a 32,768-token prefix (the long-context workload's
-# attention) and with 2,048 rows in one call (the batch workload's tokens per
-# step: ~128 rows per expert, several 128-row chunks for hot experts).
-@pytest.mark.parametrize("name,causal,P,C", [("tiny", False, None, None), ("tiny", True, None, None),
-                                             ("one_layer", False, None, None), ("one_layer", True, None, None),
-                                             ("one_layer", False, 32768, None),
-                                             ("one_layer", False, None, 2048)])
-def test_layer_parity(name, causal, P, C):
+# (workload, causal, prefix, rows, model overrides): the workloads' own layer
+# shapes, plus the full-width layer with a 32,768-token prefix (the
+# long-context workload's attention) and with 2,048 rows in one call (the
+# batch workload's tokens per step: ~128 rows per expert, several 128-row
+# chunks for hot experts), and a small layer whose projection widths (K = 768
+# and 384) are not a power-of-two multiple of 256, so the dense projections
+# take their streaming-tile form instead of the split-K form.
+@pytest.mark.parametrize("name,causal,P,C,over", [("tiny", False, None, None, None), ("tiny", True, None, None, None),
+                                                  ("one_layer", False, None, None, None),
+                                                  ("one_layer", True, None, None, None),
+                                                  ("one_layer", False, 32768, None, None),
+                                                  ("one_layer", False, None, 2048, None),
+                                                  ("tiny", False, None, None, {"d_model": 768, "n_q_heads": 6})])
+def test_layer_parity(name, causal, P, C, over):
     wl = synth.WORKLOADS[name]
-    cfg = dataclasses.replace(wl.model, n_layers=1)
+    cfg = dataclasses.replace(wl.model, n_layers=1, **(over or {}))
     P = P or wl.prefix
     C = C or cfg.canvas
-    say(f"[layer] {name} causal={causal} P={P} rows={C}")
+    say(f"[layer] {name} {over or ''} causal={causal} P={P} rows={C}")
     eng, hw = make_engine(cfg, max_ctx=P + 2 * C, max_rows=C)
     _fill_prefix(eng, cfg, P)
     h = synth.make_hidden(C, cfg.d_model, 21)
