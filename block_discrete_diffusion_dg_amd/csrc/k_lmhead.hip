@@ -5,98 +5,184 @@
 // materialised (the statistics the confidence sampler needs: codemajin.net
 // DiffusionGemma explainer §3.3).
 //
-// A work-group covers CH = 16*MT token rows by 256 vocabulary columns on the
-// weight-streaming tile: wave w owns columns 64w .. 64w+63 as four 16-row
-// blocks of the packed embedding, streamed from HBM into registers, so each
-// A fragment read from LDS feeds four matrix-core products. The row chunks
-// of one column tile get work-group ids 8 apart (same XCD): the embedding is
-// read from HBM once and re-read by the other chunks from L2.
+// A work-group of 512 threads covers 256 token rows x 256 vocabulary
+// columns. K advances in 32-wide steps; each step's operands are 32
+// fragments of 1 KB (16 token-row blocks, 16 vocabulary blocks), copied
+// global -> LDS by the load-to-LDS DMA path into a ring of four distinct LDS
+// buffers, three steps ahead of their use. Wave w computes token rows
+// 128(w/4) .. +127 against columns 64(w%4) .. +63, reading both operands from
+// LDS, so each operand byte is fetched into the compute unit once per tile.
+// Why this shape: the launch is bound by how many bytes each compute unit
+// keeps in flight (about 2.5 us of load latency at full load), and the ring
+// holds 96 KB in flight per compute unit while the 256 x 256 tile halves the
+// bytes per product of a 128-row tile. (The load-to-LDS path addresses the
+// first 128 KB of LDS only: a fifth buffer placed above that corrupts the
+// first one.) Tiles of one column range get work-group ids 8 apart (same XCD)
+// when there are several row chunks.
 #include "common.h"
 #include "kernels.h"
-#include "stream.h"
 
 namespace {
 
-constexpr int LM_NB = 4;                 // 16-column weight blocks per wave
-constexpr int LM_COLS = 4 * 16 * LM_NB;  // columns per work-group
+constexpr int LM_ROWS = 256, LM_COLS = 256, LM_BK = 32;
+constexpr int LM_FRAGS = LM_ROWS / 16 + LM_COLS / 16;  // 1 KB fragments per step
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // part[row][nt] = (max, sum exp2((L - max) * k2), first argmax bits, 0) over
 // the 256 columns of tile nt, k2 = log2(e) / tau; the lane holding the column
 // of the row's held token writes that logit to held_logit[row * held_stride].
-// Requires K % 64 == 0 and V % 256 == 0 (the configuration check enforces both).
-template <int MT>
-__global__ __launch_bounds__(256) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
+// Requires K % 128 == 0 and V % 256 == 0 (the configuration check enforces
+// d % 256 == 0 and V % 256 == 0).
+__global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
                                                      const bf16_t* __restrict__ E, int V,
                                                      const int32_t* __restrict__ held, float k2,
                                                      float4* __restrict__ part, float* __restrict__ held_logit,
                                                      int held_stride) {
-  using T = StreamTile<MT>;
-  constexpr int CH = T::CH;
-  __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
-  __shared__ float4 red[4][CH];
-  __shared__ int s_held[CH];
-
-  const int NT = V / LM_COLS, MC = div_up(rows, CH);
+  // four distinct objects: the compiler then orders each buffer's LDS reads
+  // only after the copies into that buffer
+  __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r1[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r2[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r3[LM_FRAGS][64];
+  const int NT = V / LM_COLS, MC = div_up(rows, LM_ROWS);
   int nt, mc;
   xcd_tile_coords(NT, MC, nt, mc);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int row0 = mc * CH, nrows = min(CH, rows - row0);
-  const int c0 = nt * LM_COLS + wave * 64;  // the wave's first column
-  if (tid < CH) s_held[tid] = tid < nrows ? held[row0 + tid] : -1;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave >> 2, cq = wave & 3;  // the wave's row half and column quarter
+  const int row0 = mc * LM_ROWS, nrows = min(LM_ROWS, rows - row0);
+  const int c0 = nt * LM_COLS;
 
-  const bf16_t* const wblk = E + (int64_t)(c0 / 16) * 16 * K;
-  const bf16_t* const w[LM_NB] = {wblk, wblk + 16 * K, wblk + 32 * K, wblk + 48 * K};
-  f32x4 acc[LM_NB][MT];
-  stream_tile_n<MT, LM_NB>(A, K, nullptr, row0, nrows, w, K, acc, lds);
-
-  // Per row (16mt + 4grp + r of the chunk), over the wave's 64 columns
-  // (16nb + l16): max, the smallest column holding it, and sum exp2((L - max) k2).
-  // All rows are reduced first (independent chains on the DPP network), then
-  // the held-token logits are picked out.
-  float m[MT][4];
+  // Fragments of a step: token-row block b at b (lane (g, i) holds row 16b + i,
+  // reduction indices 8g .. 8g+7 of the step; rows past the end repeat the
+  // last row), vocabulary block b at 16 + b (the packed embedding's 512
+  // contiguous elements of that block and step). Wave w copies token-row
+  // blocks w, w + 8 and vocabulary blocks w, w + 8.
+  const bf16_t* const srcA0 = A + (int64_t)(row0 + min(16 * wave + l16, nrows - 1)) * K + 8 * grp;
+  const bf16_t* const srcA1 = A + (int64_t)(row0 + min(16 * (wave + 8) + l16, nrows - 1)) * K + 8 * grp;
+  const bf16_t* const srcW0 = E + (int64_t)(c0 + 16 * wave) * K + lane * 8;
+  const bf16_t* const srcW1 = E + (int64_t)(c0 + 16 * (wave + 8)) * K + lane * 8;
+  const int nst = K / LM_BK;
+  // steps past the end reload the last step (in bounds; never used), so every
+  // step issues the same four copies and the wait counts stay static
+  auto copy = [&](u32x4 (&buf)[LM_FRAGS][64], int st) {
+    st = min(st, nst - 1);
+    const bf16_t* pa0 = srcA0 + st * LM_BK;
+    const bf16_t* pa1 = srcA1 + st * LM_BK;
+    const int64_t wo = (int64_t)(st >> 1) * 1024 + (st & 1) * 512;
+    const bf16_t* pw0 = srcW0 + wo;
+    const bf16_t* pw1 = srcW1 + wo;
+    __builtin_amdgcn_global_load_lds(pa0, (__attribute__((address_space(3))) void*)&buf[wave][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pa1, (__attribute__((address_space(3))) void*)&buf[wave + 8][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pw0, (__attribute__((address_space(3))) void*)&buf[16 + wave][0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(pw1, (__attribute__((address_space(3))) void*)&buf[24 + wave][0], 16, 0, 0);
+  };
+  f32x4 acc[4][8];  // [column block][row block] of the wave
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&buf)[LM_FRAGS][64]) {
+    u32x4 wf[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) wf[nb] = buf[16 + 4 * cq + nb][lane];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const u32x4 af = buf[8 * rh + mt][lane];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb][mt] = mfma_bf16(af, wf[nb], acc[nb][mt]);
+    }
+  };
+  // Step st: wait until this wave's copies of step st have landed (the two
+  // later steps may still be in flight), then a barrier without a memory
+  // fence (a fence would wait for every copy in flight): after it, every
+  // wave's copies of step st are in place and every wave has finished step
+  // st - 1, whose buffer the next copy reuses.
+  auto sync = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  copy(r0, 0);
+  copy(r1, 1);
+  copy(r2, 2);
+  for (int st = 0; st < nst; st += 4) {
+    sync();
+    copy(r3, st + 3);
+    compute(r0);
+    sync();
+    copy(r0, st + 4);
+    compute(r1);
+    sync();
+    copy(r1, st + 5);
+    compute(r2);
+    sync();
+    copy(r2, st + 6);
+    compute(r3);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Epilogue in the ring's memory: red[4][256] (max, sum, argmax) per column
+  // quarter and row, and the rows' held tokens.
+  float4* red = reinterpret_cast<float4*>(&r0[0][0]);
+  int* s_held = reinterpret_cast<int*>(&r1[0][0]);
+  if (tid < LM_ROWS) s_held[tid] = tid < nrows ? held[row0 + tid] : -1;
+  // Per row (128rh + 16mt + 4grp + r), over the wave's 64 columns
+  // (cw + 16nb + l16): max, the smallest column holding it, and
+  // sum exp2((L - max) k2), on the DPP network. All rows are reduced first
+  // (independent chains), then the held-token logits are picked out.
+  const int cw = c0 + 64 * cq;
+  float m[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       m[mt][r] = row16_max(fmaxf(fmaxf(acc[0][mt][r], acc[1][mt][r]), fmaxf(acc[2][mt][r], acc[3][mt][r])));
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int ix = 0x7fffffff;
       float z = 0.f;
 #pragma unroll
-      for (int nb = LM_NB - 1; nb >= 0; --nb) {
+      for (int nb = 3; nb >= 0; --nb) {
         const float v = acc[nb][mt][r];
-        if (v == m[mt][r]) ix = c0 + 16 * nb + l16;
+        if (v == m[mt][r]) ix = cw + 16 * nb + l16;
         z += __builtin_amdgcn_exp2f((v - m[mt][r]) * k2);
       }
       ix = row16_min(ix);
       z = row16_sum(z);
-      if (l16 == 0) red[wave][16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), 0.f};
+      if (l16 == 0)
+        red[cq * LM_ROWS + 128 * rh + 16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), 0.f};
     }
+  __syncthreads();
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rl = 16 * mt + 4 * grp + r;
-      const int hc = s_held[rl] - c0;
+      const int rl = 128 * rh + 16 * mt + 4 * grp + r;
+      const int hc = s_held[rl] - cw;
       if (hc >= 0 && hc < 64 && (hc & 15) == l16) {
         float hv = acc[0][mt][r];
 #pragma unroll
-        for (int nb = 1; nb < LM_NB; ++nb)
+        for (int nb = 1; nb < 4; ++nb)
           if (nb == (hc >> 4)) hv = acc[nb][mt][r];
         held_logit[(int64_t)(row0 + rl) * held_stride] = hv;
       }
     }
-  __syncthreads();
   if (tid < nrows) {
-    // merge the four waves in column order: the first wave holding the
+    // merge the four column quarters in column order: the first holding the
     // maximum also holds its smallest column
-    float4 p = red[0][tid];
+    float4 p = red[tid];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
-      const float4 o = red[w][tid];
+      const float4 o = red[w * LM_ROWS + tid];
       if (o.x > p.x) {
         p.y = o.y + p.y * __builtin_amdgcn_exp2f((p.x - o.x) * k2);
         p.x = o.x;
@@ -119,14 +205,6 @@ void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t
                    const int32_t* held, float tau, float4* part, float* held_logit, int held_stride) {
   const float k2 = 1.4426950408889634f / tau;
   const int NT = V / LM_COLS;
-#define DG_LMHEAD(MT_)                                                                                    \
-  hipLaunchKernelGGL(lmhead_kernel<MT_>, dim3(NT * div_up(rows, 16 * MT_)), dim3(256), 0, s, a, rows, K, \
-                     embed, V, held, k2, part, held_logit, held_stride)
-  if (rows <= 32)
-    DG_LMHEAD(2);
-  else if (rows <= 64)
-    DG_LMHEAD(4);
-  else
-    DG_LMHEAD(8);
-#undef DG_LMHEAD
+  hipLaunchKernelGGL(lmhead_kernel, dim3(NT * div_up(rows, LM_ROWS)), dim3(512), 0, s, a, rows, K, embed, V, held,
+                     k2, part, held_logit, held_stride);
 }

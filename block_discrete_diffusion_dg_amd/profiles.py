@@ -26,7 +26,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # Sources that define each profiled kernel (hashed into the traffic record).
 KERNEL_SOURCES = {
     "moe_experts": ["csrc/k_moe.hip", "csrc/stream.h", "csrc/common.h"],
-    "lmhead": ["csrc/k_lmhead.hip", "csrc/stream.h", "csrc/common.h"],
+    "lmhead": ["csrc/k_lmhead.hip", "csrc/common.h"],
 }
 
 
