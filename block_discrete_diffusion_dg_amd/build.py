@@ -24,6 +24,14 @@ HIPFLAGS = [
 ]
 
 
+# Per-file extra flags. Attention keeps its matrix-core accumulators in
+# ordinary VGPRs: its softmax reads and rescales them on every key tile, and
+# in the accumulator file every such access costs a register move.
+EXTRA_FLAGS = {
+    "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -37,7 +45,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

@@ -311,40 +311,53 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   if (!s_last) return;
   // merge: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, split order.
   // The group's partial lines are read only here, after every split wrote
-  // them, and caches start the kernel invalidated: no stale copies.
+  // them, and caches start the kernel invalidated: no stale copies. Every
+  // load of a batch of four splits is issued before any is used (indices
+  // past the last split are clamped and their terms skipped), so the merge
+  // costs one or two memory round trips instead of one per split.
   constexpr int MAXS = DG_ATTN_SPLITS;
+  static_assert(MAXS == 8, "two batches of four splits");
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     if (!qvalid[j]) continue;
+    const int qcol = wave * QPW + 16 * j + l16;
     float2 mls[MAXS];
+#pragma unroll
+    for (int sp = 0; sp < MAXS; ++sp) mls[sp] = ml[((int64_t)group * nsplit + min(sp, nsplit - 1)) * ATTN_QWG + qcol];
     float M = -INFINITY;
 #pragma unroll
-    for (int sp = 0; sp < MAXS; ++sp) {
-      if (sp >= nsplit) break;
-      mls[sp] = ml[((int64_t)group * nsplit + sp) * ATTN_QWG + wave * QPW + 16 * j + l16];
-      M = fmaxf(M, mls[sp].x);
-    }
+    for (int sp = 0; sp < MAXS; ++sp)
+      if (sp < nsplit) M = fmaxf(M, mls[sp].x);
     float num[ND][4], den = 0.f;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) num[dt][rr] = 0.f;
+    auto batch = [&](int s0) {
+      float4 v[4][ND];
 #pragma unroll
-    for (int sp = 0; sp < MAXS; ++sp) {
-      if (sp >= nsplit) break;
-      if (mls[sp].x == -INFINITY) continue;
-      const float wgt = exp2f(mls[sp].x - M);
-      den += wgt * mls[sp].y;
-      const float* op = opart + (((int64_t)sp * rows_total + row[j]) * Hq + qh[j]) * DH;
+      for (int u = 0; u < 4; ++u) {
+        const float* op = opart + (((int64_t)min(s0 + u, nsplit - 1) * rows_total + row[j]) * Hq + qh[j]) * DH;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const float4 v = *reinterpret_cast<const float4*>(op + 16 * dt + 4 * grp);
-        num[dt][0] += wgt * v.x;
-        num[dt][1] += wgt * v.y;
-        num[dt][2] += wgt * v.z;
-        num[dt][3] += wgt * v.w;
+        for (int dt = 0; dt < ND; ++dt) v[u][dt] = *reinterpret_cast<const float4*>(op + 16 * dt + 4 * grp);
       }
-    }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sp = s0 + u;
+        if (sp >= nsplit || mls[sp].x == -INFINITY) continue;
+        const float wgt = exp2f(mls[sp].x - M);
+        den += wgt * mls[sp].y;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          num[dt][0] += wgt * v[u][dt].x;
+          num[dt][1] += wgt * v[u][dt].y;
+          num[dt][2] += wgt * v[u][dt].z;
+          num[dt][3] += wgt * v[u][dt].w;
+        }
+      }
+    };
+    batch(0);
+    if (nsplit > 4) batch(4);
     const float inv = 1.0f / den;
     bf16_t* op = out + ((int64_t)row[j] * Hq + qh[j]) * DH;
 #pragma unroll
