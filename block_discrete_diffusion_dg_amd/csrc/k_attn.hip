@@ -171,22 +171,25 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
 
   auto compute_tile = [&](int tile, const u32x4 (&tb)[CHUNKS][64]) {
     const int k0 = tile * KT;
-    // Fragments are read from LDS at their use; the compiler schedules the
-    // reads. (Forcing all 32 reads ahead of the products costs the registers
-    // that let two work-groups share a compute unit, and measured no faster.)
+    // The tile's K fragments are read from LDS together, then the products
+    // run dimension step by dimension step over the four 16-key subtiles, so
+    // consecutive products never depend on each other.
     f32x4 s[QB][4];
 #pragma unroll
     for (int j = 0; j < QB; ++j)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) s[j][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 kf[4][NS];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const u32x4 kf = tb[ks * NS + st][lane];
+      for (int st = 0; st < NS; ++st) kf[ks][st] = tb[ks * NS + st][lane];
 #pragma unroll
-        for (int j = 0; j < QB; ++j) s[j][ks] = mfma_bf16(kf, qf[j][st], s[j][ks]);
-      }
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < QB; ++j) s[j][ks] = mfma_bf16(kf[ks][st], qf[j][st], s[j][ks]);
     const bool v_edge = k0 + KT > nk;
     const bool mask = v_edge || (causal && k0 + KT - 1 > P + qi_lo);
 #pragma unroll
