@@ -15,11 +15,11 @@ namespace {
 
 // Top-k (k <= 8) of E <= 128 logits for each of RB = 16 rows: every 16-lane
 // group of the work-group's four waves takes one row, lane l16 holding the
-// logits of experts l16 + 16m (m < 8; experts past E read as -inf). Each of k
-// rounds takes the group's arg-max (lane-local over the 8 values, then four
-// xor steps inside the group; on equal values the lower expert id wins) and
-// retires it. The selection comes out in descending order; the group's first
-// lane then writes the experts and the softmax over the selected logits,
+// logits of experts l16 + 16m (m < 8; experts past E read as -inf). Each
+// round takes the group's arg-max (lane-local over the 8 values, then four
+// DPP steps inside the group; on equal values the lower expert id wins) and
+// retires it. The selection comes out in descending order; lane j of the
+// group then writes choice j and its softmax weight over the selected logits,
 // w_j = exp(z_(j) - z_(0)) / sum_i exp(z_(i) - z_(0)), summed in that order.
 // zl: LDS tile [16][E + 1]; rows at or past `rows` are skipped.
 constexpr int RB = 16;  // rows per block
@@ -36,56 +36,59 @@ __device__ __forceinline__ void block_topk16(const float* zl, int E, int k, int 
     const int e = l16 + 16 * m;
     v[m] = e < E ? zr[e] : -INFINITY;
   }
+  // Always eight rounds (k <= 8 <= E; rounds past k are not used), written
+  // with selects so that the rounds stay free of branches.
   float sel[8];
   int sid[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
     // lane-local: experts ascend with m, so a strict '>' keeps the lower id
     float bv = v[0];
     int bi = l16;
 #pragma unroll
-    for (int m = 1; m < 8; ++m)
-      if (v[m] > bv) {
-        bv = v[m];
-        bi = l16 + 16 * m;
-      }
+    for (int m = 1; m < 8; ++m) {
+      const bool gt = v[m] > bv;
+      bv = gt ? v[m] : bv;
+      bi = gt ? l16 + 16 * m : bi;
+    }
     // across the 16 lanes of the row on the DPP network; the merge is a
     // maximum under a total order, so every lane ends with the row's winner
     auto merge = [&](float ov, int oi) {
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      const bool better = ov > bv || (ov == bv && oi < bi);
+      bv = better ? ov : bv;
+      bi = better ? oi : bi;
     };
     merge(dpp_movf<DPP_XOR1>(bv), dpp_mov<DPP_XOR1>(bi));
     merge(dpp_movf<DPP_XOR2>(bv), dpp_mov<DPP_XOR2>(bi));
     merge(dpp_movf<DPP_HALF_MIRROR>(bv), dpp_mov<DPP_HALF_MIRROR>(bi));
     merge(dpp_movf<DPP_MIRROR>(bv), dpp_mov<DPP_MIRROR>(bi));
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      if (bi == l16 + 16 * m) v[m] = -INFINITY;
+    for (int m = 0; m < 8; ++m) v[m] = bi == l16 + 16 * m ? -INFINITY : v[m];
     sel[j] = bv;
     sid[j] = bi;
   }
+  // softmax over the selection, summed in selection order (every lane of the
+  // row forms the same sum); lane j of the row then writes choice j
+  float ex[8], sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = j < k ? expf(sel[j] - sel[0]) : 0.f;
+    sum += ex[j];
+  }
   const int t = t0 + r;
-  if (l16 == 0 && t < rows) {
-    float ex[8], sum = 0.f;
+  if (l16 < k && t < rows) {
+    int my_id = sid[0];
+    float my_ex = ex[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      ex[j] = expf(sel[j] - sel[0]);
-      sum += ex[j];
+    for (int j = 1; j < 8; ++j) {
+      my_id = j == l16 ? sid[j] : my_id;
+      my_ex = j == l16 ? ex[j] : my_ex;
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      if (coherent)
-        __hip_atomic_store(idx + (int64_t)t * k + j, sid[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        idx[(int64_t)t * k + j] = sid[j];
-      w[(int64_t)t * k + j] = ex[j] / sum;
-    }
+    if (coherent)
+      __hip_atomic_store(idx + (int64_t)t * k + l16, my_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      idx[(int64_t)t * k + l16] = my_id;
+    w[(int64_t)t * k + l16] = my_ex / sum;
   }
 }
 
@@ -161,8 +164,11 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
                       : coherent ? __hip_atomic_load(a.idx + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                  : a.idx[i];
   };
-  // expert ids are loaded PB per thread at a time, all issued before any use
+  // expert ids are loaded PB per thread at a time, all issued before any use;
+  // when one batch covers every pair, they stay in registers for step 4
   constexpr int PB = 8;
+  const bool one_batch = pairs <= PB * nt;
+  int evc[PB];
   for (int i = tid; i < E * nb; i += nt) mask[i] = 0ull;
   __syncthreads();
   for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
@@ -171,6 +177,7 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
     for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
+      evc[j] = ev[j];
       const int i = i0 + j * nt, t = i / k;
       if (i < pairs) atomicOr(&mask[ev[j] * nb + (t >> 6)], 1ull << (t & 63));
     }
@@ -226,7 +233,7 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
   for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
     int ev[PB];
 #pragma unroll
-    for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+    for (int j = 0; j < PB; ++j) ev[j] = one_batch ? evc[j] : load_idx(i0 + j * nt);
 #pragma unroll
     for (int j = 0; j < PB; ++j) {
       const int i = i0 + j * nt;
@@ -405,27 +412,32 @@ __global__ __launch_bounds__(256) void router_kernel(
   // block's partial lines are read only here, after all four were written,
   // and caches start the kernel invalidated: no cache holds a stale copy.
   // (E <= 128: at most 8 entries per thread, every load issued before the sums)
+  // The loads are unconditional (indices clamped into the block's rows) and
+  // every sum is formed before any store: gfx950 counts stores in the same
+  // in-order counter as loads, so a store placed between a load and its use
+  // would make that use wait for the store's round trip too.
   float pv[8][RKS];
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    const int i = tid + 256 * b, t = min(t0 + i / E, rows - 1), e = i % E;
-    const bool ok = i < RB * E;
+    const int i = min(tid + 256 * b, RB * E - 1), t = min(t0 + i / E, rows - 1), e = i % E;
 #pragma unroll
-    for (int q = 0; q < RKS; ++q) pv[b][q] = ok ? zpart[((int64_t)q * zs + t) * E + e] : 0.f;
+    for (int q = 0; q < RKS; ++q) pv[b][q] = zpart[((int64_t)q * zs + t) * E + e];
+  }
+  float zv[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    zv[b] = pv[b][0];
+#pragma unroll
+    for (int q = 1; q < RKS; ++q) zv[b] += pv[b][q];
   }
   __syncthreads();  // the dense staging view of zt is no longer read
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int i = tid + 256 * b, r = i / E, t = t0 + r, e = i % E;
-    if (i >= RB * E) break;
-    float v = 0.f;
-    if (t < rows) {
-      v = pv[b][0];
-#pragma unroll
-      for (int q = 1; q < RKS; ++q) v += pv[b][q];
-      z[(int64_t)t * E + e] = v;
+    if (i < RB * E) {
+      if (t < rows) z[(int64_t)t * E + e] = zv[b];
+      zt[r * (E + 1) + e] = t < rows ? zv[b] : 0.f;
     }
-    zt[r * (E + 1) + e] = v;
   }
   __syncthreads();
   block_topk16(zt, E, k, t0, rows, idx, w, do_permute != 0);
