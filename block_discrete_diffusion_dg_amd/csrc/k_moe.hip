@@ -21,6 +21,8 @@
 // runs out counts itself in the spin-timeout word instead of hanging.
 //
 // combine:  h[t] += ys[t] + sum_j y[slot[t][j]]               (fixed order)
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "stream.h"
@@ -97,30 +99,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       const bf16_t* W0 = shared ? p.sg : p.wg + (int64_t)e * p.F * p.d;
       const bf16_t* W1 = shared ? p.su : p.wu + (int64_t)e * p.F * p.d;
       bf16_t* out = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
-      f32x4 ag[MT], au[MT];
-      stream_tile<MT, true>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0 + (int64_t)col0 * p.d,
-                            W1 + (int64_t)col0 * p.d, p.d, ag, au, lds);
-      // Publish: stage the 64-column tile in LDS, write whole 128-byte row
-      // segments with write-through (agent-coherent) stores, wait until they
-      // complete, then move the chunk's counter. An agent-scope release fence
-      // would instead write back this XCD's whole L2 for every item.
-      __syncthreads();   // the tile's last LDS reads are done
-      bf16_t* st = lds;  // [CH][72] bf16, inside the A tile buffers
+      // The tile takes the smallest row count that holds the chunk's rows
+      // (32, 64 or CH): most chunks of a small batch hold far fewer rows than
+      // CH, and the smaller tile stages, reads and multiplies only those.
+      auto gate_up = [&](auto mt_tag) {
+        constexpr int MTI = decltype(mt_tag)::value;
+        f32x4 ag[MTI], au[MTI];
+        stream_tile<MTI, true>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0 + (int64_t)col0 * p.d,
+                               W1 + (int64_t)col0 * p.d, p.d, ag, au, lds);
+        // Publish: stage the 64-column tile in LDS, write whole 128-byte row
+        // segments with write-through (agent-coherent) stores, wait until they
+        // complete, then move the chunk's counter. An agent-scope release fence
+        // would instead write back this XCD's whole L2 for every item.
+        __syncthreads();   // the tile's last LDS reads are done
+        bf16_t* st = lds;  // [16 MTI][72] bf16, inside the A tile buffers
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gv = ag[mt][r];
-          st[(16 * mt + 4 * grp + r) * 72 + wave * 16 + l16] = f2bf(gv / (1.0f + expf(-gv)) * au[mt][r]);
+          for (int r = 0; r < 4; ++r) {
+            const float gv = ag[mt][r];
+            st[(16 * mt + 4 * grp + r) * 72 + wave * 16 + l16] = f2bf(gv / (1.0f + expf(-gv)) * au[mt][r]);
+          }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16 * MTI * 8 / 256; ++i) {
+          const int c = threadIdx.x + 256 * i, rr = c >> 3, seg = (c & 7) * 8;
+          if (row0 + rr < n)
+            store16_coherent(out + (int64_t)(row0 + rr) * ldo + nt * 64 + seg,
+                             *reinterpret_cast<const u32x4*>(st + rr * 72 + seg));
         }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < T::CH * 8 / 256; ++i) {
-        const int c = threadIdx.x + 256 * i, rr = c >> 3, seg = (c & 7) * 8;
-        if (row0 + rr < n)
-          store16_coherent(out + (int64_t)(row0 + rr) * ldo + nt * 64 + seg,
-                           *reinterpret_cast<const u32x4*>(st + rr * 72 + seg));
-      }
+      };
+      if (MT >= 8 && nrows > 64)
+        gate_up(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
+      else if (MT >= 4 && nrows > 32)
+        gate_up(std::integral_constant<int, (MT >= 4 ? 4 : MT)>{});
+      else
+        gate_up(std::integral_constant<int, 2>{});
       wait_stores();
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_fetch_add(done + chunk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -149,22 +163,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       // routing weights of the chunk's slots, staged while the weights stream
       if (threadIdx.x < T::CH)
         s_w[threadIdx.x] = (!shared && threadIdx.x < nrows) ? p.wts[p.widx[base + row0 + threadIdx.x]] : 1.0f;
-      // 128 output columns per item: the wave owns two 16-row weight blocks
+      // 128 output columns per item: the wave owns two 16-row weight blocks;
+      // the tile takes the smallest row count that holds the chunk's rows
       const int c0 = nt * 128 + wave * 32;
-      f32x4 acc0[MT], acc1[MT];
-      stream_tile<MT, true>(A, K, nullptr, row0, nrows, W + (int64_t)c0 * K, W + (int64_t)(c0 + 16) * K, K, acc0,
-                            acc1, lds);
+      auto down = [&](auto mt_tag) {
+        constexpr int MTI = decltype(mt_tag)::value;
+        f32x4 acc0[MTI], acc1[MTI];
+        stream_tile<MTI, true>(A, K, nullptr, row0, nrows, W + (int64_t)c0 * K, W + (int64_t)(c0 + 16) * K, K, acc0,
+                               acc1, lds);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = 16 * mt + 4 * grp + r;
-          if (row0 + q < n) {
-            float* o = out + (int64_t)(row0 + q) * p.d + c0 + l16;
-            o[0] = acc0[mt][r] * s_w[q];
-            o[16] = acc1[mt][r] * s_w[q];
+          for (int r = 0; r < 4; ++r) {
+            const int q = 16 * mt + 4 * grp + r;
+            if (row0 + q < n) {
+              float* o = out + (int64_t)(row0 + q) * p.d + c0 + l16;
+              o[0] = acc0[mt][r] * s_w[q];
+              o[16] = acc1[mt][r] * s_w[q];
+            }
           }
-        }
+      };
+      if (MT >= 8 && nrows > 64)
+        down(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
+      else if (MT >= 4 && nrows > 32)
+        down(std::integral_constant<int, (MT >= 4 ? 4 : MT)>{});
+      else
+        down(std::integral_constant<int, 2>{});
     }
   }
 }
