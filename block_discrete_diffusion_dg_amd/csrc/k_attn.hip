@@ -67,23 +67,33 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
   const int rows_total = rt.n_req * n;
   const int nqv = n * rep;
   const int qblocks = div_up(nqv, ATTN_QWG);
-  // Work-group id -> (key range c = (request, kv head, split), query block).
-  // The query blocks of one key range read the same K/V tiles, so they get
-  // ids that are equal modulo 8: dispatch is round-robin over the 8 XCDs,
-  // so they share one XCD's L2 copy of those tiles (fetched from HBM once).
-  // Ranges go in runs of 8: run cb holds ranges 8cb .. 8cb+width-1, ordered
-  // query block major.
-  const int C = rt.n_req * Hkv * nsplit;
-  int c, qb;
-  {
+  // Work-group id -> (request r, kv head g, query block qb, key split).
+  // Dispatch is round-robin over the 8 XCDs (ids equal modulo 8 share an
+  // XCD and its L2). When the (request, kv head) pairs come in multiples of
+  // 8, every work-group of one pair gets ids equal modulo 8: the pair's K/V
+  // tiles are fetched into that XCD's L2 once, and the split merge reads the
+  // partial outputs its own XCD wrote. Otherwise the query blocks of one key
+  // range (r, g, split) get ids equal modulo 8, in runs of 8 ranges ordered
+  // query block major, so they still share one L2 copy of the tiles.
+  const int npairs = rt.n_req * Hkv;
+  int r, g, qb, split;
+  if ((npairs & 7) == 0) {
+    const int per = qblocks * nsplit, x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int pair = x + 8 * (i / per), local = i % per;
+    qb = local / nsplit;
+    split = local % nsplit;
+    r = pair / Hkv;
+    g = pair % Hkv;
+  } else {
+    const int C = npairs * nsplit;
     const int b = blockIdx.x, run = 8 * qblocks;
     const int cb = b / run, rem = b % run, width = min(8, C - 8 * cb);
     qb = rem / width;
-    c = 8 * cb + rem % width;
+    const int c = 8 * cb + rem % width;
+    split = c % nsplit;
+    g = (c / nsplit) % Hkv;
+    r = c / (nsplit * Hkv);
   }
-  const int split = c % nsplit;
-  const int g = (c / nsplit) % Hkv;
-  const int r = c / (nsplit * Hkv);
   const int group = (r * Hkv + g) * qblocks + qb;  // (request, kv head, query block)
 
   const int P = rt.pos0[r];
