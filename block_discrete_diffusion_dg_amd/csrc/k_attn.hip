@@ -383,7 +383,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
 }  // namespace
 
 // Splits of the key range: enough work-groups to cover the GPU about once
-// (256 compute units), at most DG_ATTN_SPLITS, at least one tile per split.
+// (256 compute units, one work-group each); when the key ranges are long
+// (at least 32 tiles per split at two work-groups per CU), enough for two
+// per CU, whose per-tile softmax chains then interleave (measured 160 ->
+// 120 us at a 32,768-key prefix; at 2,304 keys two per CU are slower). At
+// most DG_ATTN_SPLITS, at least one tile per split.
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
   (void)max_rows;
   const int rep = Hq / Hkv;
@@ -391,7 +395,8 @@ int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows) {
   int max_pos = 0;
   for (int r = 0; r < rt.n_req; ++r) max_pos = max(max_pos, rt.pos0[r]);
   const int tiles = div_up(max_pos + rt.rows_per_req, KT);
-  int ns = div_up(256, base);
+  const int target = tiles >= 32 * div_up(512, base) ? 512 : 256;
+  int ns = div_up(target, base);
   ns = min(ns, DG_ATTN_SPLITS);
   ns = min(ns, tiles);
   return max(ns, 1);
