@@ -35,7 +35,12 @@ Readings where the pages are silent (each is listed in the design doc):
   router = top-k of the router logits (ties to the lower expert id), softmax
   over the k selected logits, shared expert added with weight 1;
   SwiGLU experts; LM head tied to the embedding, no input scaling;
-  confidence = log of the temperature-tau probability of the candidate token;
+  confidence = log of the temperature-tau probability of the candidate token,
+  or (entropy mode) minus the entropy of the position's temperature-tau
+  distribution;
+  adaptive stopping compares the mean entropy of that distribution with the
+  threshold, requires every argmax to equal the previous step's, and then
+  accepts every position (the step acts as the block's last);
   candidate = held token for committed positions, greedy argmax otherwise;
   cumulative schedule k_s = floor(s * C / S);
   committed positions hold their token until they fall out of the top-k_s.
@@ -274,23 +279,62 @@ def row_stats(L: np.ndarray, held: np.ndarray, tau: float):
     return M, a, logZ, gx
 
 
+def row_entropy(L: np.ndarray, tau: float, chunk: int = 16) -> np.ndarray:
+    """Entropy in nats of each row's temperature-tau distribution,
+    H_i = -sum_v p_iv log p_iv with p_i = softmax(L_i / tau); a term with
+    p_iv = 0 contributes 0. (explainer §3.3: the sampler's uncertainty
+    measure is the predicted entropy of each canvas position.)"""
+    L = np.asarray(L, np.float64)
+    H = np.empty(L.shape[0], np.float64)
+    for r0 in range(0, L.shape[0], chunk):
+        S = L[r0:r0 + chunk] / tau
+        e = np.exp(S - S.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            plogp = np.where(p > 0, p * np.log(p), 0.0)
+        H[r0:r0 + chunk] = -plogp.sum(axis=1)
+    return H
+
+
+def adaptive_stop(H: np.ndarray, a: np.ndarray, a_prev: Optional[np.ndarray],
+                  threshold: float) -> bool:
+    """Adaptive stopping (explainer §3.3): the block stops when the mean
+    predicted entropy over the canvas is below the threshold and every
+    position's most likely token is the one it had at the previous step.
+    The first step of a block has no previous prediction and never stops."""
+    if a_prev is None:
+        return False
+    return bool(np.mean(H) < threshold and np.array_equal(np.asarray(a), np.asarray(a_prev)))
+
+
 def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
-           n_steps: int, seed: int, block: int, request: int, vocab: int):
+           n_steps: int, seed: int, block: int, request: int, vocab: int,
+           confidence: str = "prob", H: Optional[np.ndarray] = None, stop: bool = False):
     """Confidence-ordered acceptance with uniform re-noise.
 
     Candidate y_i: the held token if position i is committed, else the argmax.
-    Confidence c_i = log p_tau(y_i) = (L[y_i] - M_i)/tau - log Z_i.
+    Confidence, by `confidence`:
+      "prob":    c_i = log p_tau(y_i) = (L[y_i] - M_i)/tau - log Z_i;
+      "entropy": c_i = -H_i, so low-entropy positions come first
+                 (explainer §3.3).
     The k_s positions of highest confidence (ties to the lower position) are
     accepted (x_i = y_i, committed); every other position is re-noised to a
-    uniform id from Philox at counter (i, step, block, request).
+    uniform id from Philox at counter (i, step, block, request). When the
+    block stops early (`stop`), the step acts as the last one: every position
+    is accepted.
     Returns (new x, new committed mask, c, accepted-set boolean mask).
     """
     C = x.shape[0]
     committed = np.asarray(m).astype(bool)
     y = np.where(committed, x, a)
-    Ly = np.where(committed, gx, M)
-    c = (Ly - M) / tau - logZ
-    k_s = commit_count(step, n_steps, C)
+    if confidence == "prob":
+        Ly = np.where(committed, gx, M)
+        c = (Ly - M) / tau - logZ
+    elif confidence == "entropy":
+        c = -np.asarray(H, np.float64)
+    else:
+        raise ValueError(confidence)
+    k_s = C if stop else commit_count(step, n_steps, C)
     order = sorted(range(C), key=lambda i: (-c[i], i))
     accept = np.zeros(C, bool)
     accept[order[:k_s]] = True
@@ -364,31 +408,45 @@ def commit_block(weights, cfg, req: Request, canvas_ids: np.ndarray):
 
 def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step: int,
                  n_steps: int, seed: int, block: int, request: int,
-                 keep: Optional[Dict] = None):
+                 keep: Optional[Dict] = None, confidence: str = "prob",
+                 stop_entropy: float = 0.0, a_prev: Optional[np.ndarray] = None):
     """One denoising step of one request's canvas.
 
     The canvas attends bidirectionally to itself and to the cached prefix; the
     LM head gives per-row statistics; the sampler accepts the top-k_s positions
-    and re-noises the rest. The cache is read, never written.
+    and re-noises the rest. The cache is read, never written. With
+    stop_entropy > 0 the step checks adaptive stopping against a_prev, the
+    argmax of the previous step (None at the first step of a block).
     """
     layers = [] if keep is not None else None
     h, _, _ = forward_rows(weights, cfg, req, np.asarray(x), causal=False, keep_layers=layers)
     tau = tau_at(step, n_steps, cfg.tau_first, cfg.tau_last)
     L = logits(h, weights.final_norm, weights.embed, cfg)
     M, a, logZ, gx = row_stats(L, np.asarray(x), tau)
+    H = row_entropy(L, tau)
+    stop = stop_entropy > 0 and adaptive_stop(H, a, a_prev, stop_entropy)
     x_new, m_new, c, accept = sample(x, m, M, a, logZ, gx, tau, step, n_steps, seed, block,
-                                     request, cfg.vocab)
+                                     request, cfg.vocab, confidence=confidence, H=H, stop=stop)
     if keep is not None:
         keep.update(layers=layers, h=h, logits=L, M=M, a=a, logZ=logZ, gx=gx, c=c,
-                    accept=accept, tau=tau)
+                    accept=accept, tau=tau, H=H, stop=stop)
     return x_new, m_new
 
 
 def generate_block(weights, cfg, req: Request, n_steps: int, seed: int, block: int,
-                   request: int):
-    """Denoise one block from uniform noise for n_steps, then commit it."""
+                   request: int, confidence: str = "prob", stop_entropy: float = 0.0):
+    """Denoise one block from uniform noise for at most n_steps (fewer when
+    adaptive stopping fires), then commit it. Returns (x, m, steps taken)."""
     x, m = init_canvas(seed, block, request, cfg.canvas, cfg.vocab)
+    a_prev = None
+    taken = 0
     for s in range(1, n_steps + 1):
-        x, m = denoise_step(weights, cfg, req, x, m, s, n_steps, seed, block, request)
+        keep: Dict = {}
+        x, m = denoise_step(weights, cfg, req, x, m, s, n_steps, seed, block, request, keep=keep,
+                            confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev)
+        a_prev = keep["a"]
+        taken = s
+        if keep["stop"]:
+            break
     commit_block(weights, cfg, req, x)
-    return x, m
+    return x, m, taken

@@ -9,6 +9,7 @@ import dataclasses
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 import torch
 import torch.nn.functional as F
 
@@ -63,6 +64,19 @@ def _pin_row_stats():
     return np.allclose(logZ, scipy.special.logsumexp(L / 0.5, 1) - M / 0.5)
 
 
+def _pin_row_entropy():
+    L = RNG.normal(size=(4, 60)) * 2
+    want = scipy.stats.entropy(scipy.special.softmax(L / 0.6, axis=1), axis=1)
+    return np.allclose(om.row_entropy(L, 0.6), want)
+
+
+def _pin_adaptive_stop():
+    H = np.array([0.5, 0.25])
+    a = np.array([3, 4])
+    return (om.adaptive_stop(H, a, a.copy(), 1.0) and not om.adaptive_stop(H, a, np.array([3, 5]), 1.0)
+            and not om.adaptive_stop(H, a, a.copy(), 0.375) and not om.adaptive_stop(H, a, None, 1.0))
+
+
 def _pin_rms_norm():
     x = RNG.normal(size=(3, 32))
     g = RNG.normal(size=32)
@@ -112,12 +126,25 @@ def _bad_row_stats(L, held, tau):
     return M, a, logZ, gx
 
 
+def _bad_row_entropy(L, tau, chunk=16):
+    return _real["row_entropy"](L, 1.0, chunk)  # temperature dropped
+
+
+def _bad_row_entropy_log2(L, tau, chunk=16):
+    return _real["row_entropy"](L, tau, chunk) / np.log(2)  # bits instead of nats
+
+
+def _bad_adaptive_stop(H, a, a_prev, threshold):
+    return a_prev is not None and bool(np.mean(H) < threshold)  # argmax condition dropped
+
+
 def _bad_rms_norm(x, gain, eps):
     x = np.asarray(x, np.float64)
     return x / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)  # gain dropped
 
 
-_real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats}
+_real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
+         "row_entropy": om.row_entropy}
 
 CASES = [
     ("rope", _bad_rope, _pin_rope),
@@ -127,6 +154,9 @@ CASES = [
     ("moe", _bad_moe_no_shared, _pin_dense_mixture),
     ("row_stats", _bad_row_stats, _pin_row_stats),
     ("rms_norm", _bad_rms_norm, _pin_rms_norm),
+    ("row_entropy", _bad_row_entropy, _pin_row_entropy),
+    ("row_entropy", _bad_row_entropy_log2, _pin_row_entropy),
+    ("adaptive_stop", _bad_adaptive_stop, _pin_adaptive_stop),
 ]
 
 

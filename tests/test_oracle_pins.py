@@ -306,6 +306,81 @@ def test_sampler_invariants_over_a_block():
     assert m.all()
 
 
+def test_entropy_closed_forms_and_library():
+    tau = 0.7
+    # equal logits: the uniform distribution, H = log V
+    for V in (5, 97, 4096):
+        assert abs(om.row_entropy(np.full((1, V), 3.25), tau)[0] - np.log(V)) < 1e-12
+    # two tokens: the binary entropy of p = sigmoid(x / tau)
+    for x in (-3.0, 0.1, 2.5):
+        p = 1.0 / (1.0 + np.exp(-x / tau))
+        want = -(p * np.log(p) + (1 - p) * np.log(1 - p))
+        assert abs(om.row_entropy(np.array([[0.0, x]]), tau)[0] - want) < 1e-12
+    # k equal maxima far above the rest: H = log k (the rest underflow to p = 0)
+    L = np.full((1, 64), -1e4)
+    L[0, [3, 17, 40]] = 5.0
+    assert abs(om.row_entropy(L, tau)[0] - np.log(3)) < 1e-12
+    # random rows: scipy's entropy of the softmax, shift invariance, bounds
+    L = RNG.normal(size=(9, 300)) * 2.5
+    H = om.row_entropy(L, tau)
+    want = scipy.stats.entropy(scipy.special.softmax(L / tau, axis=1), axis=1)
+    assert np.allclose(H, want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(om.row_entropy(L + 7.0, tau), H, rtol=1e-12)
+    assert np.all(H >= 0) and np.all(H <= np.log(300))
+    # a lower temperature never raises the entropy (dH/dbeta = -beta Var_p(L) <= 0)
+    Hs = np.stack([om.row_entropy(L, t) for t in (2.0, 1.0, 0.8, 0.6, 0.4, 0.2)])
+    assert np.all(np.diff(Hs, axis=0) <= 1e-12)
+
+
+def test_entropy_confidence_and_adaptive_stop():
+    V, C, S, s = 53, 24, 6, 2
+    L = RNG.normal(size=(C, V)) * 2
+    L[5] = L[9]  # equal entropies: the lower position ranks first
+    x, m = om.init_canvas(1, 0, 0, C, V)
+    m = (np.arange(C) % 3 == 0).astype(np.uint8)
+    tau = om.tau_at(s, S, 0.8, 0.4)
+    M, a, logZ, gx = om.row_stats(L, x, tau)
+    H = om.row_entropy(L, tau)
+    x2, m2, c, acc = om.sample(x, m, M, a, logZ, gx, tau, s, S, 1, 0, 0, V, confidence="entropy", H=H)
+    k_s = om.commit_count(s, S, C)
+    order = sorted(range(C), key=lambda i: (H[i], i))
+    assert np.array_equal(np.flatnonzero(acc), np.sort(order[:k_s]))
+    assert np.array_equal(c, -H)
+    y = np.where(m.astype(bool), x, a)
+    assert np.array_equal(x2[acc], y[acc]) and m2.sum() == k_s
+    # the stop rule: mean entropy below the threshold and an unchanged argmax
+    thr_hi, thr_lo = H.mean() + 1e-9, H.mean() - 1e-9
+    assert not om.adaptive_stop(H, a, None, thr_hi)
+    assert om.adaptive_stop(H, a, a.copy(), thr_hi)
+    assert not om.adaptive_stop(H, a, a.copy(), thr_lo)
+    moved = a.copy()
+    moved[C - 1] = (moved[C - 1] + 1) % V
+    assert not om.adaptive_stop(H, a, moved, thr_hi)
+    # a stopped step accepts every position with its candidate
+    x3, m3, _, acc3 = om.sample(x, m, M, a, logZ, gx, tau, s, S, 1, 0, 0, V, confidence="entropy",
+                                H=H, stop=True)
+    assert acc3.all() and m3.all() and np.array_equal(x3, y)
+
+
+def test_adaptive_stop_in_the_denoising_step():
+    cfg, w = _tiny_model(n_layers=1)
+    req = om.Request(cfg, 64 + 2 * cfg.canvas)
+    om.prefill(w, cfg, req, synth.make_prompt(64, cfg.vocab, 0).numpy())
+    x, m = om.init_canvas(0, 0, 0, cfg.canvas, cfg.vocab)
+    k1, k2 = {}, {}
+    om.denoise_step(w, cfg, req, x, m, 2, 8, 0, 0, 0, keep=k1, stop_entropy=1e9)
+    assert not k1["stop"]  # no previous prediction
+    # the same canvas again: same argmax, so any threshold above the mean stops it
+    x2, m2 = om.denoise_step(w, cfg, req, x, m, 2, 8, 0, 0, 0, keep=k2, stop_entropy=1e9,
+                             a_prev=k1["a"])
+    assert k2["stop"] and m2.all() and np.array_equal(x2, np.where(m.astype(bool), x, k2["a"]))
+    k3 = {}
+    om.denoise_step(w, cfg, req, x, m, 2, 8, 0, 0, 0, keep=k3, stop_entropy=k1["H"].mean() * 0.5,
+                    a_prev=k1["a"])
+    assert not k3["stop"]
+    assert np.allclose(k1["H"], om.row_entropy(k1["logits"], k1["tau"]))
+
+
 # ----------------------------------------------------------------------------- whole step
 
 def _tiny_model(n_layers=1, gain_jitter=0.1, **kw):
@@ -350,7 +425,8 @@ def test_denoise_leaves_cache_untouched_and_full_block_loop_runs():
     x2, m2 = om.denoise_step(w, cfg, req, x, m, 1, 4, 0, 0, 0)
     assert np.array_equal(req.k, k0) and np.array_equal(req.v, v0) and req.length == 64
     assert m2.sum() == 8
-    x_final, m_final = om.generate_block(w, cfg, req, 4, 0, 0, 0)
+    x_final, m_final, taken = om.generate_block(w, cfg, req, 4, 0, 0, 0)
+    assert taken == 4
     assert m_final.all() and req.length == 64 + cfg.canvas
 
 
