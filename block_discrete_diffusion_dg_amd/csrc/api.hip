@@ -67,6 +67,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.ss = take(R * (d / 64) * 4);
   L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
   L.sync = take((router_sync_words(c.max_rows) + groups) * 4);  // router row blocks, then attention groups
+  L.prev = take((size_t)c.max_requests * c.canvas * 4);
   L.total = o;
   return L;
 }
@@ -107,6 +108,9 @@ struct dg_ctx {
   char* ws;
   dg_ws_layout lay;
   std::vector<int32_t> len;
+  // per slot: 1 once a denoising step of the current block has left its
+  // argmax in the workspace (adaptive stopping compares against it)
+  std::vector<uint8_t> prev_valid;
   bool sticky = false;
   std::string err;
 
@@ -270,8 +274,17 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
                                       tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
                                       (int)(sizeof(dg_row_stats) / sizeof(float))));
   STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats));
+  // the previous step's argmax of a slot counts only after a step of the
+  // same block (host-side, in stream order)
+  uint32_t prev_valid = 0;
+  for (int r = 0; r < a->n_req; ++r) {
+    if (c->prev_valid[a->req[r]]) prev_valid |= 1u << r;
+    c->prev_valid[a->req[r]] = 1;
+  }
+  const SamplerMode mode{a->confidence, a->stop_entropy > 0.f ? a->stop_entropy : 0.f,
+                         c->buf<int32_t>(L.prev), prev_valid, a->d_stop};
   STAGE(DG_STAGE_SAMPLER, launch_sampler(s, stats, a->n_req, g.canvas, g.vocab, a->d_canvas, a->d_committed,
-                                         a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats));
+                                         a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats, mode));
 }
 
 dg_status check_ctx(dg_ctx* c) {
@@ -293,6 +306,9 @@ dg_status check_step_args(dg_ctx* c, const dg_step_args* a, bool need_step) {
   }
   if (need_step && (a->n_steps <= 0 || a->step < 1 || a->step > a->n_steps))
     return c->fail(DG_EINVAL, "need 1 <= step <= n_steps");
+  if (need_step && a->confidence != DG_CONF_PROB && a->confidence != DG_CONF_ENTROPY)
+    return c->fail(DG_EINVAL, "confidence must be DG_CONF_PROB or DG_CONF_ENTROPY");
+  if (need_step && a->stop_entropy != a->stop_entropy) return c->fail(DG_EINVAL, "stop_entropy is NaN");
   return DG_OK;
 }
 
@@ -366,6 +382,7 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
   c->kv.n_kv_heads = cfg->n_kv_heads;
   c->kv.head_dim = cfg->head_dim;
   c->len.assign(cfg->max_requests, 0);
+  c->prev_valid.assign(cfg->max_requests, 0);
   *out = c;
   return DG_OK;
 }
@@ -390,6 +407,7 @@ int32_t dg_cache_len(const dg_ctx* c, int32_t req) {
 dg_status dg_reset(dg_ctx* c, int32_t req) {
   if (!c || req < 0 || req >= c->cfg.max_requests) return DG_EINVAL;
   c->len[req] = 0;
+  c->prev_valid[req] = 0;
   return DG_OK;
 }
 
@@ -432,6 +450,7 @@ dg_status dg_init_canvas(dg_ctx* c, void* stream, const dg_step_args* a) {
   if (st) return st;
   st = check_step_args(c, a, false);
   if (st) return st;
+  for (int r = 0; r < a->n_req; ++r) c->prev_valid[a->req[r]] = 0;  // a new block
   launch_init_canvas((hipStream_t)stream, a->n_req, c->cfg.canvas, c->cfg.vocab, a->d_canvas,
                      a->d_committed, a->seed, a->block, a->req);
   return c->check_hip("dg_init_canvas");
@@ -480,7 +499,10 @@ dg_status dg_commit_block(dg_ctx* c, void* stream, int32_t n_req, const int32_t*
   run_encoder(c, s, rt);
   st = c->check_hip("dg_commit_block");
   if (st) return st;
-  for (int r = 0; r < n_req; ++r) c->len[req[r]] += g.canvas;
+  for (int r = 0; r < n_req; ++r) {
+    c->len[req[r]] += g.canvas;
+    c->prev_valid[req[r]] = 0;  // the next block starts without a previous step
+  }
   return DG_OK;
 }
 

@@ -1,12 +1,18 @@
 // Vocabulary statistics merge and the confidence sampler.
 //
-// The LM-head kernel leaves, per row, one (max, sum of exp, argmax) partial
-// for every 256-column tile of the vocabulary. The merge rescales the sums to
-// the global max (online log-sum-exp) and keeps the lowest index among equal
-// maxima. The sampler then, per request (one work-group, one thread per
-// canvas position):
+// The LM-head kernel leaves, per row, one (max m, sum of exp z, argmax,
+// entropy sum w) partial for every 256-column tile of the vocabulary, with
+// t_v = (L_v - m) log2(e) / tau, z = sum 2^t_v and w = sum 2^t_v t_v. The
+// merge rescales them to the global max (online log-sum-exp; a partial
+// shifted by d = (m - M) log2(e)/tau contributes 2^d z and 2^d (w + d z)),
+// keeps the lowest index among equal maxima, and gives
+//   log Z = ln z,  H = ln z - ln2 * w / z  (entropy of softmax(L / tau)).
+// The sampler then, per request (one work-group, one thread per canvas
+// position):
 //   y_i  = held token if committed, else the argmax;
-//   c_i  = (L_i[y_i] - M_i) / tau - log Z_i;
+//   c_i  = (L_i[y_i] - M_i) / tau - log Z_i, or -H_i in entropy mode;
+//   stop = mean_i H_i < threshold and every argmax equals the previous
+//          step's (adaptive stopping; then every position is accepted);
 //   rank = #{j : c_j > c_i or (c_j == c_i and j < i)};
 //   rank < k_s: accept (x_i = y_i, committed); otherwise re-noise to a
 //   uniform id drawn from Philox4x32-10 at counter (i, step, block, slot).
@@ -19,49 +25,60 @@
 
 namespace {
 
-__device__ __forceinline__ void lse_merge(float& m, float& z, int& a, float m2, float z2, int a2,
-                                          float k2) {
+__device__ __forceinline__ void lse_merge(float& m, float& z, float& w, int& a, float m2, float z2,
+                                          float w2, int a2, float k2) {
   if (m2 > m || (m2 == m && a2 < a)) {
     // the incoming partial has the larger max (or wins the tie on index)
-    const float zz = (m == -INFINITY) ? 0.f : z * exp2f((m - m2) * k2);
-    z = z2 + zz;
+    if (m == -INFINITY) {
+      z = z2;
+      w = w2;
+    } else {
+      const float d = (m - m2) * k2, f = exp2f(d);
+      w = w2 + f * (w + d * z);
+      z = z2 + f * z;
+    }
     m = m2;
     a = a2;
-  } else {
-    z += (m2 == -INFINITY) ? 0.f : z2 * exp2f((m2 - m) * k2);
+  } else if (m2 != -INFINITY) {
+    const float d = (m2 - m) * k2, f = exp2f(d);
+    w += f * (w2 + d * z2);
+    z += f * z2;
   }
 }
 
 __global__ __launch_bounds__(256) void lm_merge_kernel(const float4* __restrict__ part, int n_parts,
                                                        float k2, dg_row_stats* __restrict__ stats) {
-  __shared__ float sm[4], sz[4];
+  __shared__ float sm[4], sz[4], sw[4];
   __shared__ int sa[4];
   const int row = blockIdx.x;
-  float m = -INFINITY, z = 0.f;
+  float m = -INFINITY, z = 0.f, w = 0.f;
   int a = 0x7fffffff;
   const float4* p = part + (int64_t)row * n_parts;
   for (int i = threadIdx.x; i < n_parts; i += 256) {
     const float4 v = p[i];
-    lse_merge(m, z, a, v.x, v.y, __float_as_int(v.z), k2);
+    lse_merge(m, z, w, a, v.x, v.y, v.w, __float_as_int(v.z), k2);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, WAVE), z2 = __shfl_xor(z, o, WAVE);
+    const float m2 = __shfl_xor(m, o, WAVE), z2 = __shfl_xor(z, o, WAVE), w2 = __shfl_xor(w, o, WAVE);
     const int a2 = __shfl_xor(a, o, WAVE);
-    lse_merge(m, z, a, m2, z2, a2, k2);
+    lse_merge(m, z, w, a, m2, z2, w2, a2, k2);
   }
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sm[wave] = m;
     sz[wave] = z;
+    sw[wave] = w;
     sa[wave] = a;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) lse_merge(m, z, a, sm[w], sz[w], sa[w], k2);
+    for (int q = 1; q < 4; ++q) lse_merge(m, z, w, a, sm[q], sz[q], sw[q], sa[q], k2);
+    const float lz = logf(z);
     stats[row].max_logit = m;
-    stats[row].log_z = logf(z);
+    stats[row].log_z = lz;
     stats[row].argmax = a;
+    stats[row].entropy = lz - 0.69314718055994531f * (w / z);
   }
 }
 
@@ -69,30 +86,48 @@ __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict_
                                                        int32_t* __restrict__ canvas,
                                                        uint8_t* __restrict__ committed, int step,
                                                        int k_s, float tau, SampleTable st,
-                                                       dg_row_stats* __restrict__ stats_out) {
-  __shared__ float cs[1024];
-  const int r = blockIdx.x, i = threadIdx.x;
+                                                       dg_row_stats* __restrict__ stats_out, SamplerMode mode) {
+  __shared__ float cs[1024], hs[1024];
+  const int r = blockIdx.x, i = threadIdx.x, nt = blockDim.x;
   const int row = r * C + i;
-  float c = 0.f;
+  float c = 0.f, H = 0.f;
   int y = 0;
-  bool held = false;
+  bool held = false, moved = false;
   dg_row_stats sr;
   if (i < C) {
     sr = stats[row];
     held = committed[row] != 0;
     y = held ? canvas[row] : sr.argmax;
-    const float Ly = held ? sr.held_logit : sr.max_logit;
-    c = (Ly - sr.max_logit) / tau - sr.log_z;
+    H = sr.entropy;
+    if (mode.confidence == DG_CONF_ENTROPY) {
+      c = -H;
+    } else {
+      const float Ly = held ? sr.held_logit : sr.max_logit;
+      c = (Ly - sr.max_logit) / tau - sr.log_z;
+    }
     cs[i] = c;
+    int32_t* prev = mode.prev_argmax + (int64_t)st.slot[r] * C + i;
+    moved = !((mode.prev_valid >> r) & 1u) || *prev != sr.argmax;
+    *prev = sr.argmax;
   }
-  __syncthreads();
+  hs[i] = H;
+  // any position whose argmax changed since the previous step of the block
+  const bool any_moved = __syncthreads_or(moved ? 1 : 0) != 0;
+  // sum of the entropies in a fixed tree order (deterministic)
+  for (int sft = 512; sft > 0; sft >>= 1) {
+    if (i < sft && i + sft < nt) hs[i] += hs[i + sft];
+    __syncthreads();
+  }
+  const bool stop = mode.stop_entropy > 0.f && !any_moved && hs[0] < mode.stop_entropy * (float)C;
+  if (i == 0 && mode.stop) mode.stop[r] = stop ? 1 : 0;
   if (i >= C) return;
+  const int k = stop ? C : k_s;
   int rank = 0;
   for (int j = 0; j < C; ++j) {
     const float cj = cs[j];
     rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
   }
-  const bool accept = rank < k_s;
+  const bool accept = rank < k;
   if (accept) {
     canvas[row] = y;
     committed[row] = 1;
@@ -103,7 +138,7 @@ __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict_
   }
   sr.conf = c;
   sr.accepted = accept ? 1 : 0;
-  sr.pad[0] = sr.pad[1] = 0;
+  sr.pad = 0;
   stats[row] = sr;
   if (stats_out) stats_out[row] = sr;
 }
@@ -119,9 +154,10 @@ void launch_lm_merge(hipStream_t s, const float4* part, int n_parts, int rows, f
 
 void launch_sampler(hipStream_t s, void* stats, int n_req, int C, int V, int32_t* canvas,
                     uint8_t* committed, int step, int k_s, float tau, const uint64_t* seeds_host,
-                    const int32_t* blocks_host, const int32_t* slots_host, void* stats_out) {
+                    const int32_t* blocks_host, const int32_t* slots_host, void* stats_out,
+                    const SamplerMode& mode) {
   SampleTable st = make_sample_table(n_req, seeds_host, blocks_host, slots_host);
   const int threads = ((C + 63) / 64) * 64;
   hipLaunchKernelGGL(sampler_kernel, dim3(n_req), dim3(threads), 0, s, (dg_row_stats*)stats, C, V,
-                     canvas, committed, step, k_s, tau, st, (dg_row_stats*)stats_out);
+                     canvas, committed, step, k_s, tau, st, (dg_row_stats*)stats_out, mode);
 }

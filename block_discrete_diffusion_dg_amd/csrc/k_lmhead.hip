@@ -1,9 +1,9 @@
 // LM head: logits L = u E^T on the gfx950 matrix cores (u: the final-normed
 // token rows, bf16; E: the tied embedding in the fragment-major layout of
 // stream.h), with an epilogue that reduces every row of each 256-column tile
-// to (max, first argmax, sum of exp), so the vocabulary-wide softmax is never
-// materialised (the statistics the confidence sampler needs: codemajin.net
-// DiffusionGemma explainer §3.3).
+// to (max, first argmax, sum of exp, entropy sum), so the vocabulary-wide
+// softmax is never materialised (the statistics the confidence sampler and
+// adaptive stopping need: codemajin.net DiffusionGemma explainer §3.3).
 //
 // A work-group of 512 threads covers 256 token rows x 256 vocabulary
 // columns. K advances in 32-wide steps; each step's operands are 32
@@ -31,8 +31,8 @@ constexpr int LM_FRAGS = LM_ROWS / 16 + LM_COLS / 16;  // 1 KB fragments per ste
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// part[row][nt] = (max, sum exp2((L - max) * k2), first argmax bits, 0) over
-// the 256 columns of tile nt, k2 = log2(e) / tau; the lane holding the column
+// part[row][nt] = (max, sum 2^t, first argmax bits, sum 2^t t) over the 256
+// columns of tile nt, t = (L - max) * k2, k2 = log2(e) / tau; the lane holding the column
 // of the row's held token writes that logit to held_logit[row * held_stride].
 // Requires K % 128 == 0 and V % 256 == 0 (the configuration check enforces
 // d % 256 == 0 and V % 256 == 0).
@@ -128,15 +128,16 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Epilogue in the ring's memory: red[4][256] (max, sum, argmax) per column
-  // quarter and row, and the rows' held tokens.
+  // Epilogue in the ring's memory: red[4][256] (max, sum, argmax, entropy
+  // sum) per column quarter and row, and the rows' held tokens.
   float4* red = reinterpret_cast<float4*>(&r0[0][0]);
   int* s_held = reinterpret_cast<int*>(&r1[0][0]);
   if (tid < LM_ROWS) s_held[tid] = tid < nrows ? held[row0 + tid] : -1;
   // Per row (128rh + 16mt + 4grp + r), over the wave's 64 columns
-  // (cw + 16nb + l16): max, the smallest column holding it, and
-  // sum exp2((L - max) k2), on the DPP network. All rows are reduced first
-  // (independent chains), then the held-token logits are picked out.
+  // (cw + 16nb + l16): max, the smallest column holding it,
+  // sum 2^t and sum 2^t t with t = (L - max) k2, on the DPP network. All rows
+  // are reduced first (independent chains), then the held-token logits are
+  // picked out.
   const int cw = c0 + 64 * cq;
   float m[8][4];
 #pragma unroll
@@ -149,17 +150,20 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int ix = 0x7fffffff;
-      float z = 0.f;
+      float z = 0.f, zt = 0.f;
 #pragma unroll
       for (int nb = 3; nb >= 0; --nb) {
         const float v = acc[nb][mt][r];
         if (v == m[mt][r]) ix = cw + 16 * nb + l16;
-        z += __builtin_amdgcn_exp2f((v - m[mt][r]) * k2);
+        const float t = (v - m[mt][r]) * k2, e = __builtin_amdgcn_exp2f(t);
+        z += e;
+        zt = fmaf(e, t, zt);
       }
       ix = row16_min(ix);
       z = row16_sum(z);
+      zt = row16_sum(zt);
       if (l16 == 0)
-        red[cq * LM_ROWS + 128 * rh + 16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), 0.f};
+        red[cq * LM_ROWS + 128 * rh + 16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), zt};
     }
   __syncthreads();
 #pragma unroll
@@ -182,13 +186,19 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
     float4 p = red[tid];
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
+      // a partial shifted down by d (= (max - new max) k2 <= 0) scales its
+      // sums by 2^d and its entropy sum picks up d times its sum
       const float4 o = red[w * LM_ROWS + tid];
       if (o.x > p.x) {
-        p.y = o.y + p.y * __builtin_amdgcn_exp2f((p.x - o.x) * k2);
+        const float d = (p.x - o.x) * k2, f = __builtin_amdgcn_exp2f(d);
+        p.w = o.w + f * fmaf(d, p.y, p.w);
+        p.y = o.y + p.y * f;
         p.x = o.x;
         p.z = o.z;
       } else {
-        p.y += o.y * __builtin_amdgcn_exp2f((o.x - p.x) * k2);
+        const float d = (o.x - p.x) * k2, f = __builtin_amdgcn_exp2f(d);
+        p.w += f * fmaf(d, o.y, o.w);
+        p.y += o.y * f;
       }
     }
     part[(int64_t)(row0 + tid) * NT + nt] = p;

@@ -77,6 +77,18 @@ void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y
 // k_head.hip
 void launch_lm_merge(hipStream_t s, const float4* part, int n_parts, int rows, float tau,
                      void* stats);
+// Sampler options: confidence (dg_confidence), adaptive stopping threshold
+// (0 = off), the per-slot argmax of the previous step [slots][C] (read, then
+// overwritten), which requests of the batch have one (bit r), and the
+// optional per-request stop flags.
+struct SamplerMode {
+  int confidence;
+  float stop_entropy;
+  int32_t* prev_argmax;
+  uint32_t prev_valid;
+  int32_t* stop;
+};
 void launch_sampler(hipStream_t s, void* stats, int n_req, int C, int V, int32_t* canvas,
                     uint8_t* committed, int step, int k_s, float tau, const uint64_t* seeds_host,
-                    const int32_t* blocks_host, const int32_t* slots_host, void* stats_out);
+                    const int32_t* blocks_host, const int32_t* slots_host, void* stats_out,
+                    const SamplerMode& mode);

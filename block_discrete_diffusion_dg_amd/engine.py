@@ -178,7 +178,9 @@ class Engine:
     def set_cache_len(self, req: int, n: int):
         self._check(self.lib.dg_set_cache_len(self.ctx, req, n))
 
-    def _args(self, reqs, canvas, committed, step, n_steps, seeds, blocks, stats):
+    def _args(self, reqs, canvas, committed, step, n_steps, seeds, blocks, stats,
+              confidence: str = "prob", stop_entropy: float = 0.0,
+              stop: Optional[torch.Tensor] = None):
         n = len(reqs)
         a = B.DGStepArgs()
         a.n_req = n
@@ -195,6 +197,11 @@ class Engine:
         a.d_committed = committed.data_ptr()
         a.step, a.n_steps = step, n_steps
         a.d_stats = _ptr(stats)
+        a.confidence = B.CONFIDENCE[confidence]
+        a.stop_entropy = float(stop_entropy)
+        if stop is not None:
+            assert stop.dtype == torch.int32 and stop.is_cuda and stop.numel() >= n
+        a.d_stop = _ptr(stop)
         return a
 
     # ------------------------------------------------------------------ the calls
@@ -207,8 +214,12 @@ class Engine:
         self._check(self.lib.dg_init_canvas(self.ctx, _stream(), ctypes.byref(a)))
 
     def denoise_step(self, reqs, canvas, committed, step, n_steps, seeds, blocks,
-                     stats: Optional[torch.Tensor] = None):
-        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats)
+                     stats: Optional[torch.Tensor] = None, confidence: str = "prob",
+                     stop_entropy: float = 0.0, stop: Optional[torch.Tensor] = None):
+        """One denoising step; `stop` (device int32 [n_req]) receives 1 where
+        adaptive stopping ended the request's block at this step."""
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
+                       stop_entropy, stop)
         self._check(self.lib.dg_denoise_step(self.ctx, _stream(), ctypes.byref(a)))
 
     def commit_block(self, reqs, canvas):
@@ -252,8 +263,10 @@ class Engine:
                                              ("idx", "w", "cnt", "off", "perm", "slot")]))
         return out
 
-    def test_head(self, reqs, h, canvas, committed, step, n_steps, seeds, blocks, stats=None):
-        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats)
+    def test_head(self, reqs, h, canvas, committed, step, n_steps, seeds, blocks, stats=None,
+                  confidence: str = "prob", stop_entropy: float = 0.0, stop=None):
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
+                       stop_entropy, stop)
         self._check(self.lib.dg_test_head(self.ctx, _stream(), ctypes.byref(a), h.data_ptr()))
 
 
@@ -262,7 +275,7 @@ def stats_fields(stats: torch.Tensor) -> Dict[str, torch.Tensor]:
     s = stats.cpu()
     f = s.view(torch.float32)
     return dict(max_logit=f[:, 0], log_z=f[:, 1], held_logit=f[:, 2], conf=f[:, 3],
-                argmax=s[:, 4], accepted=s[:, 5])
+                argmax=s[:, 4], accepted=s[:, 5], entropy=f[:, 6])
 
 
 def gpu_weights(cfg: ModelConfig, model_seed: int = 0, gain_jitter: float = 0.0,

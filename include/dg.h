@@ -103,8 +103,14 @@ typedef struct dg_row_stats {
   float conf;        /* c_i = log p_tau(candidate) */
   int32_t argmax;    /* lowest v with L_iv = M_i */
   int32_t accepted;  /* 1 if position i is in the accepted set */
-  int32_t pad[2];
+  float entropy;     /* H_i = -sum_v p_iv ln p_iv, p_i = softmax(L_i / tau_s), nats */
+  int32_t pad;
 } dg_row_stats;
+
+/* How the sampler ranks canvas positions (explainer §3.3):
+ *   DG_CONF_PROB     c_i = log p_tau(y_i), the candidate's log-probability;
+ *   DG_CONF_ENTROPY  c_i = -H_i, low-entropy positions first. */
+typedef enum { DG_CONF_PROB = 0, DG_CONF_ENTROPY = 1 } dg_confidence;
 
 /* Arguments of dg_init_canvas / dg_denoise_step.
  *   n_req        number of requests in the batch (rows = n_req * canvas)
@@ -115,6 +121,18 @@ typedef struct dg_row_stats {
  *   seed         host uint64 [n_req]: Philox key per request
  *   block        host int32 [n_req]: block index (Philox counter word 2)
  *   d_stats      optional device dg_row_stats [n_req][canvas] (NULL = none)
+ *   confidence   dg_confidence (0 = DG_CONF_PROB; another value: DG_EINVAL)
+ *   stop_entropy adaptive stopping threshold in nats (explainer §3.3);
+ *                <= 0 disables it (NaN: DG_EINVAL). A request's block stops at this step when
+ *                the mean of H_i over its canvas is below the threshold and
+ *                every position's argmax equals its argmax at the previous
+ *                step of the block; the step then accepts every position.
+ *   d_stop       optional device int32 [n_req]: 1 where the block stopped at
+ *                this step, else 0 (NULL = not reported)
+ * The library keeps each request slot's argmax of its last step in the
+ * workspace. It counts as the previous step only for steps of the same block:
+ * after dg_create, dg_init_canvas, dg_commit_block or dg_reset of a slot, the
+ * slot's next step never stops.
  * Re-noise ids come from Philox4x32-10 (Salmon et al., SC'11) with
  * key = (low, high 32 bits of seed[r]) and counter = (i, step, block[r],
  * req[r]) for canvas position i of request r; id = (word0 * vocab) >> 32.
@@ -128,6 +146,9 @@ typedef struct dg_step_args {
   const uint64_t *seed;
   const int32_t *block;
   dg_row_stats *d_stats;
+  int32_t confidence;
+  float stop_entropy;
+  int32_t *d_stop;
 } dg_step_args;
 
 typedef struct dg_ctx dg_ctx;
@@ -187,11 +208,12 @@ dg_status dg_init_canvas(dg_ctx *ctx, void *stream, const dg_step_args *a);
  *   RMSNorm, router top-k softmax, token->expert permutation, grouped SwiGLU
  *   experts plus the shared expert, weighted combine + residual;
  *   final RMSNorm; tied LM head reduced per row to (max, argmax, log-sum-exp,
- *   held-token logit) without materialising the logits; sampler:
+ *   entropy, held-token logit) without materialising the logits; sampler:
  *     tau_s = tau_first + (tau_last - tau_first) * (step-1)/(n_steps-1),
  *     k_s   = floor(step * canvas / n_steps),
  *     candidate y_i = x_i if committed else argmax_i,
- *     c_i = (L_i[y_i] - M_i)/tau_s - log Z_i,
+ *     c_i = (L_i[y_i] - M_i)/tau_s - log Z_i  (or -H_i, see dg_confidence),
+ *     k_s = canvas instead when the block stops early (stop_entropy),
  *     the k_s positions of highest c_i (ties: lower i) take y_i and are marked
  *     committed; all others get a fresh uniform id and are cleared.
  * The canvas K/V rows are written to cache rows [len, len+C) as scratch; the

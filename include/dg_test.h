@@ -39,7 +39,9 @@ extern "C" {
  *                                    64-column tile (output projection)
  *   zpart    fp32 [4][rows16][E]     router logits per quarter of d
  *                                    (rows16 = rows rounded up to 16)
- *   sync     int32 [256]             router row-block arrival counters   */
+ *   sync     int32 [256]             router row-block arrival counters
+ *   prev     int32 [max_requests][canvas]  argmax of each slot's last
+ *                                    denoising step */
 /* Word of the items buffer that counts expert-kernel waits which ran out of
  * their poll budget instead of seeing their input published. A correct run
  * leaves it unchanged; the library never resets it. */
@@ -55,7 +57,7 @@ extern "C" {
 
 typedef struct dg_ws_layout {
   size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
-      slot, hid, hid_s, y, lm_part, stats, ids, ss, zpart, sync, total;
+      slot, hid, hid_s, y, lm_part, stats, ids, ss, zpart, sync, prev, total;
 } dg_ws_layout;
 
 dg_status dg_workspace_layout(const dg_config *cfg, dg_ws_layout *out);

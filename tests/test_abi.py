@@ -63,6 +63,34 @@ def test_buffer_sizes(lib):
     assert ctypes.sizeof(B.DGRowStats) == 32
 
 
+def test_binding_structs_match_the_c_header(tmp_path):
+    """The ctypes mirrors of the public structs have the header's field
+    offsets and sizes (a plain C compiler reads dg.h / dg_test.h)."""
+    structs = {"dg_config": B.DGConfig, "dg_row_stats": B.DGRowStats, "dg_step_args": B.DGStepArgs,
+               "dg_weights": B.DGWeights, "dg_layer_weights": B.DGLayerWeights,
+               "dg_ws_layout": B.DGWsLayout}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dg_test.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
 @pytest.mark.parametrize("field,value", [("head_dim", 96), ("d_model", 1000), ("n_experts", 136),
                                          ("top_k", 9), ("vocab", 1000), ("canvas", 24),
                                          ("max_rows", 100), ("n_q_heads", 12), ("max_ctx", 300),
@@ -127,6 +155,15 @@ def test_argument_and_capacity_errors_launch_nothing(lib):
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
         a.step = 5
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        a.step = 2
+        a.confidence = 2  # neither DG_CONF_PROB nor DG_CONF_ENTROPY
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        assert b"confidence" in lib.dg_last_error(h)
+        a.confidence = B.CONFIDENCE["entropy"]
+        a.stop_entropy = float("nan")
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        assert b"NaN" in lib.dg_last_error(h)
+        a.stop_entropy = 0.0
         a.n_req = 3  # 3 * 32 rows > max_rows 64
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_ECAPACITY
         assert lib.dg_reset(h, 0) == B.DG_OK and lib.dg_cache_len(h, 0) == 0

@@ -137,6 +137,8 @@ def test_head_statistics_and_sampler(model, n_req):
     assert np.abs(st["max_logit"].double().numpy() - M1).max() < 1e-5 * scale
     assert np.abs(st["held_logit"].double().numpy() - gx1).max() < 1e-5 * scale
     assert np.abs(st["log_z"].double().numpy() - logZ1).max() < 1e-4
+    H1 = om.row_entropy(L_u, tau)
+    assert np.abs(st["entropy"].double().numpy() - H1).max() < 1e-4 * max(1.0, H1.max())
     top2 = np.sort(L_u, axis=1)[:, -2:]
     clear = (top2[:, 1] - top2[:, 0]) > 1e-5 * scale
     assert np.array_equal(st["argmax"].numpy()[clear], a1[clear])
@@ -150,6 +152,7 @@ def test_head_statistics_and_sampler(model, n_req):
     assert np.abs((st["max_logit"].double().numpy() / tau + st["log_z"].double().numpy())
                   - (M / tau + logZ)).max() <= REL_TOL * big / tau
     assert np.all(L[np.arange(rows), st["argmax"].numpy()] >= M - REL_TOL * big)
+    assert np.abs(st["entropy"].double().numpy() - om.row_entropy(L, tau)).max() <= REL_TOL * big / tau
 
     # (3) sampler: the oracle's sampler on the GPU's own statistics, per request
     x_new = x_dev.cpu().numpy()
@@ -169,6 +172,64 @@ def test_head_statistics_and_sampler(model, n_req):
             assert np.array_equal(x_new[sl], xo)
         noise = uniform_ids(seeds[r], np.arange(C), step, blocks[r], r, model.vocab)
         assert np.array_equal(x_new[sl][~acc_gpu], noise[~acc_gpu])
+
+
+@pytest.mark.parametrize("model,n_req", [(synth.TINY, 2), (synth.FULL, 1)])
+def test_entropy_confidence_and_adaptive_stop(model, n_req):
+    """Entropy ranking on the GPU's own statistics matches the oracle's
+    sampler bit for bit; the stop fires only when the previous step of the
+    same block had the same argmax everywhere and the mean entropy is below
+    the threshold, and a stopped step accepts every position."""
+    say(f"[entropy] V={model.vocab} n_req={n_req}")
+    C = model.canvas
+    rows = n_req * C
+    eng, hw = _zero_layer_engine(model, max_rows=rows, max_requests=n_req)
+    step, n_steps = 3, 8
+    h, canvas, committed = _head_case(model, n_req, step, n_steps, seed=5)
+    h = h.cuda()
+    reqs = list(range(n_req))
+    seeds, blocks = [21 + r for r in reqs], [1] * n_req
+    tau = om.tau_at(step, n_steps, model.tau_first, model.tau_last)
+    x_np, m_np = canvas.numpy().astype(np.int64), committed.numpy()
+    stop = torch.full((n_req,), -7, dtype=torch.int32, device="cuda")
+
+    def run(thr):
+        x_dev, m_dev = canvas.cuda(), committed.cuda()
+        stats = eng.new_stats(n_req)
+        eng.test_head(reqs, h, x_dev, m_dev, step, n_steps, seeds, blocks, stats, confidence="entropy",
+                      stop_entropy=thr, stop=stop)
+        torch.cuda.synchronize()
+        return x_dev.cpu().numpy(), m_dev.cpu().numpy(), stats_fields(stats), stop.cpu().numpy().copy()
+
+    # first step of the block: no previous argmax, never stops
+    x1, m1, st, stop1 = run(1e9)
+    assert np.array_equal(stop1, np.zeros(n_req))
+    H = st["entropy"].double().numpy()
+    k_s = om.commit_count(step, n_steps, C)
+    for r in reqs:
+        sl = slice(r * C, (r + 1) * C)
+        xo, mo, c, acc = om.sample(x_np[sl], m_np[sl], st["max_logit"].double().numpy()[sl],
+                                   st["argmax"].numpy()[sl], st["log_z"].double().numpy()[sl],
+                                   st["held_logit"].double().numpy()[sl], tau, step, n_steps, seeds[r],
+                                   blocks[r], r, model.vocab, confidence="entropy", H=H[sl])
+        assert np.array_equal(st["conf"].double().numpy()[sl], c)
+        assert np.array_equal(st["accepted"].numpy()[sl].astype(bool), acc)
+        assert np.array_equal(x1[sl], xo) and np.array_equal(m1[sl], mo) and mo.sum() == k_s
+    mean_h = H.reshape(n_req, C).astype(np.float32).mean(1)
+    # the same rows again: unchanged argmax, but entropy above the threshold
+    _, m2, _, stop2 = run(float(mean_h.min()) * 0.5)
+    assert np.array_equal(stop2, np.zeros(n_req)) and m2.sum() == n_req * k_s
+    # unchanged argmax and a threshold above the mean: the block stops
+    x3, m3, st3, stop3 = run(float(mean_h.max()) * 1.01)
+    assert np.array_equal(stop3, np.ones(n_req)) and m3.all() and st3["accepted"].numpy().all()
+    y = np.where(m_np.astype(bool), x_np, st3["argmax"].numpy())
+    assert np.array_equal(x3, y)
+    # a new block forgets the previous argmax
+    xi = torch.empty(rows, dtype=torch.int32, device="cuda")
+    mi = torch.empty(rows, dtype=torch.uint8, device="cuda")
+    eng.init_canvas(reqs, xi, mi, seeds, blocks)
+    _, _, _, stop4 = run(1e9)
+    assert np.array_equal(stop4, np.zeros(n_req))
 
 
 def test_init_canvas_matches_philox():

@@ -25,7 +25,12 @@ def _oracle_request(eng, cfg, slot, length):
     return req
 
 
-def test_tiny_block_loop_parity():
+@pytest.mark.parametrize("confidence,stop_entropy", [("prob", 0.0), ("entropy", 1e9)])
+def test_tiny_block_loop_parity(confidence, stop_entropy):
+    """With entropy confidence and a threshold every mean entropy is under,
+    adaptive stopping reduces to "the argmax did not change since the
+    previous step": both sides must agree on it wherever the argmax is
+    clear of ties."""
     wl = synth.WORKLOADS["tiny"]
     cfg, P, S = wl.model, wl.prefix, wl.n_steps
     C = cfg.canvas
@@ -49,22 +54,32 @@ def test_tiny_block_loop_parity():
     x0, m0 = om.init_canvas(seed, block, 0, C, cfg.vocab)
     assert np.array_equal(x.cpu().numpy(), x0) and not m.cpu().numpy().any()
 
+    a_prev = None
+    stop = torch.zeros(1, dtype=torch.int32, device="cuda")
     for s in range(1, S + 1):
-        say(f"[tiny] step {s}")
+        say(f"[tiny] {confidence} step {s}")
         x_in = x.cpu().numpy().astype(np.int64)
         m_in = m.cpu().numpy()
         stats = eng.new_stats(1)
-        eng.denoise_step([0], x, m, s, S, [seed], [block], stats)
+        eng.denoise_step([0], x, m, s, S, [seed], [block], stats, confidence=confidence,
+                         stop_entropy=stop_entropy, stop=stop)
         torch.cuda.synchronize()
         st = stats_fields(stats)
         keep = {}
-        xo, mo = om.denoise_step(hw, cfg, gpu_req, x_in, m_in, s, S, seed, block, 0, keep)
+        # teacher-forced: the oracle compares with the GPU's previous argmax
+        xo, mo = om.denoise_step(hw, cfg, gpu_req, x_in, m_in, s, S, seed, block, 0, keep,
+                                 confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev)
         big = np.abs(keep["logits"]).max()
         assert max_rel(st["max_logit"], keep["M"]) <= REL_TOL
         clear = np.array([tie_gap_ok(keep["logits"][i], 1, 2 * REL_TOL * big) for i in range(C)])
         assert np.array_equal(st["argmax"].numpy()[clear], keep["a"][clear])
+        assert np.abs(st["entropy"].double().numpy() - keep["H"]).max() <= REL_TOL * big / keep["tau"]
         assert np.abs(st["conf"].double().numpy() - keep["c"]).max() <= REL_TOL * big / keep["tau"] * 4
-        k_s = om.commit_count(s, S, C)
+        stopped = bool(stop.item())
+        if clear.all():
+            assert stopped == keep["stop"]
+        a_prev = st["argmax"].numpy().astype(np.int64)
+        k_s = C if stopped else om.commit_count(s, S, C)
         acc = st["accepted"].numpy().astype(bool)
         assert acc.sum() == k_s == m.cpu().numpy().sum()
         if tie_gap_ok(keep["c"], k_s, REL_TOL * big / keep["tau"] * 4) and clear.all():
@@ -73,6 +88,8 @@ def test_tiny_block_loop_parity():
         # the KV cache is only read by a denoising step
         assert torch.equal(eng.kv_view()[0, :, :, :, :P], kv_prefix)
         assert eng.cache_len(0) == P
+        if stopped:
+            break
     assert m.cpu().numpy().all()
 
     say("[tiny] commit")
