@@ -21,6 +21,12 @@ Parity status per function (what pins each, see tests/test_oracle_pins.py):
                   unless re-noised, last step accepts everything)
   whole step      zero-layer model reduces to RMSNorm(E[x]) E^T; causal
                   consistency of prefill vs prefill + commit
+  row_entropy     closed forms (uniform, two tokens, k-way ties); scipy's
+                  entropy of the softmax; temperature monotonicity
+  adaptive_stop   its four cases; a stopped step accepts every position
+  fp8 (E4M3)      torch's float8_e4m3fn decode and encode; round trip of
+                  every finite code; ties to even; row-exponent minimality;
+                  half-ulp error bound
   metrics         the pages' worked TPF/TPS example
 Fidelity to the trained DiffusionGemma model: parity unpinned (no weights).
 """

@@ -14,6 +14,7 @@ import torch
 import torch.nn.functional as F
 
 from block_discrete_diffusion_dg_amd import synth
+from oracle import fp8 as om_fp8
 from oracle import model as om
 from tests.test_oracle_pins import _sdpa_reference
 
@@ -75,6 +76,28 @@ def _pin_adaptive_stop():
     a = np.array([3, 4])
     return (om.adaptive_stop(H, a, a.copy(), 1.0) and not om.adaptive_stop(H, a, np.array([3, 5]), 1.0)
             and not om.adaptive_stop(H, a, a.copy(), 0.375) and not om.adaptive_stop(H, a, None, 1.0))
+
+
+def _pin_e4m3_encode():
+    v = np.array([1 + 1 / 16, 1 + 3 / 16, 2.0 ** -9 * 1.5, 3.3, -0.07, 200.0], np.float32)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.array_equal(om_fp8.e4m3_encode(v), want)
+
+
+def _pin_row_exponent():
+    return om_fp8.row_exponent([448.0, 449.0, 224.0]).tolist() == [0, 1, -1]
+
+
+def _bad_e4m3_encode(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    out = _real_fp8["e4m3_encode"](np.sign(v) * np.minimum(a * (1 + 2.0 ** -12), 448.0))  # ties rounded up
+    return out
+
+
+def _bad_row_exponent(amax):
+    f, x = np.frexp(np.asarray(amax, np.float64))
+    return (x - 9).astype(np.int64)  # ignores a mantissa above 448's
 
 
 def _pin_rms_norm():
@@ -143,6 +166,8 @@ def _bad_rms_norm(x, gain, eps):
     return x / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)  # gain dropped
 
 
+_real_fp8 = {"e4m3_encode": om_fp8.e4m3_encode}
+
 _real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
          "row_entropy": om.row_entropy}
 
@@ -164,4 +189,17 @@ CASES = [
 def test_planted_mistake_is_caught(monkeypatch, name, bad, pin):
     assert pin(), "pin must hold for the real oracle"
     monkeypatch.setattr(om, name, bad)
+    assert not pin(), "pin failed to catch the planted mistake"
+
+
+FP8_CASES = [
+    ("e4m3_encode", _bad_e4m3_encode, _pin_e4m3_encode),
+    ("row_exponent", _bad_row_exponent, _pin_row_exponent),
+]
+
+
+@pytest.mark.parametrize("name,bad,pin", FP8_CASES, ids=[f"{c[0]}:{c[1].__name__}" for c in FP8_CASES])
+def test_planted_fp8_mistake_is_caught(monkeypatch, name, bad, pin):
+    assert pin(), "pin must hold for the real oracle"
+    monkeypatch.setattr(om_fp8, name, bad)
     assert not pin(), "pin failed to catch the planted mistake"
