@@ -31,6 +31,14 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def fp8_expert_bytes(cfg, touched_experts):
+    """Algorithmic bytes of one expert-kernel launch with FP8 expert weights:
+    one byte per weight plus a 4-byte scale per weight row, for the touched
+    experts and the shared expert."""
+    d, F, Fs = cfg.d_model, cfg.d_expert, cfg.d_shared
+    return touched_experts * (3 * F * d + (2 * F + d) * 4) + 3 * Fs * d + (2 * Fs + d) * 4
+
+
 def algorithmic_model(cfg, prefix, rows, touched_experts):
     """Bytes and flops per kernel class (per launch) that one denoising step
     must move / do.
@@ -125,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="full", choices=["full", "long", "batch", "tiny", "one_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--no-fp8-variant", action="store_true",
+                    help="skip the extra measurement with FP8 expert weights")
     ap.add_argument("--copy-probe-mib", type=int, default=512,
                     help="after the run, copy this many MiB device-to-device with a plain copy "
                          "kernel (reference for hardware byte counters)")
@@ -303,7 +313,64 @@ def main():
         # reaches on this GPU in the same run
         out["roofline"]["peak_measured"] = round(copy_gbs, 1)
         out["roofline"]["frac_measured"] = round(out["roofline"]["achieved"] / copy_gbs, 4)
+    if not args.no_fp8_variant and args.workload == "full":
+        out["variants"] = {"fp8_experts": fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
+                                                      blocks, canvas0, dev)}
     print(json.dumps(out), flush=True)
+
+
+def fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds, blocks, canvas0, dev):
+    """The same step with the expert matrices stored as FP8 (E4M3 codes and
+    power-of-two row scales, quantised on the GPU from the same bf16
+    weights): a separate variant at reduced weight precision, reported
+    beside the bf16 headline, never in its place."""
+    import torch
+    from block_discrete_diffusion_dg_amd import synth
+    from block_discrete_diffusion_dg_amd.engine import Engine
+    P, S, C = wl.prefix, wl.n_steps, cfg.canvas
+    rows = len(reqs) * C
+    eng = Engine(cfg, layers, embed, final, max_ctx=P + 2 * C, max_requests=len(reqs), max_rows=rows,
+                 expert_format="fp8")
+    for r in reqs:
+        eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
+    x = torch.from_numpy(canvas0).to(dev)
+    m = torch.zeros(rows, dtype=torch.uint8, device=dev)
+
+    def run(n, start):
+        for i in range(n):
+            eng.denoise_step(reqs, x, m, (start + i) % S + 1, S, seeds, blocks)
+
+    run(args.warmup, 0)
+    moe0 = eng.moe_counters()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(args.steps, args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    eng.timing(True)
+    moe1 = eng.moe_counters()
+    run(args.steps, args.warmup + args.steps)
+    stages = eng.timing_read()
+    moe2 = eng.moe_counters()
+    eng.timing(False)
+    if moe2["spin_timeouts"] != moe0["spin_timeouts"]:
+        raise RuntimeError("expert kernel waits ran out during the FP8 steps")
+    touched = (moe2["touched_total"] - moe1["touched_total"]) / max(1, moe2["permute_calls"] - moe1["permute_calls"])
+    ex_ms = stages["experts"][0] / max(1, stages["experts"][1])
+    b = fp8_expert_bytes(cfg, touched)
+    log(f"fp8 experts: {ms:.3f} ms/step, expert launch {ex_ms * 1e3:.1f} us")
+    eng.close()
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
+            "canvas_tok_s": round(1e3 / ms * rows, 1),
+            "weights": "expert matrices E4M3 + per-row power-of-two scales; everything else bf16",
+            "experts_kernel": {"bound": "hbm", "bytes_per_launch": round(b), "avg_launch_ms": round(ex_ms, 4),
+                               "achieved": round(b / (ex_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "peak": HBM_PEAK / 1e9, "frac": round(b / (ex_ms * 1e-3) / HBM_PEAK, 4),
+                               "touched_experts_per_layer": round(touched, 2)},
+            "stages_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}}
 
 
 if __name__ == "__main__":

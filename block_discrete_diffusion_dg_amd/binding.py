@@ -24,7 +24,11 @@ class DGConfig(ctypes.Structure):
     _fields_ = [(n, c_i32) for n in ("n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
                                      "n_experts", "top_k", "d_expert", "d_shared", "vocab",
                                      "canvas", "max_ctx", "max_requests", "max_rows")] + \
-               [(n, c_f32) for n in ("rms_eps", "rope_theta", "tau_first", "tau_last")]
+               [(n, c_f32) for n in ("rms_eps", "rope_theta", "tau_first", "tau_last")] + \
+               [("expert_format", c_i32)]
+
+
+WEIGHT_FORMAT = {"bf16": 0, "fp8": 1}
 
 
 LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "w_gate", "w_up", "w_down",
@@ -34,8 +38,14 @@ LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "w_gate", "
 PACKED_FIELDS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
 
 
+# Expert matrices (bf16 fragment-major, or FP8 codes with row scales) and the
+# fields holding their FP8 row scales, in the same order.
+EXPERT_FIELDS = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+SCALE_FIELDS = ("s_gate", "s_up", "s_down", "ss_gate", "ss_up", "ss_down")
+
+
 class DGLayerWeights(ctypes.Structure):
-    _fields_ = [(n, c_vp) for n in LAYER_FIELDS]
+    _fields_ = [(n, c_vp) for n in LAYER_FIELDS + SCALE_FIELDS]
 
 
 class DGWeights(ctypes.Structure):
@@ -77,6 +87,7 @@ SIGNATURES = {
                           ctypes.POINTER(c_vp)]),
     "dg_destroy": (None, [c_vp]),
     "dg_pack_weight": (c_i32, [c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
+    "dg_quantize_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32]),
     "dg_init_canvas": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
     "dg_denoise_step": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),

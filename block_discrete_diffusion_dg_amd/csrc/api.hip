@@ -24,7 +24,8 @@ int router_sync_words(int max_rows) { return div_up(max_rows, 16) + 1; }
 
 struct LayerW {
   const bf16_t *attn_norm, *w_qkv, *w_o, *moe_norm, *w_router;
-  const bf16_t *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
+  const void *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;  // bf16 or FP8 codes
+  ExpertScales fp8;                                                // FP8 row scales
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -94,6 +95,8 @@ const char* check_config(const dg_config& c) {
   if (c.max_ctx < 2 * c.canvas || c.max_ctx % 32) return "max_ctx must be a multiple of 32 holding at least two blocks";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.tau_first > 0.f) || !(c.tau_last > 0.f))
     return "rms_eps >= 0, rope_theta > 0 and temperatures > 0 required";
+  if (c.expert_format != DG_WEIGHTS_BF16 && c.expert_format != DG_WEIGHTS_FP8)
+    return "expert_format must be DG_WEIGHTS_BF16 or DG_WEIGHTS_FP8";
   return nullptr;
 }
 
@@ -229,7 +232,8 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
         launch_moe_experts(s, u, rows, d, g.d_expert, g.d_shared, g.n_experts, g.top_k, c->buf<int32_t>(L.perm),
                            c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<float>(L.w),
                            c->buf<int32_t>(L.wslot), items, w.w_gate, w.w_up, w.w_down, w.ws_gate, w.ws_up,
-                           w.ws_down, c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s), y, ys));
+                           w.ws_down, g.expert_format == DG_WEIGHTS_FP8 ? &w.fp8 : nullptr,
+                           c->buf<bf16_t>(L.hid), c->buf<bf16_t>(L.hid_s), y, ys));
   STAGE(DG_STAGE_COMBINE, launch_moe_combine(s, h, ys, y, c->buf<int32_t>(L.slot), rows, d, g.top_k,
                                              next_gain, g.rms_eps, u));
 }
@@ -365,15 +369,20 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
     const dg_layer_weights& s = w->layers[l];
     const void* ptrs[] = {s.attn_norm, s.w_qkv, s.w_o, s.moe_norm, s.w_router, s.w_gate,
                           s.w_up, s.w_down, s.ws_gate, s.ws_up, s.ws_down};
-    for (const void* p : ptrs)
-      if (!p) {
-        delete c;
-        return DG_EINVAL;
-      }
+    const void* scales[] = {s.s_gate, s.s_up, s.s_down, s.ss_gate, s.ss_up, s.ss_down};
+    bool ok = true;
+    for (const void* p : ptrs) ok = ok && p;
+    if (cfg->expert_format == DG_WEIGHTS_FP8)
+      for (const void* p : scales) ok = ok && p;
+    if (!ok) {
+      delete c;
+      return DG_EINVAL;
+    }
     c->layers[l] = LayerW{(const bf16_t*)s.attn_norm, (const bf16_t*)s.w_qkv, (const bf16_t*)s.w_o,
-                          (const bf16_t*)s.moe_norm,  (const bf16_t*)s.w_router, (const bf16_t*)s.w_gate,
-                          (const bf16_t*)s.w_up,      (const bf16_t*)s.w_down,   (const bf16_t*)s.ws_gate,
-                          (const bf16_t*)s.ws_up,     (const bf16_t*)s.ws_down};
+                          (const bf16_t*)s.moe_norm,  (const bf16_t*)s.w_router, s.w_gate,
+                          s.w_up,                     s.w_down,                   s.ws_gate,
+                          s.ws_up,                    s.ws_down,
+                          ExpertScales{s.s_gate, s.s_up, s.s_down, s.ss_gate, s.ss_up, s.ss_down}};
   }
   c->kv.base = (bf16_t*)d_kv_cache;
   c->kv.head_stride = (int64_t)cfg->max_ctx * cfg->head_dim;
@@ -396,6 +405,16 @@ dg_status dg_pack_weight(void* stream, const void* d_src, void* d_dst, int64_t n
   const int64_t bytes = n * (int64_t)k * 2;
   if (s0 < d0 + bytes && d0 < s0 + bytes) return DG_EINVAL;  // overlapping buffers
   launch_pack((hipStream_t)stream, (const bf16_t*)d_src, (bf16_t*)d_dst, n, k);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
+}
+
+dg_status dg_quantize_fp8(void* stream, const void* d_src, void* d_dst, float* d_scale, int64_t n, int32_t k) {
+  if (!d_src || !d_dst || !d_scale || n <= 0 || k <= 0 || n % 16 != 0 || k % 64 != 0) return DG_EINVAL;
+  const char* s0 = (const char*)d_src;
+  const char* d0 = (const char*)d_dst;
+  const int64_t src_bytes = n * (int64_t)k * 2, dst_bytes = n * (int64_t)k;
+  if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return DG_EINVAL;  // overlapping buffers
+  launch_quant_fp8((hipStream_t)stream, (const bf16_t*)d_src, (uint8_t*)d_dst, d_scale, n, k);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
 }
 

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void qkv_kernel(const bf16_t* __restrict__ u, 
   const int64_t r0 = (int64_t)head * dh + pw % half;  // first row of the wave's block
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 a0[DMT], a1[DMT];
-  stream_tile<DMT, true, DENSE_DW, DENSE_DW>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, d, a0, a1, lds);
+  stream_tile<DMT, true, DENSE_DW, DENSE_DW>(u, d, nullptr, row0, nrows, w + r0 * d, w + (r0 + half) * d, nullptr,
+                                             nullptr, d, a0, a1, lds);
   const bool rotate = head < p.Hq + p.Hkv;
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
@@ -192,7 +193,8 @@ __global__ __launch_bounds__(256) void resid_kernel(const bf16_t* __restrict__ a
   const int col0 = nt * 64 + wave * 16, col = col0 + l16;
   const int row0 = mc * T::CH, nrows = min(T::CH, rows - row0);
   f32x4 acc[DMT], unused[DMT];
-  stream_tile<DMT, false, DENSE_DW, DENSE_DW>(a, K, nullptr, row0, nrows, w + (int64_t)col0 * K, nullptr, K, acc, unused, lds);
+  stream_tile<DMT, false, DENSE_DW, DENSE_DW>(a, K, nullptr, row0, nrows, w + (int64_t)col0 * K, nullptr, nullptr,
+                                              nullptr, K, acc, unused, lds);
 #pragma unroll
   for (int mt = 0; mt < DMT; ++mt)
 #pragma unroll

@@ -118,7 +118,65 @@ __global__ void pack_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__
   }
 }
 
+// OCP E4M3 code of v (finite, |v| <= 448), rounded to nearest with ties to
+// even: below 2^-6 the representable values are multiples of 2^-9 (a result
+// of 8 is the smallest normal number, whose code is also 8); in
+// [2^E, 2^(E+1)) they are multiples of 2^(E-3). Sign bit from the value.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = __float_as_uint(v) >> 31;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    int x;
+    (void)frexpf(a, &x);  // a = f * 2^x with f in [0.5, 1)
+    int E = x - 1;
+    float q = rintf(ldexpf(a, 3 - E));  // in [8, 16]; exact scaling, then round half to even
+    if (q == 16.0f) {
+      E += 1;
+      q = 8.0f;
+    }
+    code = ((uint32_t)(E + 7) << 3) | ((uint32_t)q - 8u);
+  }
+  return (sign << 7) | code;
+}
+
+// FP8 weights from a row-major bf16 matrix src [n][k], one wave per row:
+// scale[row] = 2^e for the smallest integer e with max_k |src| <= 448 * 2^e
+// (e = 0 for a zero row; 448 = 0.875 * 2^9), and dst holds the E4M3 code of
+// src * 2^-e (exact scaling) of every element at its pack8_index position.
+// Each lane encodes 8 consecutive elements (8 contiguous bytes of dst).
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                        float* __restrict__ scale, int64_t n, int k) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= n) return;  // wave-uniform
+  const bf16_t* r = src + row * k;
+  float amax = 0.f;
+  for (int c = lane; c < k; c += 64) amax = fmaxf(amax, fabsf(bf2f(r[c])));
+  amax = wave_max(amax);
+  int e = 0;
+  if (amax > 0.f) {
+    int x;
+    const float f = frexpf(amax, &x);
+    e = f <= 0.875f ? x - 9 : x - 8;
+  }
+  if (lane == 0) scale[row] = ldexpf(1.0f, e);
+  for (int c0 = lane * 8; c0 < k; c0 += 512) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j >> 2] |= e4m3_code(ldexpf(bf2f(r[c0 + j]), -e)) << (8 * (j & 3));
+    *reinterpret_cast<u32x2*>(dst + pack8_index(row, c0, k)) = u32x2{w[0], w[1]};
+  }
+}
+
 }  // namespace
+
+void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k) {
+  const int64_t blocks = (n + 3) / 4;
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, scale, n, k);
+}
 
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k) {
   const int64_t pieces = n * (k / 8);

@@ -6,6 +6,7 @@
 // cut into chunks of CH = 16*MT rows, and every (group, column tile, row
 // chunk) is one work item, of one of two kinds:
 //   gate/up:  hid[slot][f] = silu(x W_gate[f]) * (x W_up[f])   (bf16; 64 columns f)
+//   (weights bf16, or FP8 codes with per-row scales widened to bf16 in the tile)
 //   down:     y[slot][c]   = w_slot * (hid[slot] W_down[c])     (fp32, 128 columns c;
 //                                                              shared: ys[t][c])
 // The permutation kernel writes the exclusive item offsets of both kinds and
@@ -38,10 +39,19 @@ struct MoeArgs {
   const float* wts;                 // routing weights [rows*k]
   const int32_t* widx;              // slot -> index into wts
   int32_t* items;                   // MoeItems layout
-  const bf16_t *wg, *wu, *wd, *sg, *su, *sd;  // fragment-major weights
+  const void *wg, *wu, *wd, *sg, *su, *sd;  // fragment-major weights (bf16, or FP8 codes)
+  ExpertScales sc;                          // FP8 row scales (unused for bf16)
   bf16_t *hid, *hid_s;
   float *y, *ys;
 };
+
+// Start of weight row `row` of a fragment-major matrix with K columns (rows
+// in multiples of 16): 16-row blocks are contiguous, so the block holding
+// row r starts r*K elements in.
+template <bool W8>
+__device__ __forceinline__ const void* wrow(const void* base, int64_t row, int K) {
+  return static_cast<const char*>(base) + row * K * (W8 ? 1 : 2);
+}
 
 // 16-byte store that writes through to device-coherent memory (visible to
 // every XCD once complete; no L2 write-back needed). The nop covers the
@@ -60,7 +70,7 @@ __device__ __forceinline__ int next_item(int32_t* counter, int* s_slot) {
   return __builtin_amdgcn_readfirstlane(*s_slot);  // wave-uniform: branches stay scalar
 }
 
-template <int MT>
+template <int MT, bool W8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2 : 3))) void moe_experts_kernel(MoeArgs p) {
   using T = StreamTile<MT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
@@ -96,8 +106,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
     if (up) {
       const int col0 = nt * 64 + wave * 16;
       const int ldo = shared ? p.Fs : p.F;
-      const bf16_t* W0 = shared ? p.sg : p.wg + (int64_t)e * p.F * p.d;
-      const bf16_t* W1 = shared ? p.su : p.wu + (int64_t)e * p.F * p.d;
+      // weight row of column col0 in the gate / up matrices (an expert bank
+      // is one [E*F][d] matrix)
+      const int64_t wr = shared ? col0 : (int64_t)e * p.F + col0;
+      const void* W0 = wrow<W8>(shared ? p.sg : p.wg, wr, p.d);
+      const void* W1 = wrow<W8>(shared ? p.su : p.wu, wr, p.d);
+      const float* S0 = W8 ? (shared ? p.sc.sg : p.sc.g) + wr : nullptr;
+      const float* S1 = W8 ? (shared ? p.sc.su : p.sc.u) + wr : nullptr;
       bf16_t* out = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
       // The tile takes the smallest row count that holds the chunk's rows
       // (32, 64 or CH): most chunks of a small batch hold far fewer rows than
@@ -105,8 +120,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       auto gate_up = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 ag[MTI], au[MTI];
-        stream_tile<MTI, true>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0 + (int64_t)col0 * p.d,
-                               W1 + (int64_t)col0 * p.d, p.d, ag, au, lds);
+        stream_tile<MTI, true, 2, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0, W1, S0, S1,
+                                         p.d, ag, au, lds);
         // Publish: stage the 64-column tile in LDS, write whole 128-byte row
         // segments with write-through (agent-coherent) stores, wait until they
         // complete, then move the chunk's counter. An agent-scope release fence
@@ -158,7 +173,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       __syncthreads();
       const int K = shared ? p.Fs : p.F;
       const bf16_t* A = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
-      const bf16_t* W = shared ? p.sd : p.wd + (int64_t)e * p.d * p.F;
       float* out = shared ? p.ys : p.y + (int64_t)base * p.d;
       // routing weights of the chunk's slots, staged while the weights stream
       if (threadIdx.x < T::CH)
@@ -166,11 +180,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       // 128 output columns per item: the wave owns two 16-row weight blocks;
       // the tile takes the smallest row count that holds the chunk's rows
       const int c0 = nt * 128 + wave * 32;
+      const int64_t wr = shared ? c0 : (int64_t)e * p.d + c0;  // weight row of output column c0
+      const void* Wd = shared ? p.sd : p.wd;
+      const float* Sd = W8 ? (shared ? p.sc.sd : p.sc.d) + wr : nullptr;
       auto down = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 acc0[MTI], acc1[MTI];
-        stream_tile<MTI, true>(A, K, nullptr, row0, nrows, W + (int64_t)c0 * K, W + (int64_t)(c0 + 16) * K, K, acc0,
-                               acc1, lds);
+        stream_tile<MTI, true, 2, 2, W8>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
+                                         Sd, W8 ? Sd + 16 : nullptr, K, acc0, acc1, lds);
 #pragma unroll
         for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
@@ -282,24 +299,34 @@ static int resident_blocks(Kernel kernel, int& cache) {
   }
   return cache;
 }
-static int g_resident[3];  // MT=8, MT=4, MT=2
+static int g_resident[2][3];  // [bf16, fp8][MT=8, MT=4, MT=2]
+
+template <bool W8>
+static void launch_experts_fmt(hipStream_t s, const MoeArgs& p, int ch) {
+  int* res = g_resident[W8 ? 1 : 0];
+  if (ch == 128)
+    hipLaunchKernelGGL((moe_experts_kernel<8, W8>), dim3(resident_blocks(moe_experts_kernel<8, W8>, res[0])),
+                       dim3(256), 0, s, p);
+  else if (ch == 64)
+    hipLaunchKernelGGL((moe_experts_kernel<4, W8>), dim3(resident_blocks(moe_experts_kernel<4, W8>, res[1])),
+                       dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((moe_experts_kernel<2, W8>), dim3(resident_blocks(moe_experts_kernel<2, W8>, res[2])),
+                       dim3(256), 0, s, p);
+}
 
 void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, int Fs, int E, int k,
                         const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
-                        const int32_t* widx, int32_t* items, const bf16_t* wg, const bf16_t* wu,
-                        const bf16_t* wd, const bf16_t* sg, const bf16_t* su, const bf16_t* sd, bf16_t* hid,
+                        const int32_t* widx, int32_t* items, const void* wg, const void* wu, const void* wd,
+                        const void* sg, const void* su, const void* sd, const ExpertScales* fp8, bf16_t* hid,
                         bf16_t* hid_s, float* y, float* ys) {
-  MoeArgs p{u, rows, d, F, Fs, E, perm, cnt, off, wts, widx, items, wg, wu, wd, sg, su, sd, hid, hid_s, y, ys};
+  MoeArgs p{u,  rows, d,  F,  Fs, E,  perm, cnt, off, wts, widx, items, wg, wu, wd, sg,
+            su, sd,   fp8 ? *fp8 : ExpertScales{}, hid, hid_s, y, ys};
   const int ch = moe_rows_per_chunk(rows, E, k);
-  if (ch == 128)
-    hipLaunchKernelGGL(moe_experts_kernel<8>, dim3(resident_blocks(moe_experts_kernel<8>, g_resident[0])),
-                       dim3(256), 0, s, p);
-  else if (ch == 64)
-    hipLaunchKernelGGL(moe_experts_kernel<4>, dim3(resident_blocks(moe_experts_kernel<4>, g_resident[1])),
-                       dim3(256), 0, s, p);
+  if (fp8)
+    launch_experts_fmt<true>(s, p, ch);
   else
-    hipLaunchKernelGGL(moe_experts_kernel<2>, dim3(resident_blocks(moe_experts_kernel<2>, g_resident[2])),
-                       dim3(256), 0, s, p);
+    launch_experts_fmt<false>(s, p, ch);
 }
 
 void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y, const int32_t* slot,

@@ -15,6 +15,7 @@ void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas,
                         const uint64_t* seeds_host, const int32_t* blocks_host,
                         const int32_t* slots_host);
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k);
+void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k);
 
 // k_dense.hip (weight-streaming dense projections)
 // launch_qkv also zeroes the n_sync arrival counters of the layer's router
@@ -65,10 +66,17 @@ size_t permute_lds_bytes(int rows, int E, int k);
 // k_moe.hip
 int moe_rows_per_chunk(int rows, int E, int k);
 int moe_chunk_bound(int rows, int E, int k);
+// Row scales of FP8 expert weights: g / u [E*F], d [E*d] (routed banks),
+// sg / su [Fs], sd [d] (shared expert).
+struct ExpertScales {
+  const float *g, *u, *d, *sg, *su, *sd;
+};
+// Expert weights are bf16 (fp8 == nullptr) or FP8 codes with the given row
+// scales.
 void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, int Fs, int E, int k,
                         const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
-                        const int32_t* widx, int32_t* items, const bf16_t* wg, const bf16_t* wu,
-                        const bf16_t* wd, const bf16_t* sg, const bf16_t* su, const bf16_t* sd, bf16_t* hid,
+                        const int32_t* widx, int32_t* items, const void* wg, const void* wu, const void* wd,
+                        const void* sg, const void* su, const void* sd, const ExpertScales* fp8, bf16_t* hid,
                         bf16_t* hid_s, float* y, float* ys);
 void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y,
                         const int32_t* slot, int rows, int d, int k, const bf16_t* next_gain,

@@ -21,6 +21,15 @@
 //
 // Reduction-index assignment per K-step: MFMA step q in {0,1}, lane group g
 // uses k0 + 32q + 8g .. +7 for both operands.
+//
+// FP8 weights (W8): OCP E4M3 codes in the fragment-major byte layout of
+// pack8_index, with one power-of-two scale per weight row. A lane's 16 bytes
+// of a K-step hold its row's 8 codes of MFMA step 0, then the 8 of step 1;
+// one 16-byte load per block and step brings them in, and the hardware
+// conversion widens them to bf16 times the row scale, which is exact (every
+// E4M3 value times a power of two within range is a bf16 value). The
+// products and accumulation are then those of the bf16 tile, on half the
+// weight bytes.
 #pragma once
 
 #include <type_traits>
@@ -47,6 +56,25 @@ __host__ __device__ __forceinline__ int64_t pack_index(int64_t n, int64_t k, int
          (kk & 7);
 }
 
+// Byte index of W[n][k] in the FP8 fragment-major layout of an [N][K] matrix
+// (N % 16 == 0, K % 64 == 0): block n/16 of 16 rows is contiguous (16*K
+// bytes); inside it, K-step k/64 is 1024 bytes ordered [lane][q][8] with
+// lane = 16*((k%32)/8) + n%16, q = (k%64)/32 and byte k%8.
+__host__ __device__ __forceinline__ int64_t pack8_index(int64_t n, int64_t k, int64_t K) {
+  const int64_t kk = k & 63;
+  return (n >> 4) * 16 * K + (k >> 6) * 1024 + (((kk & 31) >> 3) * 16 + (n & 15)) * 16 + (kk >> 5) * 8 + (kk & 7);
+}
+
+// Eight E4M3 codes (two words) -> eight bf16 values times scale s.
+__device__ __forceinline__ u32x4 widen_fp8(uint32_t w0, uint32_t w1, float s) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
 // acc[nb][mt][r] = sum_k A[row][k] * W_nb[n][k] for row = row0 + 16*mt +
 // 4*(lane/16) + r of the chunk and n = the lane's weight row: lane l16 of the
 // wave's nb-th 16-row block w[nb], packed fragment-major (a block is the
@@ -66,14 +94,18 @@ struct Lcm {
   static constexpr int value = A_ / gcd(A_, B_) * B_;
 };
 
-template <int MT, int NB, int DW = 2, int DA = 2>
+// W8: the blocks hold FP8 codes (pack8_index) and wsc[nb] points at the
+// block's 16 row scales; otherwise bf16 (pack_index) and wsc is unused.
+template <int MT, int NB, int DW = 2, int DA = 2, bool W8 = false>
 __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int lda,
                                               const int32_t* __restrict__ rowmap, int row0, int nrows,
-                                              const bf16_t* const (&w)[NB], int K, f32x4 (&acc)[NB][MT],
-                                              bf16_t* lds) {
+                                              const void* const (&w)[NB], const float* const (&wsc)[NB], int K,
+                                              f32x4 (&acc)[NB][MT], bf16_t* lds) {
   using T = StreamTile<MT>;
   constexpr int BK = T::BK, ACH = T::ACH, LDA = T::LDA, CH = T::CH;
   constexpr int NW = DW + 1, NA = DA + 1, U = Lcm<NW, NA>::value;
+  constexpr int NQ = W8 ? 1 : 2;                  // 16-byte weight loads per block and K-step
+  constexpr int STEP_BYTES = W8 ? 1024 : 2048;    // bytes of one K-step of a 16-row block
   static_assert(DW >= 2 && DA >= 2, "loads run at least two steps ahead");
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
 
@@ -93,12 +125,16 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
     aoff[i] = r * LDA + kc;
   }
   const int nk = K / BK;
-  const bf16_t* wl[NB];
+  const char* wl[NB];
+  float sc[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wl[nb] = w[nb] + lane * 8;
+  for (int nb = 0; nb < NB; ++nb) {
+    wl[nb] = static_cast<const char*>(w[nb]) + lane * 16;
+    sc[nb] = W8 ? wsc[nb][l16] : 1.0f;
+  }
 
   u32x4 ra[NA][ACH];
-  u32x4 b[NW][NB][2];
+  u32x4 b[NW][NB][NQ];
 
   // Loads of step st (clamped to the last step) into register sets sa / sw.
   // A loads go first in each step, so the wait for the next step's A rows
@@ -109,11 +145,11 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
     for (int i = 0; i < ACH; ++i) ra[sa][i] = ld16(arow[i] + k0);
   };
   auto issue_w = [&](int sw, int st) {
-    const int k0 = min(st, nk - 1) * BK;
+    const int64_t off = (int64_t)min(st, nk - 1) * STEP_BYTES;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < NQ; ++q)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[sw][nb][q] = ld16(wl[nb] + k0 * 16 + q * 512);
+      for (int nb = 0; nb < NB; ++nb) b[sw][nb][q] = ld16(wl[nb] + off + q * 1024);
   };
   auto stage = [&](int sa, int buf) {
 #pragma unroll
@@ -127,7 +163,13 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
     for (int q = 0; q < 2; ++q) {
       u32x4 bq[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bq[nb] = live ? b[sw][nb][q] : zero;
+      for (int nb = 0; nb < NB; ++nb) {
+        // FP8: code 0 is +0, so zeroing the codes zeroes the widened operand
+        if constexpr (W8)
+          bq[nb] = widen_fp8(live ? b[sw][nb][0][2 * q] : 0u, live ? b[sw][nb][0][2 * q + 1] : 0u, sc[nb]);
+        else
+          bq[nb] = live ? b[sw][nb][q] : zero;
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 a = ld16(As + (16 * mt + l16) * LDA + 32 * q + 8 * grp);
@@ -164,25 +206,27 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
 
 // One weight row per lane (acc0), or with GATED two (acc0 from w0, acc1 from
 // w1): the single-block and paired forms of stream_tile_n.
-template <int MT, bool GATED, int DW = 2, int DA = 2>
+template <int MT, bool GATED, int DW = 2, int DA = 2, bool W8 = false>
 __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
                                             const int32_t* __restrict__ rowmap, int row0, int nrows,
-                                            const bf16_t* __restrict__ w0,
-                                            const bf16_t* __restrict__ w1, int K,
+                                            const void* __restrict__ w0, const void* __restrict__ w1,
+                                            const float* s0, const float* s1, int K,
                                             f32x4 (&acc0)[MT], f32x4 (&acc1)[MT], bf16_t* lds) {
   if constexpr (GATED) {
-    const bf16_t* const w[2] = {w0, w1};
+    const void* const w[2] = {w0, w1};
+    const float* const ws[2] = {s0, s1};
     f32x4 acc[2][MT];
-    stream_tile_n<MT, 2, DW, DA>(A, lda, rowmap, row0, nrows, w, K, acc, lds);
+    stream_tile_n<MT, 2, DW, DA, W8>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       acc0[mt] = acc[0][mt];
       acc1[mt] = acc[1][mt];
     }
   } else {
-    const bf16_t* const w[1] = {w0};
+    const void* const w[1] = {w0};
+    const float* const ws[1] = {s0};
     f32x4 acc[1][MT];
-    stream_tile_n<MT, 1, DW, DA>(A, lda, rowmap, row0, nrows, w, K, acc, lds);
+    stream_tile_n<MT, 1, DW, DA, W8>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc[0][mt];
   }

@@ -38,6 +38,22 @@ def pack_weight(t: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def quantize_fp8(t: torch.Tensor):
+    """FP8 (E4M3) codes of a row-major bf16 matrix or expert bank
+    (fragment-major, uint8, same element count) and its fp32 row scales,
+    made on the GPU by dg_quantize_fp8."""
+    assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous()
+    k = t.shape[-1]
+    n = t.numel() // k
+    lib = B.load()
+    codes = torch.empty(t.numel(), dtype=torch.uint8, device=t.device)
+    scale = torch.empty(n, dtype=torch.float32, device=t.device)
+    st = lib.dg_quantize_fp8(_stream(), t.data_ptr(), codes.data_ptr(), scale.data_ptr(), n, k)
+    if st != B.DG_OK:
+        raise B.DGError(st, f"dg_quantize_fp8 failed for shape {tuple(t.shape)}")
+    return codes, scale
+
+
 def v_to_cache_order(v: torch.Tensor) -> torch.Tensor:
     """V rows [..., n, dh] (n % 32 == 0) -> the cache's element order: inside
     each 32-key block, key o = 16*half + 4*g + r and dim c sit at
@@ -69,7 +85,8 @@ class Engine:
 
     def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
                  embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
-                 max_requests: int = 1, max_rows: Optional[int] = None):
+                 max_requests: int = 1, max_rows: Optional[int] = None,
+                 expert_format: str = "bf16"):
         self.lib = B.load()
         self.cfg = cfg
         dev = embed.device
@@ -83,6 +100,8 @@ class Engine:
         c.max_ctx, c.max_requests, c.max_rows = max_ctx, max_requests, self.max_rows
         c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
         c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
+        c.expert_format = B.WEIGHT_FORMAT[expert_format]
+        self.expert_format = expert_format
         self.c_cfg = c
         embed = pack_weight(embed)  # the tied LM head streams it fragment-major
         self._keep = [embed, final_norm]
@@ -91,7 +110,11 @@ class Engine:
             for name in LAYER_TENSORS:
                 t = lw[name]
                 assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == dev, name
-                if name in B.PACKED_FIELDS:
+                if expert_format == "fp8" and name in B.EXPERT_FIELDS:
+                    t, scale = quantize_fp8(t)
+                    self._keep.append(scale)
+                    setattr(arr[i], B.SCALE_FIELDS[B.EXPERT_FIELDS.index(name)], scale.data_ptr())
+                elif name in B.PACKED_FIELDS:
                     t = pack_weight(t)
                 self._keep.append(t)
                 setattr(arr[i], name, t.data_ptr())

@@ -71,7 +71,18 @@ typedef struct dg_config {
   int32_t max_requests;  /* number of request slots in the KV cache */
   int32_t max_rows;      /* largest number of rows one call processes */
   float rms_eps, rope_theta, tau_first, tau_last;
+  int32_t expert_format; /* dg_weight_format of the expert matrices (0 = bf16) */
 } dg_config;
+
+/* Storage of the routed and shared expert matrices (w_gate, w_up, w_down,
+ * ws_gate, ws_up, ws_down):
+ *   DG_WEIGHTS_BF16  bf16, fragment-major (dg_pack_weight);
+ *   DG_WEIGHTS_FP8   OCP E4M3 codes with one power-of-two scale per weight
+ *                    row, as made by dg_quantize_fp8; the s_* / ss_* fields
+ *                    of dg_layer_weights point at the scales. The
+ *                    explainer's step timings (§5.2) are measured at FP8
+ *                    precision; the pages do not give the format. */
+typedef enum { DG_WEIGHTS_BF16 = 0, DG_WEIGHTS_FP8 = 1 } dg_weight_format;
 
 /* One layer's weights (device, bf16):
  *   attn_norm [d]        w_qkv [(Hq+2Hkv)*dh][d]   (q heads, then k, then v)
@@ -85,6 +96,9 @@ typedef struct dg_config {
 typedef struct dg_layer_weights {
   const void *attn_norm, *w_qkv, *w_o, *moe_norm, *w_router;
   const void *w_gate, *w_up, *w_down, *ws_gate, *ws_up, *ws_down;
+  /* FP8 experts only (NULL otherwise): device fp32 row scales of
+   * w_gate and w_up [E*F], w_down [E*d], ws_gate and ws_up [Fs], ws_down [d] */
+  const float *s_gate, *s_up, *s_down, *ss_gate, *ss_up, *ss_down;
 } dg_layer_weights;
 
 /* embed [V][d] is also the LM head (tied), fragment-major (dg_pack_weight
@@ -165,6 +179,19 @@ typedef struct dg_ctx dg_ctx;
  * buffers overlap, or n % 16 != 0 or k % 64 != 0. A launch failure returns
  * DG_EHIP. Needs no context. */
 dg_status dg_pack_weight(void *stream, const void *d_src, void *d_dst, int64_t n, int32_t k);
+
+/* FP8 copy of a row-major bf16 matrix W [n][k] (device pointers), for
+ * DG_WEIGHTS_FP8 experts. For each row, d_scale[row] = 2^e with the smallest
+ * integer e such that max_k |W[row][k]| <= 448 * 2^e (1 for a zero row), and
+ * d_dst holds the OCP E4M3 code of W * 2^-e (round to nearest, ties to
+ * even) in the FP8 fragment-major layout: rows in blocks of 16, each block's
+ * K-steps of 64 as 1024 bytes [lane][q][8] with lane = 16*((k%32)/8) + n%16,
+ * q = (k%64)/32, byte k%8. An expert bank [E][N][K] is one [E*N][K] matrix.
+ * Needs n % 16 == 0, k % 64 == 0, finite weights, and d_dst [n*k bytes] not
+ * overlapping d_src; else DG_EINVAL, nothing launched. Asynchronous on
+ * stream; the caller owns all three buffers. */
+dg_status dg_quantize_fp8(void *stream, const void *d_src, void *d_dst, float *d_scale, int64_t n,
+                          int32_t k);
 
 /* Bytes of KV cache for ONE request slot:
  * n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2.

@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY, like the rest of this package.
 
-The pages' fast configuration serves the model with FP8 weights (the
-codemajin.net explainer's throughput section quotes its H100 numbers on a
-quantised build); they do not give the format. The reading taken here:
+The codemajin.net explainer's step timings (§5.2) are measured at FP8
+precision, and a news page puts the quantised model in 18 GB; neither gives
+the format. The reading taken here:
 
   * element format: OCP 8-bit floating point E4M3 ("e4m3fn"): 1 sign bit,
     4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the

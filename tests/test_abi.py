@@ -183,3 +183,35 @@ def test_pack_weight_rejects_bad_arguments(lib):
     # 16 x 64 bf16 = 2048 bytes: destinations overlapping the source are refused
     assert lib.dg_pack_weight(None, ok_src, ok_src + 2046, 16, 64) == B.DG_EINVAL
     assert lib.dg_pack_weight(None, ok_src + 2046, ok_src, 16, 64) == B.DG_EINVAL
+
+
+def test_quantize_fp8_rejects_bad_arguments(lib):
+    ok_src, ok_dst, ok_sc = 0x100000, 0x900000, 0xA00000
+    q = lib.dg_quantize_fp8
+    assert q(None, None, ok_dst, ok_sc, 16, 64) == B.DG_EINVAL
+    assert q(None, ok_src, None, ok_sc, 16, 64) == B.DG_EINVAL
+    assert q(None, ok_src, ok_dst, None, 16, 64) == B.DG_EINVAL
+    assert q(None, ok_src, ok_dst, ok_sc, 24, 64) == B.DG_EINVAL  # n % 16
+    assert q(None, ok_src, ok_dst, ok_sc, 16, 96) == B.DG_EINVAL  # k % 64
+    assert q(None, ok_src, ok_dst, ok_sc, -16, 64) == B.DG_EINVAL
+    # 16 x 64: 2048 source bytes, 1024 destination bytes; overlaps are refused
+    assert q(None, ok_src, ok_src + 2047, ok_sc, 16, 64) == B.DG_EINVAL
+    assert q(None, ok_src + 1023, ok_src, ok_sc, 16, 64) == B.DG_EINVAL
+
+
+def test_fp8_experts_need_their_scales(lib):
+    c = _cfg(model=synth.TINY, max_ctx=256, max_requests=1, max_rows=32)
+    c.expert_format = 2
+    assert lib.dg_workspace_bytes(ctypes.byref(c)) == 0  # unknown format: unsupported config
+    c.expert_format = B.WEIGHT_FORMAT["fp8"]
+    layers = (B.DGLayerWeights * c.n_layers)()
+    for n in B.LAYER_FIELDS:
+        setattr(layers[0], n, 0x1000)
+    w = B.DGWeights(0x1000, 0x1000, layers)
+    ws = lib.dg_workspace_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws, ctypes.byref(h)) == B.DG_EINVAL
+    for n in B.SCALE_FIELDS:
+        setattr(layers[0], n, 0x2000)
+    assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws, ctypes.byref(h)) == B.DG_OK
+    lib.dg_destroy(h)

@@ -99,6 +99,50 @@ def test_route_bit_exact(model, rows):
     assert np.array_equal(out["slot"].cpu().numpy(), slot)
 
 
+# ------------------------------------------------------------------------ FP8 weights
+
+def _unpack8(codes, n, k):
+    """Row-major [n][k] view of FP8 fragment-major bytes (the layout dg.h
+    documents for dg_quantize_fp8)."""
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    idx = ((nn >> 4) * 16 * k + (kk >> 6) * 1024 + (((kk & 31) >> 3) * 16 + (nn & 15)) * 16
+           + ((kk & 63) >> 5) * 8 + (kk & 7))
+    return codes[idx]
+
+
+@pytest.mark.parametrize("which", ["tiny_bank", "full_down", "edges"])
+def test_quantize_fp8_bit_exact(which):
+    from block_discrete_diffusion_dg_amd.engine import quantize_fp8
+    from oracle import fp8
+    say(f"[fp8] quantize {which}")
+    if which == "tiny_bank":
+        w = synth.make_layer_weights(synth.TINY, 0, 7)["w_gate"]  # [E][F][d]
+    elif which == "full_down":
+        w = synth.make_layer_weights(dataclasses.replace(synth.FULL, n_experts=2), 0, 7)["w_down"][1]
+    else:
+        # a zero row, rows whose maximum sits exactly on 448 * 2^e or just
+        # above it, tiny rows (subnormal codes), negative zeros, ties
+        rng = np.random.default_rng(3)
+        w = rng.standard_normal((64, 128)).astype(np.float32) * 0.02
+        w[0] = 0.0
+        w[1, 5] = 448.0
+        w[2, 7] = -448.0 * 2.0 ** -10
+        w[3, 9] = 449.0
+        w[4] = rng.standard_normal(128) * 1e-6
+        w[5, :8] = -0.0
+        w[6, 0] = 448.0
+        w[6, 1:9] = [1 + 1 / 16, 1 + 3 / 16, 2.0 ** -8 * 1.5, 300.0, 432.0, -432.0, 2.0 ** -9 * 0.5, 7.5]
+        w = torch.from_numpy(w).to(torch.bfloat16)
+    w2 = w.reshape(-1, w.shape[-1]).contiguous()
+    n, k = w2.shape
+    codes, scale = quantize_fp8(w2.cuda())
+    torch.cuda.synchronize()
+    codes = _unpack8(codes.cpu().numpy(), n, k)
+    want_codes, want_e = fp8.quantize_rows(om.f64(w2))
+    assert np.array_equal(scale.cpu().double().numpy(), np.exp2(want_e.astype(np.float64)))
+    assert np.array_equal(codes, want_codes)
+
+
 # ------------------------------------------------------------------------ LM head + sampler
 
 def _head_case(model, n_req, step, n_steps, seed=3):
@@ -266,19 +310,24 @@ def _cache_rows(eng, slot, layer, lo, hi):
 # chunks for hot experts), and a small layer whose projection widths (K = 768
 # and 384) are not a power-of-two multiple of 256, so the dense projections
 # take their streaming-tile form instead of the split-K form.
-@pytest.mark.parametrize("name,causal,P,C,over", [("tiny", False, None, None, None), ("tiny", True, None, None, None),
-                                                  ("one_layer", False, None, None, None),
-                                                  ("one_layer", True, None, None, None),
-                                                  ("one_layer", False, 32768, None, None),
-                                                  ("one_layer", False, None, 2048, None),
-                                                  ("tiny", False, None, None, {"d_model": 768, "n_q_heads": 6})])
-def test_layer_parity(name, causal, P, C, over):
+@pytest.mark.parametrize("name,causal,P,C,over,fmt", [
+    ("tiny", False, None, None, None, "bf16"), ("tiny", True, None, None, None, "bf16"),
+    ("one_layer", False, None, None, None, "bf16"),
+    ("one_layer", True, None, None, None, "bf16"),
+    ("one_layer", False, 32768, None, None, "bf16"),
+    ("one_layer", False, None, 2048, None, "bf16"),
+    ("tiny", False, None, None, {"d_model": 768, "n_q_heads": 6}, "bf16"),
+    ("tiny", False, None, None, None, "fp8"),
+    ("one_layer", False, None, None, None, "fp8")])
+def test_layer_parity(name, causal, P, C, over, fmt):
+    """With fmt "fp8" the experts stream E4M3 weights; the oracle multiplies
+    with its own dequantisation of the same bf16 weights."""
     wl = synth.WORKLOADS[name]
     cfg = dataclasses.replace(wl.model, n_layers=1, **(over or {}))
     P = P or wl.prefix
     C = C or cfg.canvas
-    say(f"[layer] {name} {over or ''} causal={causal} P={P} rows={C}")
-    eng, hw = make_engine(cfg, max_ctx=P + 2 * C, max_rows=C)
+    say(f"[layer] {name} {over or ''} causal={causal} P={P} rows={C} experts={fmt}")
+    eng, hw = make_engine(cfg, max_ctx=P + 2 * C, max_rows=C, expert_format=fmt)
     _fill_prefix(eng, cfg, P)
     h = synth.make_hidden(C, cfg.d_model, 21)
     h_dev = h.cuda()
