@@ -363,13 +363,16 @@ def fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds, blocks, canvas
     b = fp8_expert_bytes(cfg, touched)
     log(f"fp8 experts: {ms:.3f} ms/step, expert launch {ex_ms * 1e3:.1f} us")
     eng.close()
+    from block_discrete_diffusion_dg_amd.profiles import traffic_for
+    traffic = traffic_for("moe_experts", f"moe_experts_fp8_{wl.name}_traffic")
     return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
             "canvas_tok_s": round(1e3 / ms * rows, 1),
             "weights": "expert matrices E4M3 + per-row power-of-two scales; everything else bf16",
             "experts_kernel": {"bound": "hbm", "bytes_per_launch": round(b), "avg_launch_ms": round(ex_ms, 4),
                                "achieved": round(b / (ex_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                "peak": HBM_PEAK / 1e9, "frac": round(b / (ex_ms * 1e-3) / HBM_PEAK, 4),
-                               "touched_experts_per_layer": round(touched, 2)},
+                               "touched_experts_per_layer": round(touched, 2),
+                               "traffic": round(traffic) if traffic is not None else None},
             "stages_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in stages.items() if v[1]}}
 
 

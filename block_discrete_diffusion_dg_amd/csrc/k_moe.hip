@@ -83,6 +83,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
     s_dn[i] = p.items[MOE_ITEMS_DN + i];
     s_ch[i] = p.items[MOE_CHUNKS + i];
   }
+  // weight loads run this many K-steps ahead (for FP8 too: five steps ahead,
+  // which would keep as many bytes in flight as bf16, spilled registers and
+  // measured slower)
+  constexpr int EXPERT_DW = 2;
   int32_t* queue = p.items + MOE_QUEUE;
   int32_t* done = p.items + MOE_DONE;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       auto gate_up = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 ag[MTI], au[MTI];
-        stream_tile<MTI, true, 2, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0, W1, S0, S1,
+        stream_tile<MTI, true, EXPERT_DW, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0, W1, S0, S1,
                                          p.d, ag, au, lds);
         // Publish: stage the 64-column tile in LDS, write whole 128-byte row
         // segments with write-through (agent-coherent) stores, wait until they
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       auto down = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 acc0[MTI], acc1[MTI];
-        stream_tile<MTI, true, 2, 2, W8>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
+        stream_tile<MTI, true, EXPERT_DW, 2, W8>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
                                          Sd, W8 ? Sd + 16 : nullptr, K, acc0, acc1, lds);
 #pragma unroll
         for (int mt = 0; mt < MTI; ++mt)
