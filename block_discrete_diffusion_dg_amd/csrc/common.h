@@ -24,7 +24,7 @@ constexpr int MOE_QUEUE = 408;            // work-queue head
 constexpr int MOE_SPIN_TIMEOUTS = 409;    // waits that ran out (never reset)
 constexpr int MOE_TOUCHED_TOTAL = 410;    // uint64: experts with >= 1 row, summed over calls
 constexpr int MOE_PERMUTE_CALLS = 412;    // uint64: permutation calls (both never reset)
-constexpr int MOE_DONE = 416;             // per-chunk count of finished gate/up tiles
+constexpr int MOE_DONE = 416;             // per-chunk count of finished 32-column gate/up units
 #define DG_ATTN_SPLITS 8    // maximum key splits of the attention kernel
 #define WAVE 64
 

@@ -90,13 +90,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
   int32_t* queue = p.items + MOE_QUEUE;
   int32_t* done = p.items + MOE_DONE;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+  // Gate/up items beyond the first round of the resident grid start only as
+  // work-groups free up, and the down items of their chunks wait for them.
+  // Each runs as two half items of 32 columns instead, taken by two
+  // work-groups, so that the last gate/up work streams with twice the
+  // concurrency. Queue: n_full whole items, 2*n_split halves, then the down
+  // items. Chunk counters count 32-column units (a whole item adds 2).
+  __syncthreads();  // the item tables above are in LDS for every thread
+  const int n_gu = s_gu[G];
+  const int n_split = max(0, n_gu - (int)gridDim.x);
+  const int n_full = n_gu - n_split;
+  const int n_gu_q = n_full + 2 * n_split;
   for (;;) {
     const int b = next_item(queue, &s_item);
-    const int n_gu = s_gu[G], total = n_gu + s_dn[G];
+    const int total = n_gu_q + s_dn[G];
     if (b >= total) break;
-    const bool up = b < n_gu;
+    const bool up = b < n_gu_q;
     const int32_t* s_it = up ? s_gu : s_dn;
-    const int bl = up ? b : b - n_gu;
+    int bl, half = -1;  // half item: which 32 of the item's 64 columns
+    if (!up) {
+      bl = b - n_gu_q;
+    } else if (b < n_full) {
+      bl = b;
+    } else {
+      const int unit = 2 * n_full + (b - n_full);
+      bl = unit >> 1;
+      half = unit & 1;
+    }
     const int gi = __builtin_amdgcn_readfirstlane(find_group(s_it, G, bl));
     const bool shared = gi == 0;
     const int e = gi - 1;
@@ -148,17 +168,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
                              *reinterpret_cast<const u32x4*>(st + rr * 72 + seg));
         }
       };
-      if (MT >= 8 && nrows > 64)
-        gate_up(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
-      else if (MT >= 4 && nrows > 32)
-        gate_up(std::integral_constant<int, (MT >= 4 ? 4 : MT)>{});
-      else
-        gate_up(std::integral_constant<int, 2>{});
+      // Half item: 32 columns; waves 0-1 stream the gate rows of its two
+      // 16-column blocks, waves 2-3 the up rows, and the SwiGLU is formed
+      // from both halves staged in LDS (same products, same results as the
+      // whole item).
+      const bool is_up = wave >= 2;
+      const int colh = nt * 64 + half * 32;
+      const int64_t wrh = (shared ? 0 : (int64_t)e * p.F) + colh + 16 * (wave & 1);
+      const void* Wh = wrow<W8>(is_up ? (shared ? p.su : p.wu) : (shared ? p.sg : p.wg), wrh, p.d);
+      const float* Sh = W8 ? (is_up ? (shared ? p.sc.su : p.sc.u) : (shared ? p.sc.sg : p.sc.g)) + wrh : nullptr;
+      auto gate_up_half = [&](auto mt_tag) {
+        constexpr int MTI = decltype(mt_tag)::value;
+        constexpr int LDF = 33;  // padded fp32 row of the staging tiles
+        f32x4 acc[MTI], unused[MTI];
+        stream_tile<MTI, false, EXPERT_DW, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, Wh, nullptr,
+                                                  Sh, nullptr, p.d, acc, unused, lds);
+        __syncthreads();  // the tile's last LDS reads are done
+        float* stf = reinterpret_cast<float*>(lds);  // [gate, up][16 MTI][LDF] fp32
+        float* mine = stf + (is_up ? 16 * MTI * LDF : 0);
+#pragma unroll
+        for (int mt = 0; mt < MTI; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mine[(16 * mt + 4 * grp + r) * LDF + 16 * (wave & 1) + l16] = acc[mt][r];
+        __syncthreads();
+        for (int c = threadIdx.x; c < 16 * MTI * 4; c += 256) {
+          const int rr = c >> 2, seg = (c & 3) * 8;
+          if (row0 + rr < n) {
+            u32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float g0 = stf[rr * LDF + seg + 2 * j], g1 = stf[rr * LDF + seg + 2 * j + 1];
+              const float u0 = stf[(16 * MTI + rr) * LDF + seg + 2 * j];
+              const float u1 = stf[(16 * MTI + rr) * LDF + seg + 2 * j + 1];
+              v[j] = (uint32_t)f2bf(g0 / (1.0f + expf(-g0)) * u0) | ((uint32_t)f2bf(g1 / (1.0f + expf(-g1)) * u1) << 16);
+            }
+            store16_coherent(out + (int64_t)(row0 + rr) * ldo + colh + seg, v);
+          }
+        }
+      };
+      if (half < 0) {
+        if (MT >= 8 && nrows > 64)
+          gate_up(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
+        else if (MT >= 4 && nrows > 32)
+          gate_up(std::integral_constant<int, (MT >= 4 ? 4 : MT)>{});
+        else
+          gate_up(std::integral_constant<int, 2>{});
+      } else {
+        if (MT >= 8 && nrows > 64)
+          gate_up_half(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
+        else if (MT >= 4 && nrows > 32)
+          gate_up_half(std::integral_constant<int, (MT >= 4 ? 4 : MT)>{});
+        else
+          gate_up_half(std::integral_constant<int, 2>{});
+      }
       wait_stores();
       __syncthreads();
-      if (threadIdx.x == 0) __hip_atomic_fetch_add(done + chunk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(done + chunk, half < 0 ? 2 : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      const int need = (shared ? p.Fs : p.F) / 64;  // gate/up column tiles of the chunk
+      const int need = (shared ? p.Fs : p.F) / 32;  // 32-column units of the chunk's gate/up work
       // Poll with device-coherent relaxed loads. No cache invalidation is
       // needed after the wait (an agent-scope acquire would invalidate this
       // XCD's whole L2 on every poll): caches start the kernel invalidated,
