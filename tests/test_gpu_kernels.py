@@ -318,7 +318,8 @@ def _cache_rows(eng, slot, layer, lo, hi):
     ("one_layer", False, None, 2048, None, "bf16"),
     ("tiny", False, None, None, {"d_model": 768, "n_q_heads": 6}, "bf16"),
     ("tiny", False, None, None, None, "fp8"),
-    ("one_layer", False, None, None, None, "fp8")])
+    ("one_layer", False, None, None, None, "fp8"),
+    ("one_layer", False, None, 2048, None, "fp8")])
 def test_layer_parity(name, causal, P, C, over, fmt):
     """With fmt "fp8" the experts stream E4M3 weights; the oracle multiplies
     with its own dequantisation of the same bf16 weights."""
