@@ -41,7 +41,8 @@ Readings where the pages are silent (each is listed in the design doc):
   adaptive stopping compares the mean entropy of that distribution with the
   threshold, requires every argmax to equal the previous step's, and then
   accepts every position (the step acts as the block's last);
-  candidate = held token for committed positions, greedy argmax otherwise;
+  candidate = held token for committed positions, greedy argmax otherwise
+  (or a sample of softmax(L/tau) by Gumbel-max, from counter-based uniforms);
   cumulative schedule k_s = floor(s * C / S);
   committed positions hold their token until they fall out of the top-k_s.
 """
@@ -51,7 +52,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from .philox import uniform_ids
+from .philox import gumbel_uniforms, uniform_ids
 
 
 def f64(a) -> np.ndarray:
@@ -296,6 +297,24 @@ def row_entropy(L: np.ndarray, tau: float, chunk: int = 16) -> np.ndarray:
     return H
 
 
+def gumbel_candidates(L: np.ndarray, tau: float, seed: int, step: int, block: int, request: int,
+                      rows: Optional[Sequence[int]] = None):
+    """Sampled candidates y_i ~ softmax(L_i / tau) by the Gumbel-max identity:
+    y_i = argmax_v (L_iv / tau - ln(-ln u_iv)) with the position's uniforms
+    u (philox.gumbel_uniforms), ties to the lower id. Returns (y, L_i[y_i])
+    for the given rows (default: all)."""
+    L = np.asarray(L, np.float64)
+    rows = range(L.shape[0]) if rows is None else rows
+    ys, ly = [], []
+    for i in rows:
+        u = gumbel_uniforms(seed, i, step, block, request, L.shape[1])
+        key = L[i] / tau - np.log(-np.log(u))
+        y = int(np.argmax(key))
+        ys.append(y)
+        ly.append(L[i, y])
+    return np.array(ys, np.int64), np.array(ly, np.float64)
+
+
 def adaptive_stop(H: np.ndarray, a: np.ndarray, a_prev: Optional[np.ndarray],
                   threshold: float) -> bool:
     """Adaptive stopping (explainer §3.3): the block stops when the mean
@@ -309,10 +328,13 @@ def adaptive_stop(H: np.ndarray, a: np.ndarray, a_prev: Optional[np.ndarray],
 
 def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
            n_steps: int, seed: int, block: int, request: int, vocab: int,
-           confidence: str = "prob", H: Optional[np.ndarray] = None, stop: bool = False):
+           confidence: str = "prob", H: Optional[np.ndarray] = None, stop: bool = False,
+           drawn: Optional[tuple] = None):
     """Confidence-ordered acceptance with uniform re-noise.
 
-    Candidate y_i: the held token if position i is committed, else the argmax.
+    Candidate y_i: the held token if position i is committed, else the argmax
+    or, when `drawn` = (ids, their logits) is given, the sampled candidate
+    (gumbel_candidates).
     Confidence, by `confidence`:
       "prob":    c_i = log p_tau(y_i) = (L[y_i] - M_i)/tau - log Z_i;
       "entropy": c_i = -H_i, so low-entropy positions come first
@@ -326,9 +348,10 @@ def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
     """
     C = x.shape[0]
     committed = np.asarray(m).astype(bool)
-    y = np.where(committed, x, a)
+    cand, Lc = (a, M) if drawn is None else drawn
+    y = np.where(committed, x, cand)
     if confidence == "prob":
-        Ly = np.where(committed, gx, M)
+        Ly = np.where(committed, gx, Lc)
         c = (Ly - M) / tau - logZ
     elif confidence == "entropy":
         c = -np.asarray(H, np.float64)
@@ -409,7 +432,8 @@ def commit_block(weights, cfg, req: Request, canvas_ids: np.ndarray):
 def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step: int,
                  n_steps: int, seed: int, block: int, request: int,
                  keep: Optional[Dict] = None, confidence: str = "prob",
-                 stop_entropy: float = 0.0, a_prev: Optional[np.ndarray] = None):
+                 stop_entropy: float = 0.0, a_prev: Optional[np.ndarray] = None,
+                 candidate: str = "argmax"):
     """One denoising step of one request's canvas.
 
     The canvas attends bidirectionally to itself and to the cached prefix; the
@@ -425,11 +449,13 @@ def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step:
     M, a, logZ, gx = row_stats(L, np.asarray(x), tau)
     H = row_entropy(L, tau)
     stop = stop_entropy > 0 and adaptive_stop(H, a, a_prev, stop_entropy)
+    drawn = gumbel_candidates(L, tau, seed, step, block, request) if candidate == "sample" else None
     x_new, m_new, c, accept = sample(x, m, M, a, logZ, gx, tau, step, n_steps, seed, block,
-                                     request, cfg.vocab, confidence=confidence, H=H, stop=stop)
+                                     request, cfg.vocab, confidence=confidence, H=H, stop=stop,
+                                     drawn=drawn)
     if keep is not None:
         keep.update(layers=layers, h=h, logits=L, M=M, a=a, logZ=logZ, gx=gx, c=c,
-                    accept=accept, tau=tau, H=H, stop=stop)
+                    accept=accept, tau=tau, H=H, stop=stop, drawn=drawn)
     return x_new, m_new
 
 

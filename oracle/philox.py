@@ -17,6 +17,13 @@ Mapping used by both sides of the build:
             initial canvas
   id      = (word0 * V) >> 32, which is word0 >> (32 - log2 V) when V is a
             power of two.
+
+Gumbel noise for sampling candidates (our reading as well): the uniform of
+vocabulary id v at canvas position i is word ((v >> 4) & 3) of
+  Philox(key, counter = (v with bits 4 and 5 cleared, i,
+                         (block << 16) | step, 0x80000000 | request)),
+as u = ((word >> 8) + 1/2) / 2^24, strictly inside (0, 1). The top bit of
+the last counter word keeps these streams apart from the re-noise draws.
 """
 from __future__ import annotations
 
@@ -69,3 +76,17 @@ def uniform_ids(seed: int, positions, step: int, block: int, request: int,
     ctr[..., 3] = np.uint64(request)
     w0 = philox4x32_10(ctr, seed_key(seed))[..., 0].astype(np.uint64)
     return ((w0 * np.uint64(vocab)) >> _SH).astype(np.int64)
+
+
+def gumbel_uniforms(seed: int, position: int, step: int, block: int, request: int,
+                    vocab: int) -> np.ndarray:
+    """The uniforms u_v (float64, exact) of one canvas position, v = 0..V-1."""
+    v = np.arange(vocab, dtype=np.uint64)
+    ctr = np.zeros((vocab, 4), dtype=np.uint64)
+    ctr[:, 0] = v & ~np.uint64(0x30)
+    ctr[:, 1] = np.uint64(position)
+    ctr[:, 2] = (np.uint64(block) << np.uint64(16)) | np.uint64(step)
+    ctr[:, 3] = np.uint64(0x80000000) | np.uint64(request)
+    words = philox4x32_10(ctr, seed_key(seed))
+    w = words[np.arange(vocab), ((v >> np.uint64(4)) & np.uint64(3)).astype(np.int64)].astype(np.uint64)
+    return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)

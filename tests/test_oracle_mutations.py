@@ -16,6 +16,7 @@ import torch.nn.functional as F
 from block_discrete_diffusion_dg_amd import synth
 from oracle import fp8 as om_fp8
 from oracle import model as om
+from oracle import philox as om_philox
 from tests.test_oracle_pins import _sdpa_reference
 
 RNG = np.random.default_rng(99)
@@ -100,6 +101,30 @@ def _bad_row_exponent(amax):
     return (x - 9).astype(np.int64)  # ignores a mantissa above 448's
 
 
+def _pin_gumbel():
+    L_row = np.array([0.3, -1.2, 1.1, 0.0])
+    n = 6000
+    ys, _ = om.gumbel_candidates(np.tile(L_row, (n, 1)), 0.5, 7, 3, 1, 0)
+    freq = np.bincount(ys, minlength=4) / n
+    p = scipy.special.softmax(L_row / 0.5)
+    return scipy.stats.chi2.sf(n * np.sum((freq - p) ** 2 / p), 3) > 1e-4
+
+
+def _bad_gumbel_no_tau(L, tau, seed, step, block, request, rows=None):
+    return _real["gumbel_candidates"](L, 1.0, seed, step, block, request, rows)  # temperature dropped
+
+
+def _bad_gumbel_sign(L, tau, seed, step, block, request, rows=None):
+    L = np.asarray(L, np.float64)
+    ys, ly = [], []
+    for i in range(L.shape[0]):
+        u = om_philox.gumbel_uniforms(seed, i, step, block, request, L.shape[1])
+        y = int(np.argmax(L[i] / tau + np.log(-np.log(u))))  # noise sign flipped
+        ys.append(y)
+        ly.append(L[i, y])
+    return np.array(ys), np.array(ly)
+
+
 def _pin_rms_norm():
     x = RNG.normal(size=(3, 32))
     g = RNG.normal(size=32)
@@ -169,7 +194,7 @@ def _bad_rms_norm(x, gain, eps):
 _real_fp8 = {"e4m3_encode": om_fp8.e4m3_encode}
 
 _real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
-         "row_entropy": om.row_entropy}
+         "row_entropy": om.row_entropy, "gumbel_candidates": om.gumbel_candidates}
 
 CASES = [
     ("rope", _bad_rope, _pin_rope),
@@ -182,6 +207,8 @@ CASES = [
     ("row_entropy", _bad_row_entropy, _pin_row_entropy),
     ("row_entropy", _bad_row_entropy_log2, _pin_row_entropy),
     ("adaptive_stop", _bad_adaptive_stop, _pin_adaptive_stop),
+    ("gumbel_candidates", _bad_gumbel_no_tau, _pin_gumbel),
+    ("gumbel_candidates", _bad_gumbel_sign, _pin_gumbel),
 ]
 
 

@@ -17,6 +17,7 @@ from block_discrete_diffusion_dg_amd import synth
 from oracle import fp8
 from oracle import model as om
 from oracle import metrics
+from oracle import philox as philox_mod
 from oracle.philox import philox4x32_10, uniform_ids
 from tests.conftest import golden
 
@@ -380,6 +381,53 @@ def test_adaptive_stop_in_the_denoising_step():
                     a_prev=k1["a"])
     assert not k3["stop"]
     assert np.allclose(k1["H"], om.row_entropy(k1["logits"], k1["tau"]))
+
+
+def _gumbel_frequencies(L_row, tau, n, seed=7):
+    L = np.tile(np.asarray(L_row, np.float64), (n, 1))
+    ys, ly = om.gumbel_candidates(L, tau, seed, 3, 1, 0)
+    assert np.array_equal(ly, L[np.arange(n), ys])
+    return np.bincount(ys, minlength=L.shape[1]) / n
+
+
+def test_gumbel_candidates_follow_the_tempered_softmax():
+    """Gumbel-max: argmax_v (L_v / tau + G_v) is distributed as
+    softmax(L / tau); a chi-square test over 20,000 positions."""
+    L_row = np.array([0.3, -1.2, 1.1, 0.0, 0.7, -0.4])
+    tau = 0.6
+    n = 20000
+    freq = _gumbel_frequencies(L_row, tau, n)
+    p = scipy.special.softmax(L_row / tau)
+    chi2 = n * np.sum((freq - p) ** 2 / p)
+    assert scipy.stats.chi2.sf(chi2, len(p) - 1) > 1e-3, chi2
+    # a vanishing temperature gives the argmax
+    assert np.all(om.gumbel_candidates(np.tile(L_row, (50, 1)), 1e-4, 7, 3, 1, 0)[0] == 2)
+
+
+def test_gumbel_uniforms_lie_on_the_24_bit_grid_inside_the_interval():
+    u = philox_mod.gumbel_uniforms(11, 5, 2, 1, 3, 4096)
+    assert np.all((u > 0) & (u < 1))
+    g = u * (1 << 24) - 0.5
+    assert np.array_equal(g, np.round(g))
+    # the four ids that share a counter take its four words; other positions,
+    # steps, blocks and requests draw other streams
+    assert len(set(np.round(g[[0, 16, 32, 48]]).astype(int))) == 4
+    for args in [(11, 6, 2, 1, 3), (11, 5, 3, 1, 3), (11, 5, 2, 2, 3), (11, 5, 2, 1, 4), (12, 5, 2, 1, 3)]:
+        assert not np.array_equal(philox_mod.gumbel_uniforms(*args, 4096), u)
+
+
+def test_sampled_candidates_in_the_sampler():
+    V, C, S, s = 40, 16, 4, 2
+    L = RNG.normal(size=(C, V)) * 2
+    x, _ = om.init_canvas(2, 0, 0, C, V)
+    m = (np.arange(C) % 4 == 1).astype(np.uint8)
+    tau = om.tau_at(s, S, 0.8, 0.4)
+    M, a, logZ, gx = om.row_stats(L, x, tau)
+    drawn = om.gumbel_candidates(L, tau, 2, s, 0, 0)
+    x2, m2, c, acc = om.sample(x, m, M, a, logZ, gx, tau, s, S, 2, 0, 0, V, drawn=drawn)
+    y = np.where(m.astype(bool), x, drawn[0])
+    assert np.allclose(c, scipy.special.log_softmax(L / tau, axis=1)[np.arange(C), y], atol=1e-12)
+    assert np.array_equal(x2[acc], y[acc])
 
 
 # ----------------------------------------------------------------------------- FP8 weights
