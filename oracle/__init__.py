@@ -26,7 +26,7 @@ Parity status per function (what pins each, see tests/test_oracle_pins.py):
   adaptive_stop   its four cases; a stopped step accepts every position
   gumbel_candidates  chi-square against softmax(L / tau) over 20,000
                   positions; argmax at vanishing temperature; uniforms on
-                  the 24-bit grid inside (0, 1), distinct streams
+                  the 23-bit grid inside (0, 1), distinct streams
   fp8 (E4M3)      torch's float8_e4m3fn decode and encode; round trip of
                   every finite code; ties to even; row-exponent minimality;
                   half-ulp error bound

@@ -22,8 +22,9 @@ Gumbel noise for sampling candidates (our reading as well): the uniform of
 vocabulary id v at canvas position i is word ((v >> 4) & 3) of
   Philox(key, counter = (v with bits 4 and 5 cleared, i,
                          (block << 16) | step, 0x80000000 | request)),
-as u = ((word >> 8) + 1/2) / 2^24, strictly inside (0, 1). The top bit of
-the last counter word keeps these streams apart from the re-noise draws.
+as u = ((word >> 9) + 1/2) / 2^23, strictly inside (0, 1) and exact in
+float32. The top bit of the last counter word keeps these streams apart from
+the re-noise draws.
 """
 from __future__ import annotations
 
@@ -89,4 +90,4 @@ def gumbel_uniforms(seed: int, position: int, step: int, block: int, request: in
     ctr[:, 3] = np.uint64(0x80000000) | np.uint64(request)
     words = philox4x32_10(ctr, seed_key(seed))
     w = words[np.arange(vocab), ((v >> np.uint64(4)) & np.uint64(3)).astype(np.int64)].astype(np.uint64)
-    return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)
+    return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)

@@ -404,10 +404,11 @@ def test_gumbel_candidates_follow_the_tempered_softmax():
     assert np.all(om.gumbel_candidates(np.tile(L_row, (50, 1)), 1e-4, 7, 3, 1, 0)[0] == 2)
 
 
-def test_gumbel_uniforms_lie_on_the_24_bit_grid_inside_the_interval():
+def test_gumbel_uniforms_lie_on_the_23_bit_grid_inside_the_interval():
     u = philox_mod.gumbel_uniforms(11, 5, 2, 1, 3, 4096)
     assert np.all((u > 0) & (u < 1))
-    g = u * (1 << 24) - 0.5
+    g = u * (1 << 23) - 0.5
+    assert np.array_equal(u.astype(np.float32).astype(np.float64), u)  # exact in float32
     assert np.array_equal(g, np.round(g))
     # the four ids that share a counter take its four words; other positions,
     # steps, blocks and requests draw other streams
