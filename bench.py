@@ -313,10 +313,40 @@ def main():
         # reaches on this GPU in the same run
         out["roofline"]["peak_measured"] = round(copy_gbs, 1)
         out["roofline"]["frac_measured"] = round(out["roofline"]["achieved"] / copy_gbs, 4)
-    if not args.no_fp8_variant and args.workload == "full":
-        out["variants"] = {"fp8_experts": fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
-                                                      blocks, canvas0, dev)}
+    if args.workload == "full":
+        out["variants"] = {"sampled_candidates": sampled_variant(args, eng, reqs, seeds, blocks, x, m, S)}
+        if not args.no_fp8_variant:
+            out["variants"]["fp8_experts"] = fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
+                                                         blocks, canvas0, dev)
     print(json.dumps(out), flush=True)
+
+
+def sampled_variant(args, eng, reqs, seeds, blocks, x, m, S):
+    """The same step with sampled candidates (Gumbel-max over the vocabulary
+    in the LM-head epilogue) instead of the argmax: the cost of the draw."""
+    import torch
+
+    def run(n, start):
+        for i in range(n):
+            eng.denoise_step(reqs, x, m, (start + i) % S + 1, S, seeds, blocks, candidate="sample")
+
+    run(args.warmup, 0)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(args.steps, args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    eng.timing(True)
+    run(args.steps, args.warmup + args.steps)
+    stages = eng.timing_read()
+    eng.timing(False)
+    log(f"sampled candidates: {ms:.3f} ms/step")
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
+            "lmhead_ms": round(stages["lmhead"][0] / max(1, stages["lmhead"][1]), 4),
+            "merge_ms": round(stages["merge"][0] / max(1, stages["merge"][1]), 4)}
 
 
 def fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds, blocks, canvas0, dev):

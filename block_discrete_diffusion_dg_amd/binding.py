@@ -54,7 +54,8 @@ class DGWeights(ctypes.Structure):
 
 class DGRowStats(ctypes.Structure):
     _fields_ = [("max_logit", c_f32), ("log_z", c_f32), ("held_logit", c_f32), ("conf", c_f32),
-                ("argmax", c_i32), ("accepted", c_i32), ("entropy", c_f32), ("pad", c_i32)]
+                ("argmax", c_i32), ("accepted", c_i32), ("entropy", c_f32), ("sample", c_i32),
+                ("sample_logit", c_f32), ("pad", c_i32)]
 
 
 ROW_STATS_BYTES = ctypes.sizeof(DGRowStats)
@@ -64,14 +65,16 @@ class DGStepArgs(ctypes.Structure):
     _fields_ = [("n_req", c_i32), ("req", ctypes.POINTER(c_i32)), ("d_canvas", c_vp),
                 ("d_committed", c_vp), ("step", c_i32), ("n_steps", c_i32),
                 ("seed", ctypes.POINTER(ctypes.c_uint64)), ("block", ctypes.POINTER(c_i32)),
-                ("d_stats", c_vp), ("confidence", c_i32), ("stop_entropy", c_f32), ("d_stop", c_vp)]
+                ("d_stats", c_vp), ("confidence", c_i32), ("stop_entropy", c_f32), ("d_stop", c_vp),
+                ("candidate", c_i32)]
 
 
 CONFIDENCE = {"prob": 0, "entropy": 1}
+CANDIDATE = {"argmax": 0, "sample": 1}
 
 
 WS_FIELDS = ("h", "u", "q", "attn_o", "attn_part", "attn_ml", "rope", "z", "idx", "w", "wslot",
-             "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "stats", "ids", "ss", "zpart", "sync",
+             "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "lm_gpart", "stats", "ids", "ss", "zpart", "sync",
              "prev", "total")
 
 

@@ -63,6 +63,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.hid_s = take(R * c.d_shared * 2);
   L.y = take(R * k * d * 4 + R * d * 4);  // routed outputs, then the shared expert's
   L.lm_part = take(R * (size_t)lmhead_parts(c.vocab) * 16);
+  L.lm_gpart = take(R * (size_t)lmhead_parts(c.vocab) * 16);
   L.stats = take(R * sizeof(dg_row_stats));
   L.ids = take(R * 4);
   L.ss = take(R * (d / 64) * 4);
@@ -274,10 +275,14 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   const float tau = tau_for(g, a->step, a->n_steps);
   const int k_s = (int)(((int64_t)a->step * g.canvas) / a->n_steps);
   dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
+  const bool drawn = a->candidate == DG_CAND_SAMPLE;
+  GumbelDraw gd{make_sample_table(a->n_req, a->seed, a->block, a->req), g.canvas, a->step, 1.0f / tau,
+                c->buf<float4>(L.lm_gpart)};
   STAGE(DG_STAGE_LMHEAD, launch_lmhead(s, c->buf<bf16_t>(L.u), rows, g.d_model, c->embed, g.vocab, a->d_canvas,
                                       tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
-                                      (int)(sizeof(dg_row_stats) / sizeof(float))));
-  STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats));
+                                      (int)(sizeof(dg_row_stats) / sizeof(float)), drawn ? &gd : nullptr));
+  STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats,
+                                        drawn ? c->buf<float4>(L.lm_gpart) : nullptr));
   // the previous step's argmax of a slot counts only after a step of the
   // same block (host-side, in stream order)
   uint32_t prev_valid = 0;
@@ -285,7 +290,7 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
     if (c->prev_valid[a->req[r]]) prev_valid |= 1u << r;
     c->prev_valid[a->req[r]] = 1;
   }
-  const SamplerMode mode{a->confidence, a->stop_entropy > 0.f ? a->stop_entropy : 0.f,
+  const SamplerMode mode{a->confidence, a->candidate, a->stop_entropy > 0.f ? a->stop_entropy : 0.f,
                          c->buf<int32_t>(L.prev), prev_valid, a->d_stop};
   STAGE(DG_STAGE_SAMPLER, launch_sampler(s, stats, a->n_req, g.canvas, g.vocab, a->d_canvas, a->d_committed,
                                          a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats, mode));
@@ -313,6 +318,14 @@ dg_status check_step_args(dg_ctx* c, const dg_step_args* a, bool need_step) {
   if (need_step && a->confidence != DG_CONF_PROB && a->confidence != DG_CONF_ENTROPY)
     return c->fail(DG_EINVAL, "confidence must be DG_CONF_PROB or DG_CONF_ENTROPY");
   if (need_step && a->stop_entropy != a->stop_entropy) return c->fail(DG_EINVAL, "stop_entropy is NaN");
+  if (need_step && a->candidate != DG_CAND_ARGMAX && a->candidate != DG_CAND_SAMPLE)
+    return c->fail(DG_EINVAL, "candidate must be DG_CAND_ARGMAX or DG_CAND_SAMPLE");
+  if (need_step && a->candidate == DG_CAND_SAMPLE) {
+    if (a->n_steps >= (1 << 16)) return c->fail(DG_EINVAL, "sampled candidates need n_steps < 65536");
+    for (int r = 0; r < a->n_req; ++r)
+      if (a->block[r] < 0 || a->block[r] >= (1 << 15))
+        return c->fail(DG_EINVAL, "sampled candidates need 0 <= block < 32768");
+  }
   return DG_OK;
 }
 

@@ -9,7 +9,8 @@
 //   log Z = ln z,  H = ln z - ln2 * w / z  (entropy of softmax(L / tau)).
 // The sampler then, per request (one work-group, one thread per canvas
 // position):
-//   y_i  = held token if committed, else the argmax;
+//   y_i  = held token if committed, else the argmax (or the sampled
+//          candidate: the largest L/tau + Gumbel noise over the tiles);
 //   c_i  = (L_i[y_i] - M_i) / tau - log Z_i, or -H_i in entropy mode;
 //   stop = mean_i H_i < threshold and every argmax equals the previous
 //          step's (adaptive stopping; then every position is accepted);
@@ -46,10 +47,20 @@ __device__ __forceinline__ void lse_merge(float& m, float& z, float& w, int& a, 
   }
 }
 
+// Larger key wins; equal keys go to the lower column.
+__device__ __forceinline__ void key_merge(float& k, int& c, float& lg, float k2_, int c2, float lg2) {
+  if (k2_ > k || (k2_ == k && c2 < c)) {
+    k = k2_;
+    c = c2;
+    lg = lg2;
+  }
+}
+
 __global__ __launch_bounds__(256) void lm_merge_kernel(const float4* __restrict__ part, int n_parts,
-                                                       float k2, dg_row_stats* __restrict__ stats) {
-  __shared__ float sm[4], sz[4], sw[4];
-  __shared__ int sa[4];
+                                                       float k2, dg_row_stats* __restrict__ stats,
+                                                       const float4* __restrict__ gpart) {
+  __shared__ float sm[4], sz[4], sw[4], sk[4], sl[4];
+  __shared__ int sa[4], sc[4];
   const int row = blockIdx.x;
   float m = -INFINITY, z = 0.f, w = 0.f;
   int a = 0x7fffffff;
@@ -80,6 +91,32 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(const float4* __restrict_
     stats[row].argmax = a;
     stats[row].entropy = lz - 0.69314718055994531f * (w / z);
   }
+  if (!gpart) return;
+  // sampled candidate: the largest key over the tiles
+  float gk = -INFINITY, gl = 0.f;
+  int gc = 0x7fffffff;
+  const float4* gp = gpart + (int64_t)row * n_parts;
+  for (int i = threadIdx.x; i < n_parts; i += 256) {
+    const float4 v = gp[i];
+    key_merge(gk, gc, gl, v.x, __float_as_int(v.y), v.z);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float k_ = __shfl_xor(gk, o, WAVE), l_ = __shfl_xor(gl, o, WAVE);
+    const int c_ = __shfl_xor(gc, o, WAVE);
+    key_merge(gk, gc, gl, k_, c_, l_);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sk[wave] = gk;
+    sc[wave] = gc;
+    sl[wave] = gl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int q = 1; q < 4; ++q) key_merge(gk, gc, gl, sk[q], sc[q], sl[q]);
+    stats[row].sample = gc;
+    stats[row].sample_logit = gl;
+  }
 }
 
 __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict__ stats, int C, int V,
@@ -97,12 +134,13 @@ __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict_
   if (i < C) {
     sr = stats[row];
     held = committed[row] != 0;
-    y = held ? canvas[row] : sr.argmax;
+    const bool drawn = mode.candidate == DG_CAND_SAMPLE;
+    y = held ? canvas[row] : (drawn ? sr.sample : sr.argmax);
     H = sr.entropy;
     if (mode.confidence == DG_CONF_ENTROPY) {
       c = -H;
     } else {
-      const float Ly = held ? sr.held_logit : sr.max_logit;
+      const float Ly = held ? sr.held_logit : (drawn ? sr.sample_logit : sr.max_logit);
       c = (Ly - sr.max_logit) / tau - sr.log_z;
     }
     cs[i] = c;
@@ -138,7 +176,6 @@ __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict_
   }
   sr.conf = c;
   sr.accepted = accept ? 1 : 0;
-  sr.pad = 0;
   stats[row] = sr;
   if (stats_out) stats_out[row] = sr;
 }
@@ -146,10 +183,10 @@ __global__ __launch_bounds__(1024) void sampler_kernel(dg_row_stats* __restrict_
 }  // namespace
 
 void launch_lm_merge(hipStream_t s, const float4* part, int n_parts, int rows, float tau,
-                     void* stats) {
+                     void* stats, const float4* gpart) {
   const float k2 = 1.4426950408889634f / tau;
   hipLaunchKernelGGL(lm_merge_kernel, dim3(rows), dim3(256), 0, s, part, n_parts, k2,
-                     (dg_row_stats*)stats);
+                     (dg_row_stats*)stats, gpart);
 }
 
 void launch_sampler(hipStream_t s, void* stats, int n_req, int C, int V, int32_t* canvas,

@@ -21,6 +21,7 @@
 // when there are several row chunks.
 #include "common.h"
 #include "kernels.h"
+#include "philox.h"
 
 namespace {
 
@@ -36,11 +37,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // of the row's held token writes that logit to held_logit[row * held_stride].
 // Requires K % 128 == 0 and V % 256 == 0 (the configuration check enforces
 // d % 256 == 0 and V % 256 == 0).
+// With GUMBEL the epilogue also draws each row's sampled candidate over the
+// tile: the column with the largest L / tau + G (G the Gumbel noise of the
+// row's canvas position and that column, lowest column on ties) goes to
+// gpart[row][nt] = (key, column bits, its logit, 0).
+template <bool GUMBEL>
 __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
                                                      const bf16_t* __restrict__ E, int V,
                                                      const int32_t* __restrict__ held, float k2,
                                                      float4* __restrict__ part, float* __restrict__ held_logit,
-                                                     int held_stride) {
+                                                     int held_stride, GumbelDraw gd) {
   // four distinct objects: the compiler then orders each buffer's LDS reads
   // only after the copies into that buffer
   __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
@@ -165,6 +171,37 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
       if (l16 == 0)
         red[cq * LM_ROWS + 128 * rh + 16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), zt};
     }
+  float4* red2 = reinterpret_cast<float4*>(&r2[0][0]);  // [4][256] sampled-candidate partials
+  if constexpr (GUMBEL) {
+    // one Philox call per (lane, row) gives the noise of the lane's four
+    // columns cw + 16 nb + l16: they share the counter, word nb each
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 128 * rh + 16 * mt + 4 * grp + r;
+        const int rowc = min(row0 + rl, rows - 1);
+        const int rq = rowc / gd.C, pos = rowc - rq * gd.C;
+        const u32x4 wd = philox4x32_10((uint32_t)(cw + l16), (uint32_t)pos,
+                                       ((uint32_t)gd.st.block[rq] << 16) | (uint32_t)gd.step,
+                                       0x80000000u | (uint32_t)gd.st.slot[rq], gd.st.key_lo[rq], gd.st.key_hi[rq]);
+        float best = -INFINITY, bl = 0.f;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const float key = acc[nb][mt][r] * gd.k1 + gumbel_of_word(wd[nb]);
+          if (key > best) {
+            best = key;
+            bi = cw + 16 * nb + l16;
+            bl = acc[nb][mt][r];
+          }
+        }
+        const float mk = row16_max(best);
+        const int ci = row16_min(best == mk ? bi : 0x7fffffff);
+        const float lg = row16_max(bi == ci ? bl : -INFINITY);
+        if (l16 == 0) red2[cq * LM_ROWS + rl] = float4{mk, __int_as_float(ci), lg, 0.f};
+      }
+  }
   __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -202,6 +239,16 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
       }
     }
     part[(int64_t)(row0 + tid) * NT + nt] = p;
+    if constexpr (GUMBEL) {
+      // column quarters in column order: a later quarter wins only with a larger key
+      float4 g = red2[tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 o = red2[w * LM_ROWS + tid];
+        if (o.x > g.x) g = o;
+      }
+      gd.gpart[(int64_t)(row0 + tid) * NT + nt] = g;
+    }
   }
 }
 
@@ -212,9 +259,15 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
 int lmhead_parts(int V) { return V / LM_COLS; }
 
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
-                   const int32_t* held, float tau, float4* part, float* held_logit, int held_stride) {
+                   const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
+                   const GumbelDraw* gumbel) {
   const float k2 = 1.4426950408889634f / tau;
   const int NT = V / LM_COLS;
-  hipLaunchKernelGGL(lmhead_kernel, dim3(NT * div_up(rows, LM_ROWS)), dim3(512), 0, s, a, rows, K, embed, V, held,
-                     k2, part, held_logit, held_stride);
+  const dim3 grid(NT * div_up(rows, LM_ROWS));
+  if (gumbel)
+    hipLaunchKernelGGL(lmhead_kernel<true>, grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part, held_logit,
+                       held_stride, *gumbel);
+  else
+    hipLaunchKernelGGL(lmhead_kernel<false>, grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part,
+                       held_logit, held_stride, GumbelDraw{});
 }

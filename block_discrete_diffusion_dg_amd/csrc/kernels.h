@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "common.h"
+#include "philox.h"
 
 // k_elem.hip
 void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
@@ -28,8 +29,18 @@ void launch_qkv(hipStream_t s, const bf16_t* u, int rows, int d, const bf16_t* w
 void launch_resid(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* w, int N, float* h, float* ss);
 
 // k_lmhead.hip (LM head with fused vocabulary statistics; embed fragment-major)
+// Sampled candidates drawn in the LM-head epilogue (Gumbel-max): the
+// requests' Philox keys, blocks and slots, canvas rows per request, the step,
+// 1 / tau, and the per-tile partials [rows][V/256] (key, column, logit, 0).
+struct GumbelDraw {
+  SampleTable st;
+  int C, step;
+  float k1;
+  float4* gpart;
+};
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
-                   const int32_t* held, float tau, float4* part, float* held_logit, int held_stride);
+                   const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
+                   const GumbelDraw* gumbel);
 int lmhead_parts(int V);
 
 // k_attn.hip
@@ -83,14 +94,16 @@ void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y
                         float eps, bf16_t* u);
 
 // k_head.hip
+// gpart: the sampled-candidate partials of launch_lmhead, or nullptr.
 void launch_lm_merge(hipStream_t s, const float4* part, int n_parts, int rows, float tau,
-                     void* stats);
+                     void* stats, const float4* gpart);
 // Sampler options: confidence (dg_confidence), adaptive stopping threshold
 // (0 = off), the per-slot argmax of the previous step [slots][C] (read, then
 // overwritten), which requests of the batch have one (bit r), and the
 // optional per-request stop flags.
 struct SamplerMode {
   int confidence;
+  int candidate;  // dg_candidate
   float stop_entropy;
   int32_t* prev_argmax;
   uint32_t prev_valid;

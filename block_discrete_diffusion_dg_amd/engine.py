@@ -203,7 +203,7 @@ class Engine:
 
     def _args(self, reqs, canvas, committed, step, n_steps, seeds, blocks, stats,
               confidence: str = "prob", stop_entropy: float = 0.0,
-              stop: Optional[torch.Tensor] = None):
+              stop: Optional[torch.Tensor] = None, candidate: str = "argmax"):
         n = len(reqs)
         a = B.DGStepArgs()
         a.n_req = n
@@ -225,6 +225,7 @@ class Engine:
         if stop is not None:
             assert stop.dtype == torch.int32 and stop.is_cuda and stop.numel() >= n
         a.d_stop = _ptr(stop)
+        a.candidate = B.CANDIDATE[candidate]
         return a
 
     # ------------------------------------------------------------------ the calls
@@ -238,11 +239,12 @@ class Engine:
 
     def denoise_step(self, reqs, canvas, committed, step, n_steps, seeds, blocks,
                      stats: Optional[torch.Tensor] = None, confidence: str = "prob",
-                     stop_entropy: float = 0.0, stop: Optional[torch.Tensor] = None):
+                     stop_entropy: float = 0.0, stop: Optional[torch.Tensor] = None,
+                     candidate: str = "argmax"):
         """One denoising step; `stop` (device int32 [n_req]) receives 1 where
         adaptive stopping ended the request's block at this step."""
         a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
-                       stop_entropy, stop)
+                       stop_entropy, stop, candidate)
         self._check(self.lib.dg_denoise_step(self.ctx, _stream(), ctypes.byref(a)))
 
     def commit_block(self, reqs, canvas):
@@ -287,18 +289,18 @@ class Engine:
         return out
 
     def test_head(self, reqs, h, canvas, committed, step, n_steps, seeds, blocks, stats=None,
-                  confidence: str = "prob", stop_entropy: float = 0.0, stop=None):
+                  confidence: str = "prob", stop_entropy: float = 0.0, stop=None, candidate: str = "argmax"):
         a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
-                       stop_entropy, stop)
+                       stop_entropy, stop, candidate)
         self._check(self.lib.dg_test_head(self.ctx, _stream(), ctypes.byref(a), h.data_ptr()))
 
 
 def stats_fields(stats: torch.Tensor) -> Dict[str, torch.Tensor]:
-    """Split a [rows][8] int32 dg_row_stats tensor into named CPU tensors."""
+    """Split a [rows][10] int32 dg_row_stats tensor into named CPU tensors."""
     s = stats.cpu()
     f = s.view(torch.float32)
     return dict(max_logit=f[:, 0], log_z=f[:, 1], held_logit=f[:, 2], conf=f[:, 3],
-                argmax=s[:, 4], accepted=s[:, 5], entropy=f[:, 6])
+                argmax=s[:, 4], accepted=s[:, 5], entropy=f[:, 6], sample=s[:, 7], sample_logit=f[:, 8])
 
 
 def gpu_weights(cfg: ModelConfig, model_seed: int = 0, gain_jitter: float = 0.0,

@@ -118,8 +118,21 @@ typedef struct dg_row_stats {
   int32_t argmax;    /* lowest v with L_iv = M_i */
   int32_t accepted;  /* 1 if position i is in the accepted set */
   float entropy;     /* H_i = -sum_v p_iv ln p_iv, p_i = softmax(L_i / tau_s), nats */
+  int32_t sample;    /* sampled candidate (DG_CAND_SAMPLE only, else unspecified) */
+  float sample_logit;/* L_i[sample] */
   int32_t pad;
 } dg_row_stats;
+
+/* The candidate of a position that is not committed:
+ *   DG_CAND_ARGMAX  the most likely token (lowest id on ties);
+ *   DG_CAND_SAMPLE  a draw from softmax(L_i / tau_s) by the Gumbel-max
+ *                   identity: argmax_v (L_iv / tau_s - ln(-ln u_iv)), lowest
+ *                   id on ties. u_iv is word ((v >> 4) & 3) of Philox4x32-10
+ *                   with key = seed and counter = (v & ~0x30, i,
+ *                   (block << 16) | step, 0x80000000 | req), as
+ *                   ((word >> 9) + 1/2) * 2^-23. The pages accept the most
+ *                   likely tokens (explainer §3.3); sampling is a variant. */
+typedef enum { DG_CAND_ARGMAX = 0, DG_CAND_SAMPLE = 1 } dg_candidate;
 
 /* How the sampler ranks canvas positions (explainer §3.3):
  *   DG_CONF_PROB     c_i = log p_tau(y_i), the candidate's log-probability;
@@ -143,6 +156,8 @@ typedef enum { DG_CONF_PROB = 0, DG_CONF_ENTROPY = 1 } dg_confidence;
  *                step of the block; the step then accepts every position.
  *   d_stop       optional device int32 [n_req]: 1 where the block stopped at
  *                this step, else 0 (NULL = not reported)
+ *   candidate    dg_candidate (0 = DG_CAND_ARGMAX; another value: DG_EINVAL);
+ *                needs block < 2^15 and n_steps < 2^16 for DG_CAND_SAMPLE
  * The library keeps each request slot's argmax of its last step in the
  * workspace. It counts as the previous step only for steps of the same block:
  * after dg_create, dg_init_canvas, dg_commit_block or dg_reset of a slot, the
@@ -163,6 +178,7 @@ typedef struct dg_step_args {
   int32_t confidence;
   float stop_entropy;
   int32_t *d_stop;
+  int32_t candidate;
 } dg_step_args;
 
 typedef struct dg_ctx dg_ctx;
@@ -238,7 +254,8 @@ dg_status dg_init_canvas(dg_ctx *ctx, void *stream, const dg_step_args *a);
  *   entropy, held-token logit) without materialising the logits; sampler:
  *     tau_s = tau_first + (tau_last - tau_first) * (step-1)/(n_steps-1),
  *     k_s   = floor(step * canvas / n_steps),
- *     candidate y_i = x_i if committed else argmax_i,
+ *     candidate y_i = x_i if committed else argmax_i (or a sample, see
+ *     dg_candidate),
  *     c_i = (L_i[y_i] - M_i)/tau_s - log Z_i  (or -H_i, see dg_confidence),
  *     k_s = canvas instead when the block stops early (stop_entropy),
  *     the k_s positions of highest c_i (ties: lower i) take y_i and are marked

@@ -34,6 +34,8 @@ extern "C" {
  *   hid      bf16 [rows*k][F]        routed expert SwiGLU activations
  *   hid_s    bf16 [rows][Fs]         shared expert SwiGLU activations
  *   y        fp32 [rows*k][d]        routed expert outputs (weighted)
+ *   lm_gpart float4 [rows][V/256]    sampled-candidate partials per
+ *                                    vocabulary tile (key, id, logit, 0)
  *   stats    dg_row_stats [rows]     per-row LM-head statistics
  *   ss       fp32 [d/64][rows]       partial sums of squares of h per
  *                                    64-column tile (output projection)
@@ -57,7 +59,7 @@ extern "C" {
 
 typedef struct dg_ws_layout {
   size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
-      slot, hid, hid_s, y, lm_part, stats, ids, ss, zpart, sync, prev, total;
+      slot, hid, hid_s, y, lm_part, lm_gpart, stats, ids, ss, zpart, sync, prev, total;
 } dg_ws_layout;
 
 dg_status dg_workspace_layout(const dg_config *cfg, dg_ws_layout *out);

@@ -60,7 +60,7 @@ def test_buffer_sizes(lib):
     assert lay.total == ws > 0
     offs = [getattr(lay, n) for n in B.WS_FIELDS[:-1]]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-    assert ctypes.sizeof(B.DGRowStats) == 32
+    assert ctypes.sizeof(B.DGRowStats) == 40
 
 
 def test_binding_structs_match_the_c_header(tmp_path):

@@ -276,6 +276,64 @@ def test_entropy_confidence_and_adaptive_stop(model, n_req):
     assert np.array_equal(stop4, np.zeros(n_req))
 
 
+def _gumbel_keys(L_row, tau, seed, pos, step, block, req):
+    from oracle.philox import gumbel_uniforms
+    u = gumbel_uniforms(seed, pos, step, block, req, L_row.shape[0])
+    return L_row / tau - np.log(-np.log(u))
+
+
+@pytest.mark.parametrize("model,n_req", [(synth.TINY, 2), (synth.FULL, 1)])
+def test_sampled_candidates_match_the_oracle(model, n_req):
+    """DG_CAND_SAMPLE: the Gumbel-max draw over the whole vocabulary equals
+    the oracle's draw with the same uniforms on the same bf16 operand, except
+    where the oracle's two best keys lie within the float32 band; the sampler
+    then ranks the drawn candidates exactly as the oracle's sampler does."""
+    say(f"[sample] V={model.vocab} n_req={n_req}")
+    C = model.canvas
+    rows = n_req * C
+    eng, hw = _zero_layer_engine(model, max_rows=rows, max_requests=n_req)
+    step, n_steps = 4, 12
+    h, canvas, committed = _head_case(model, n_req, step, n_steps, seed=9)
+    reqs = list(range(n_req))
+    seeds, blocks = [31 + r for r in reqs], [3] * n_req
+    x_dev, m_dev = canvas.cuda(), committed.cuda()
+    stats = eng.new_stats(n_req)
+    eng.test_head(reqs, h.cuda(), x_dev, m_dev, step, n_steps, seeds, blocks, stats, candidate="sample")
+    torch.cuda.synchronize()
+    st = stats_fields(stats)
+    u_gpu = eng.ws_view("u", torch.bfloat16, (rows, model.d_model)).cpu()
+    L_u = om.f64(u_gpu) @ om.f64(hw.embed).T
+    tau = om.tau_at(step, n_steps, model.tau_first, model.tau_last)
+    scale = np.abs(L_u).max()
+    sample = st["sample"].numpy()
+    mismatches = 0
+    for row in range(rows):
+        r, i = divmod(row, C)
+        key = _gumbel_keys(L_u[row], tau, seeds[r], i, step, blocks[r], r)
+        top = np.argsort(key)[::-1][:2]
+        assert key[sample[row]] >= key[top[0]] - 1e-4 * (1 + abs(key[top[0]]))
+        assert abs(st["sample_logit"].double().numpy()[row] - L_u[row, sample[row]]) < 1e-5 * scale
+        if key[top[0]] - key[top[1]] > 1e-4 * (1 + abs(key[top[0]])):
+            assert sample[row] == top[0], row
+        elif sample[row] != top[0]:
+            mismatches += 1
+    say(f"  draws within the tie band: {mismatches}")
+    x_np, m_np = canvas.numpy().astype(np.int64), committed.numpy()
+    x_new, m_new = x_dev.cpu().numpy(), m_dev.cpu().numpy()
+    for r in reqs:
+        sl = slice(r * C, (r + 1) * C)
+        drawn = (sample[sl].astype(np.int64), st["sample_logit"].double().numpy()[sl])
+        xo, mo, c, acc = om.sample(x_np[sl], m_np[sl], st["max_logit"].double().numpy()[sl],
+                                   st["argmax"].numpy()[sl], st["log_z"].double().numpy()[sl],
+                                   st["held_logit"].double().numpy()[sl], tau, step, n_steps, seeds[r],
+                                   blocks[r], r, model.vocab, drawn=drawn)
+        assert np.abs(st["conf"].double().numpy()[sl] - c).max() < 1e-4
+        k_s = om.commit_count(step, n_steps, C)
+        if tie_gap_ok(c, k_s, 1e-4):
+            assert np.array_equal(st["accepted"].numpy()[sl].astype(bool), acc)
+            assert np.array_equal(x_new[sl], xo) and np.array_equal(m_new[sl], mo)
+
+
 def test_init_canvas_matches_philox():
     model = synth.TINY
     eng, _ = _zero_layer_engine(model, max_rows=2 * model.canvas, max_requests=2)

@@ -10,6 +10,7 @@ import torch
 from block_discrete_diffusion_dg_amd import synth
 from block_discrete_diffusion_dg_amd.engine import stats_fields
 from oracle import model as om
+from oracle import philox as philox_mod
 from tests.gpu_util import REL_TOL, make_engine, max_rel, say, tie_gap_ok
 
 pytestmark = pytest.mark.gpu
@@ -25,8 +26,9 @@ def _oracle_request(eng, cfg, slot, length):
     return req
 
 
-@pytest.mark.parametrize("confidence,stop_entropy", [("prob", 0.0), ("entropy", 1e9)])
-def test_tiny_block_loop_parity(confidence, stop_entropy):
+@pytest.mark.parametrize("confidence,stop_entropy,candidate",
+                         [("prob", 0.0, "argmax"), ("entropy", 1e9, "argmax"), ("prob", 0.0, "sample")])
+def test_tiny_block_loop_parity(confidence, stop_entropy, candidate):
     """With entropy confidence and a threshold every mean entropy is under,
     adaptive stopping reduces to "the argmax did not change since the
     previous step": both sides must agree on it wherever the argmax is
@@ -62,16 +64,27 @@ def test_tiny_block_loop_parity(confidence, stop_entropy):
         m_in = m.cpu().numpy()
         stats = eng.new_stats(1)
         eng.denoise_step([0], x, m, s, S, [seed], [block], stats, confidence=confidence,
-                         stop_entropy=stop_entropy, stop=stop)
+                         stop_entropy=stop_entropy, stop=stop, candidate=candidate)
         torch.cuda.synchronize()
         st = stats_fields(stats)
         keep = {}
         # teacher-forced: the oracle compares with the GPU's previous argmax
         xo, mo = om.denoise_step(hw, cfg, gpu_req, x_in, m_in, s, S, seed, block, 0, keep,
-                                 confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev)
+                                 confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev,
+                                 candidate=candidate)
         big = np.abs(keep["logits"]).max()
         assert max_rel(st["max_logit"], keep["M"]) <= REL_TOL
         clear = np.array([tie_gap_ok(keep["logits"][i], 1, 2 * REL_TOL * big) for i in range(C)])
+        if candidate == "sample":
+            # draws: equal wherever the oracle's two best Gumbel keys are apart
+            # by more than the logits' error over tau
+            for i in range(C):
+                key = keep["logits"][i] / keep["tau"] - np.log(-np.log(
+                    philox_mod.gumbel_uniforms(seed, i, s, block, 0, cfg.vocab)))
+                ok = tie_gap_ok(key, 1, 2 * REL_TOL * big / keep["tau"])
+                clear[i] &= ok
+                if ok:
+                    assert st["sample"].numpy()[i] == keep["drawn"][0][i], i
         assert np.array_equal(st["argmax"].numpy()[clear], keep["a"][clear])
         assert np.abs(st["entropy"].double().numpy() - keep["H"]).max() <= REL_TOL * big / keep["tau"]
         assert np.abs(st["conf"].double().numpy() - keep["c"]).max() <= REL_TOL * big / keep["tau"] * 4
