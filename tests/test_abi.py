@@ -164,6 +164,15 @@ def test_argument_and_capacity_errors_launch_nothing(lib):
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
         assert b"NaN" in lib.dg_last_error(h)
         a.stop_entropy = 0.0
+        a.candidate = 2  # neither DG_CAND_ARGMAX nor DG_CAND_SAMPLE
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        assert b"candidate" in lib.dg_last_error(h)
+        a.candidate = B.CANDIDATE["sample"]
+        blocks[0] = 1 << 15  # beyond the counter's block field
+        assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_EINVAL
+        assert b"block" in lib.dg_last_error(h)
+        blocks[0] = 0
+        a.candidate = B.CANDIDATE["argmax"]
         a.n_req = 3  # 3 * 32 rows > max_rows 64
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_ECAPACITY
         assert lib.dg_reset(h, 0) == B.DG_OK and lib.dg_cache_len(h, 0) == 0
