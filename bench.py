@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="full", choices=["full", "long", "batch", "tiny", "one_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--n-req", type=int, default=0,
+                    help="override the workload's number of requests (batch-size sweep; 0 = the workload's)")
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the extra measurement with FP8 expert weights")
     ap.add_argument("--copy-probe-mib", type=int, default=512,
@@ -152,7 +154,7 @@ def main():
     from block_discrete_diffusion_dg_amd.engine import Engine, gpu_weights
 
     wl = synth.WORKLOADS[args.workload]
-    cfg, P, S, n_req = wl.model, wl.prefix, wl.n_steps, wl.n_req
+    cfg, P, S, n_req = wl.model, wl.prefix, wl.n_steps, args.n_req or wl.n_req
     C = cfg.canvas
     rows = n_req * C
     dev = "cuda:0"
@@ -313,7 +315,7 @@ def main():
         # reaches on this GPU in the same run
         out["roofline"]["peak_measured"] = round(copy_gbs, 1)
         out["roofline"]["frac_measured"] = round(out["roofline"]["achieved"] / copy_gbs, 4)
-    if args.workload == "full":
+    if args.workload == "full" and not args.n_req:
         out["variants"] = {"sampled_candidates": sampled_variant(args, eng, reqs, seeds, blocks, x, m, S)}
         if not args.no_fp8_variant:
             out["variants"]["fp8_experts"] = fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
