@@ -143,7 +143,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoising step "
-              "is measured on a single MI355X; multi-GPU sharding is not part of this build.",
+              "is measured on a single MI355X; multi-GPU sharding is not implemented.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -27,7 +27,7 @@ Sources (cited by page and section):
                the KV cache, denoising uses bidirectional attention over the
                canvas; confident tokens are fixed step by step
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   pre-norm RMSNorm (eps 1e-6) before attention and MoE plus a final norm;
   rotate-half RoPE, theta 10000, canvas at absolute positions P..P+C-1;
   scale 1/sqrt(head_dim), no soft-cap, no sliding window;
