@@ -30,6 +30,8 @@ Parity status per function (what pins each, see tests/test_oracle_pins.py):
   fp8 (E4M3)      torch's float8_e4m3fn decode and encode; round trip of
                   every finite code; ties to even; row-exponent minimality;
                   half-ulp error bound
+  ar_step         equals a causal pass over the whole sequence from an
+                  empty cache (K/V rows, last-row logits, next token)
   metrics         the pages' worked TPF/TPS example
 Fidelity to the trained DiffusionGemma model: parity unpinned (no weights).
 """

@@ -459,6 +459,24 @@ def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step:
     return x_new, m_new
 
 
+def ar_step(weights, cfg, req: Request, token: int):
+    """One autoregressive decode step: the causal pass over the single token
+    at position req.length appends its K/V rows, and the LM head over that
+    row gives the next token, the greedy argmax (lowest id on ties). The
+    explainer's §5.2 compares a denoising step with one such step.
+    Returns (next token, the row's logits)."""
+    ids = np.asarray([token], np.int64)
+    h, ks, vs = forward_rows(weights, cfg, req, ids, causal=True)
+    P = req.length
+    assert P + 1 <= req.k.shape[1]
+    for l in range(cfg.n_layers):
+        req.k[l, P:P + 1] = ks[l]
+        req.v[l, P:P + 1] = vs[l]
+    req.length = P + 1
+    L = logits(h, weights.final_norm, weights.embed, cfg)[0]
+    return int(np.argmax(L)), L
+
+
 def generate_block(weights, cfg, req: Request, n_steps: int, seed: int, block: int,
                    request: int, confidence: str = "prob", stop_entropy: float = 0.0):
     """Denoise one block from uniform noise for at most n_steps (fewer when

@@ -531,6 +531,31 @@ def test_denoise_leaves_cache_untouched_and_full_block_loop_runs():
     assert m_final.all() and req.length == 64 + cfg.canvas
 
 
+def test_ar_step_equals_a_full_causal_pass():
+    """The incremental decode step (cached prefix + one row) against a causal
+    pass over the whole sequence from an empty cache: the same K/V rows and
+    the same last-row logits, so the same next token."""
+    cfg, w = _tiny_model(n_layers=2)
+    prompt = synth.make_prompt(40, cfg.vocab, 3).numpy().astype(np.int64)
+    req = om.Request(cfg, 64)
+    om.prefill(w, cfg, req, prompt)
+    tok = int(prompt[-1])
+    seq = list(prompt)
+    for _ in range(3):
+        nxt, L = om.ar_step(w, cfg, req, tok)
+        seq.append(tok)
+        full = om.Request(cfg, 64)
+        h, ks, vs = om.forward_rows(w, cfg, full, np.asarray(seq, np.int64), causal=True)
+        L_full = om.logits(h[-1:], w.final_norm, w.embed, cfg)[0]
+        assert np.allclose(L, L_full, rtol=1e-9, atol=1e-9)
+        assert nxt == int(np.argmax(L_full))
+        for l in range(cfg.n_layers):
+            assert np.allclose(req.k[l, :len(seq)], ks[l], rtol=1e-9, atol=1e-12)
+            assert np.allclose(req.v[l, :len(seq)], vs[l], rtol=1e-9, atol=1e-12)
+        assert req.length == len(seq)
+        tok = nxt
+
+
 # ----------------------------------------------------------------------------- metrics
 
 def test_throughput_worked_example():
