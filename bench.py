@@ -316,11 +316,36 @@ def main():
         out["roofline"]["peak_measured"] = round(copy_gbs, 1)
         out["roofline"]["frac_measured"] = round(out["roofline"]["achieved"] / copy_gbs, 4)
     if args.workload == "full" and not args.n_req:
-        out["variants"] = {"sampled_candidates": sampled_variant(args, eng, reqs, seeds, blocks, x, m, S)}
+        out["variants"] = {"sampled_candidates": sampled_variant(args, eng, reqs, seeds, blocks, x, m, S),
+                           "ar_step": ar_variant(args, eng, reqs, P, ms)}
         if not args.no_fp8_variant:
             out["variants"]["fp8_experts"] = fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
                                                          blocks, canvas0, dev)
     print(json.dumps(out), flush=True)
+
+
+def ar_variant(args, eng, reqs, P, denoise_ms):
+    """Greedy autoregressive decode steps (one token per request, causal pass
+    plus a one-row LM head) at the same prefix: the explainer's §5.2 compares
+    a denoising step with one such step (3.2x on its hardware)."""
+    import torch
+    tok = torch.zeros(len(reqs), dtype=torch.int32, device=f"cuda:{torch.cuda.current_device()}")
+    for _ in range(args.warmup):
+        tok = eng.ar_step(reqs, tok)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        tok = eng.ar_step(reqs, tok)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    for r in reqs:
+        eng.set_cache_len(r, P)
+    log(f"ar step: {ms:.3f} ms")
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(1e3 / ms * len(reqs), 1),
+            "denoise_over_ar": round(denoise_ms / ms, 3)}
 
 
 def sampled_variant(args, eng, reqs, seeds, blocks, x, m, S):

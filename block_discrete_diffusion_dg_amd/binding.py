@@ -92,6 +92,7 @@ SIGNATURES = {
     "dg_pack_weight": (c_i32, [c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_quantize_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32]),
+    "dg_ar_step": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp, c_vp]),
     "dg_init_canvas": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
     "dg_denoise_step": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),
     "dg_commit_block": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp]),

@@ -477,6 +477,40 @@ dg_status dg_prefill(dg_ctx* c, void* stream, int32_t req, const int32_t* d_ids,
   return DG_OK;
 }
 
+dg_status dg_ar_step(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req, const int32_t* d_tokens,
+                     int32_t* d_next) {
+  dg_status st = check_ctx(c);
+  if (st) return st;
+  const dg_config& g = c->cfg;
+  if (n_req <= 0 || n_req > DG_MAX_REQ || !req || !d_tokens || !d_next)
+    return c->fail(DG_EINVAL, "ar_step: null pointer or n_req outside 1..16");
+  if (n_req > g.max_rows) return c->fail(DG_ECAPACITY, "ar_step: n_req exceeds max_rows");
+  for (int r = 0; r < n_req; ++r) {
+    if (req[r] < 0 || req[r] >= g.max_requests) return c->fail(DG_EINVAL, "ar_step: slot out of range");
+    for (int q = 0; q < r; ++q)
+      if (req[q] == req[r]) return c->fail(DG_EINVAL, "ar_step: duplicate slot");
+    if ((int64_t)c->len[req[r]] + 1 > g.max_ctx) return c->fail(DG_ECAPACITY, "ar_step: cache is full");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const dg_ws_layout& L = c->lay;
+  ReqTable rt = make_table(c, n_req, req, 1);
+  launch_rope_table(s, rt, g.head_dim, g.rope_theta, c->buf<float2>(L.rope));
+  run_embed(c, s, d_tokens, n_req, true);
+  // causal, with every layer complete (the last one feeds the final norm)
+  for (int l = 0; l < g.n_layers; ++l) run_layer(c, s, l, rt, 1, false, gain_after(c, l));
+  dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
+  launch_lmhead(s, c->buf<bf16_t>(L.u), n_req, g.d_model, c->embed, g.vocab, d_tokens, 1.0f,
+                c->buf<float4>(L.lm_part), &stats[0].held_logit, (int)(sizeof(dg_row_stats) / sizeof(float)),
+                nullptr);
+  launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), n_req, 1.0f, stats, nullptr);
+  (void)hipMemcpy2DAsync(d_next, sizeof(int32_t), &stats[0].argmax, sizeof(dg_row_stats), sizeof(int32_t), n_req,
+                         hipMemcpyDeviceToDevice, s);
+  st = c->check_hip("dg_ar_step");
+  if (st) return st;
+  for (int r = 0; r < n_req; ++r) c->len[req[r]] += 1;
+  return DG_OK;
+}
+
 dg_status dg_init_canvas(dg_ctx* c, void* stream, const dg_step_args* a) {
   dg_status st = check_ctx(c);
   if (st) return st;

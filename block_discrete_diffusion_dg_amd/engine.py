@@ -247,6 +247,15 @@ class Engine:
                        stop_entropy, stop, candidate)
         self._check(self.lib.dg_denoise_step(self.ctx, _stream(), ctypes.byref(a)))
 
+    def ar_step(self, reqs, tokens: torch.Tensor) -> torch.Tensor:
+        """One greedy autoregressive step per request: appends the tokens'
+        K/V rows and returns the next tokens (device int32 [n_req])."""
+        assert tokens.dtype == torch.int32 and tokens.is_cuda and tokens.numel() == len(reqs)
+        arr = (ctypes.c_int32 * len(reqs))(*reqs)
+        nxt = torch.empty(len(reqs), dtype=torch.int32, device=tokens.device)
+        self._check(self.lib.dg_ar_step(self.ctx, _stream(), len(reqs), arr, tokens.data_ptr(), nxt.data_ptr()))
+        return nxt
+
     def commit_block(self, reqs, canvas):
         arr = (ctypes.c_int32 * len(reqs))(*reqs)
         self._check(self.lib.dg_commit_block(self.ctx, _stream(), len(reqs), arr, canvas.data_ptr()))

@@ -272,6 +272,17 @@ dg_status dg_denoise_step(dg_ctx *ctx, void *stream, const dg_step_args *a);
 dg_status dg_commit_block(dg_ctx *ctx, void *stream, int32_t n_req, const int32_t *req,
                           const int32_t *d_canvas);
 
+/* One autoregressive decode step per request (AR mode; the explainer's §5.2
+ * compares a denoising step with one such step): the causal encoder pass over
+ * d_tokens[r] (device int32 [n_req]) at position len of slot req[r] appends
+ * that token's K/V rows (len += 1), and the LM head over its row gives
+ * d_next[r] (device int32 [n_req]) = the greedy argmax, lowest id on ties.
+ * Needs 1 <= n_req <= min(16, max_rows), distinct slots and len + 1 <=
+ * max_ctx (else DG_EINVAL / DG_ECAPACITY, nothing launched). The workspace's
+ * first n_req LM-head statistics rows are overwritten. */
+dg_status dg_ar_step(dg_ctx *ctx, void *stream, int32_t n_req, const int32_t *req, const int32_t *d_tokens,
+                     int32_t *d_next);
+
 /* Committed KV length of a request slot (host-side bookkeeping), or -1. */
 int32_t dg_cache_len(const dg_ctx *ctx, int32_t req);
 

@@ -175,6 +175,14 @@ def test_argument_and_capacity_errors_launch_nothing(lib):
         a.candidate = B.CANDIDATE["argmax"]
         a.n_req = 3  # 3 * 32 rows > max_rows 64
         assert lib.dg_denoise_step(h, None, ctypes.byref(a)) == B.DG_ECAPACITY
+        # AR step: bad sizes and slots, and a full cache, launch nothing
+        one = (ctypes.c_int32 * 1)(0)
+        assert lib.dg_ar_step(h, None, 0, one, 0x2000, 0x3000) == B.DG_EINVAL
+        assert lib.dg_ar_step(h, None, 1, one, None, 0x3000) == B.DG_EINVAL
+        assert lib.dg_ar_step(h, None, 2, dup, 0x2000, 0x3000) == B.DG_EINVAL
+        lib.dg_set_cache_len(h, 0, 256)
+        assert lib.dg_ar_step(h, None, 1, one, 0x2000, 0x3000) == B.DG_ECAPACITY
+        assert lib.dg_cache_len(h, 0) == 256
         assert lib.dg_reset(h, 0) == B.DG_OK and lib.dg_cache_len(h, 0) == 0
         assert lib.dg_reset(h, 9) == B.DG_EINVAL
     finally:

@@ -166,3 +166,31 @@ def test_step_is_deterministic_and_batch_matches_single():
     assert max_rel(b["max_logit"], a["max_logit"]) < 1e-4
     assert torch.equal(a["argmax"], b["argmax"])
     assert eng.moe_counters()["spin_timeouts"] == 0
+
+
+def test_ar_steps_match_the_oracle():
+    """AR mode: greedy decode steps of two requests appended to their caches;
+    next tokens equal the oracle's argmax wherever its two best logits are
+    apart by more than the band, and the appended K/V rows match."""
+    cfg = synth.TINY
+    P, n_steps = 40, 3
+    eng, hw = make_engine(cfg, max_ctx=128, max_requests=2, max_rows=cfg.canvas)
+    prompts = [synth.make_prompt(P, cfg.vocab, 21 + r) for r in range(2)]
+    for r in range(2):
+        eng.prefill(r, prompts[r].cuda())
+    tokens = torch.tensor([int(p[-1]) for p in prompts], dtype=torch.int32, device="cuda")
+    for step in range(n_steps):
+        say(f"[ar] step {step}")
+        refs = [_oracle_request(eng, cfg, r, P + step) for r in range(2)]  # teacher-forced caches
+        nxt = eng.ar_step([0, 1], tokens)
+        torch.cuda.synchronize()
+        for r in range(2):
+            assert eng.cache_len(r) == P + step + 1
+            want, L = om.ar_step(hw, cfg, refs[r], int(tokens[r]))
+            if tie_gap_ok(L, 1, 2 * REL_TOL * np.abs(L).max()):
+                assert int(nxt[r]) == want, (step, r)
+            got = _oracle_request(eng, cfg, r, P + step + 1)
+            assert max_rel(got.k[:, P + step], refs[r].k[:, P + step]) <= REL_TOL
+            assert max_rel(got.v[:, P + step], refs[r].v[:, P + step]) <= REL_TOL
+        tokens = nxt
+
