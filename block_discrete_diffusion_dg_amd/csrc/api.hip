@@ -503,8 +503,9 @@ dg_status dg_ar_step(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req,
                 c->buf<float4>(L.lm_part), &stats[0].held_logit, (int)(sizeof(dg_row_stats) / sizeof(float)),
                 nullptr);
   launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), n_req, 1.0f, stats, nullptr);
-  (void)hipMemcpy2DAsync(d_next, sizeof(int32_t), &stats[0].argmax, sizeof(dg_row_stats), sizeof(int32_t), n_req,
-                         hipMemcpyDeviceToDevice, s);
+  const hipError_t ce = hipMemcpy2DAsync(d_next, sizeof(int32_t), &stats[0].argmax, sizeof(dg_row_stats),
+                                         sizeof(int32_t), n_req, hipMemcpyDeviceToDevice, s);
+  if (ce != hipSuccess) return c->fail(DG_EHIP, std::string("dg_ar_step: ") + hipGetErrorString(ce));
   st = c->check_hip("dg_ar_step");
   if (st) return st;
   for (int r = 0; r < n_req; ++r) c->len[req[r]] += 1;
