@@ -27,5 +27,5 @@ def test_algorithmic_bytes_of_the_expert_launch():
     # + the shared expert's 25.2 MB (three 2048 x 2048 bf16 matrices)
     assert kinds["experts"][0] == 553_648_128 + 25_165_824
     assert per_step["lmhead"][0] == 1_073_741_824  # the tied embedding, read once
-    # FP8: 64 x (4,325,376 code bytes + 11,824 scale bytes) + 12,582,912 + 24,576
-    assert bench.fp8_expert_bytes(synth.FULL, 64.0) == 64 * (4_325_376 + 11_824) + 12_582_912 + 24_576
+    # FP8: 64 x (4,325,376 code bytes + 13,824 scale bytes) + 12,582,912 + 24,576
+    assert bench.fp8_expert_bytes(synth.FULL, 64.0) == 64 * (4_325_376 + 13_824) + 12_582_912 + 24_576
