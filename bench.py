@@ -341,6 +341,7 @@ def ar_variant(args, eng, reqs, P, denoise_ms):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    eng.sync()  # raises if a bounded wait of the expert kernel ran out
     for r in reqs:
         eng.set_cache_len(r, P)
     log(f"ar step: {ms:.3f} ms")

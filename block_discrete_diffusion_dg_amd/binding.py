@@ -100,10 +100,14 @@ SIGNATURES = {
     "dg_reset": (c_i32, [c_vp, c_i32]),
     "dg_set_cache_len": (c_i32, [c_vp, c_i32, c_i32]),
     "dg_last_error": (ctypes.c_char_p, [c_vp]),
+    "dg_sync": (c_i32, [c_vp, c_vp]),
     "dg_workspace_layout": (c_i32, [ctypes.POINTER(DGConfig), ctypes.POINTER(DGWsLayout)]),
     "dg_test_layer": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_i32]),
     "dg_test_route": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "dg_test_head": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs), c_vp]),
+    "dg_test_forward": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs), c_vp, c_vp]),
+    "dg_test_sample": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs), c_vp]),
+    "dg_test_attention": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_i32, c_vp]),
     "dg_timing_enable": (c_i32, [c_vp, c_i32]),
     "dg_timing_read": (c_i32, [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32]),
 }

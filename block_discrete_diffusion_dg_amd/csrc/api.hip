@@ -115,6 +115,9 @@ struct dg_ctx {
   // per slot: 1 once a denoising step of the current block has left its
   // argmax in the workspace (adaptive stopping compares against it)
   std::vector<uint8_t> prev_valid;
+  // expert-kernel waits that ran out, as last read by dg_sync (the counter
+  // starts at zero in the zero-filled workspace)
+  int32_t timeouts_seen = 0;
   bool sticky = false;
   std::string err;
 
@@ -267,13 +270,12 @@ float tau_for(const dg_config& g, int step, int n_steps) {
   return g.tau_first + (g.tau_last - g.tau_first) * (float)(step - 1) / (float)(n_steps - 1);
 }
 
-// LM-head statistics, merge and sampler over the rows in u (already final-normed).
-void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
+// LM-head statistics and their merge over the rows in u (already final-normed).
+void run_lm_stats(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   const dg_config& g = c->cfg;
   const dg_ws_layout& L = c->lay;
   const int rows = a->n_req * g.canvas;
   const float tau = tau_for(g, a->step, a->n_steps);
-  const int k_s = (int)(((int64_t)a->step * g.canvas) / a->n_steps);
   dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
   const bool drawn = a->candidate == DG_CAND_SAMPLE;
   GumbelDraw gd{make_sample_table(a->n_req, a->seed, a->block, a->req), g.canvas, a->step, 1.0f / tau,
@@ -283,6 +285,15 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
                                       (int)(sizeof(dg_row_stats) / sizeof(float)), drawn ? &gd : nullptr));
   STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats,
                                         drawn ? c->buf<float4>(L.lm_gpart) : nullptr));
+}
+
+// The confidence sampler over the per-row statistics in the workspace.
+void run_sampler(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
+  const dg_config& g = c->cfg;
+  const dg_ws_layout& L = c->lay;
+  const float tau = tau_for(g, a->step, a->n_steps);
+  const int k_s = (int)(((int64_t)a->step * g.canvas) / a->n_steps);
+  dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
   // the previous step's argmax of a slot counts only after a step of the
   // same block (host-side, in stream order)
   uint32_t prev_valid = 0;
@@ -294,6 +305,12 @@ void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
                          c->buf<int32_t>(L.prev), prev_valid, a->d_stop};
   STAGE(DG_STAGE_SAMPLER, launch_sampler(s, stats, a->n_req, g.canvas, g.vocab, a->d_canvas, a->d_committed,
                                          a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats, mode));
+}
+
+// LM-head statistics, merge and sampler over the rows in u (already final-normed).
+void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
+  run_lm_stats(c, s, a);
+  run_sampler(c, s, a);
 }
 
 dg_status check_ctx(dg_ctx* c) {
@@ -452,6 +469,25 @@ dg_status dg_set_cache_len(dg_ctx* c, int32_t req, int32_t len) {
 
 const char* dg_last_error(const dg_ctx* c) { return c ? c->err.c_str() : "null context"; }
 
+dg_status dg_sync(dg_ctx* c, void* stream) {
+  dg_status st = check_ctx(c);
+  if (st) return st;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  int32_t timeouts = 0;
+  if (e == hipSuccess)
+    e = hipMemcpy(&timeouts, c->buf<int32_t>(c->lay.items) + MOE_SPIN_TIMEOUTS, sizeof(int32_t),
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return c->fail(DG_EHIP, std::string("dg_sync: ") + hipGetErrorString(e));
+  if (timeouts != c->timeouts_seen) {
+    const int32_t n = timeouts - c->timeouts_seen;
+    c->timeouts_seen = timeouts;
+    return c->fail(DG_EHIP, "dg_sync: " + std::to_string(n) +
+                                " bounded wait(s) of the expert kernel ran out; results since the previous "
+                                "dg_sync are unspecified");
+  }
+  return DG_OK;
+}
+
 dg_status dg_prefill(dg_ctx* c, void* stream, int32_t req, const int32_t* d_ids, int32_t n) {
   dg_status st = check_ctx(c);
   if (st) return st;
@@ -523,7 +559,15 @@ dg_status dg_init_canvas(dg_ctx* c, void* stream, const dg_step_args* a) {
   return c->check_hip("dg_init_canvas");
 }
 
-dg_status dg_denoise_step(dg_ctx* c, void* stream, const dg_step_args* a) {
+}  // extern "C"
+
+namespace {
+
+// The denoising step; with d_h_layers, the residual stream after the
+// embedding and after every layer is copied out ([n_layers + 1][rows][d]);
+// with d_idx_layers, every layer's expert choices ([n_layers][rows][k]).
+dg_status denoise(dg_ctx* c, void* stream, const dg_step_args* a, float* d_h_layers, int32_t* d_idx_layers,
+                  const char* name) {
   dg_status st = check_ctx(c);
   if (st) return st;
   st = check_step_args(c, a, true);
@@ -536,11 +580,33 @@ dg_status dg_denoise_step(dg_ctx* c, void* stream, const dg_step_args* a) {
   const dg_ws_layout& L = c->lay;
   ReqTable rt = make_table(c, a->n_req, a->req, g.canvas);
   const int rows = a->n_req * g.canvas;
+  const size_t h_bytes = (size_t)rows * g.d_model * sizeof(float);
+  auto copy_h = [&](int at) {
+    if (d_h_layers)
+      (void)hipMemcpyAsync((char*)d_h_layers + (size_t)at * h_bytes, c->buf<float>(L.h), h_bytes,
+                           hipMemcpyDeviceToDevice, s);
+  };
   STAGE(DG_STAGE_EMBED, launch_rope_table(s, rt, g.head_dim, g.rope_theta, c->buf<float2>(L.rope));
         run_embed(c, s, a->d_canvas, rows, true));
-  for (int l = 0; l < g.n_layers; ++l) run_layer(c, s, l, rt, 0, false, gain_after(c, l));
+  copy_h(0);
+  const size_t idx_bytes = (size_t)rows * g.top_k * sizeof(int32_t);
+  for (int l = 0; l < g.n_layers; ++l) {
+    run_layer(c, s, l, rt, 0, false, gain_after(c, l));
+    copy_h(l + 1);
+    if (d_idx_layers)
+      (void)hipMemcpyAsync((char*)d_idx_layers + (size_t)l * idx_bytes, c->buf<int32_t>(L.idx), idx_bytes,
+                           hipMemcpyDeviceToDevice, s);
+  }
   run_head(c, s, a);
-  return c->check_hip("dg_denoise_step");
+  return c->check_hip(name);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_denoise_step(dg_ctx* c, void* stream, const dg_step_args* a) {
+  return denoise(c, stream, a, nullptr, nullptr, "dg_denoise_step");
 }
 
 dg_status dg_commit_block(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req,
@@ -634,6 +700,50 @@ dg_status dg_test_head(dg_ctx* c, void* stream, const dg_step_args* a, const flo
                  c->buf<bf16_t>(c->lay.u));
   run_head(c, s, a);
   return c->check_hip("dg_test_head");
+}
+
+dg_status dg_test_forward(dg_ctx* c, void* stream, const dg_step_args* a, float* d_h_layers,
+                          int32_t* d_idx_layers) {
+  if (c && !c->sticky && !d_h_layers) return c->fail(DG_EINVAL, "test_forward: null hidden-state buffer");
+  return denoise(c, stream, a, d_h_layers, d_idx_layers, "dg_test_forward");
+}
+
+dg_status dg_test_sample(dg_ctx* c, void* stream, const dg_step_args* a, const dg_row_stats* d_in) {
+  dg_status st = check_ctx(c);
+  if (st) return st;
+  st = check_step_args(c, a, true);
+  if (st) return st;
+  if (!d_in) return c->fail(DG_EINVAL, "test_sample: null statistics");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t bytes = (size_t)a->n_req * c->cfg.canvas * sizeof(dg_row_stats);
+  (void)hipMemcpyAsync(c->buf<dg_row_stats>(c->lay.stats), d_in, bytes, hipMemcpyDeviceToDevice, s);
+  run_sampler(c, s, a);
+  return c->check_hip("dg_test_sample");
+}
+
+dg_status dg_test_attention(dg_ctx* c, void* stream, int32_t req, int32_t layer, const void* d_q, int32_t n,
+                            int32_t causal, void* d_o) {
+  dg_status st = check_ctx(c);
+  if (st) return st;
+  const dg_config& g = c->cfg;
+  if (req < 0 || req >= g.max_requests || layer < 0 || layer >= g.n_layers || !d_q || !d_o || n <= 0 ||
+      n > g.max_rows)
+    return c->fail(DG_EINVAL, "test_attention: bad arguments");
+  if ((int64_t)c->len[req] + n > g.max_ctx) return c->fail(DG_ECAPACITY, "test_attention: beyond max_ctx");
+  hipStream_t s = (hipStream_t)stream;
+  const dg_ws_layout& L = c->lay;
+  ReqTable rt = make_table(c, 1, &req, n);
+  const size_t qd = (size_t)g.n_q_heads * g.head_dim;
+  const int rsync = router_sync_words(g.max_rows);
+  (void)hipMemsetAsync(c->buf<int32_t>(L.sync) + rsync, 0,
+                       attn_groups_bound(g.max_rows, g.n_q_heads, g.n_kv_heads) * sizeof(int32_t), s);
+  (void)hipMemcpyAsync(c->buf<bf16_t>(L.q), d_q, (size_t)n * qd * 2, hipMemcpyDeviceToDevice, s);
+  const int ns = attn_splits(rt, g.n_q_heads, g.n_kv_heads, g.max_rows);
+  launch_attention(s, c->buf<bf16_t>(L.q), c->kv, layer, rt, g.n_q_heads, g.n_kv_heads, g.head_dim, causal ? 1 : 0,
+                   ns, c->buf<float>(L.attn_part), c->buf<float2>(L.attn_ml), c->buf<int32_t>(L.sync) + rsync,
+                   c->buf<bf16_t>(L.attn_o));
+  (void)hipMemcpyAsync(d_o, c->buf<bf16_t>(L.attn_o), (size_t)n * qd * 2, hipMemcpyDeviceToDevice, s);
+  return c->check_hip("dg_test_attention");
 }
 
 dg_status dg_timing_enable(dg_ctx* c, int32_t enable) {

@@ -195,6 +195,11 @@ class Engine:
         return {"spin_timeouts": int(w[B.ITEMS_SPIN_TIMEOUTS]), "touched_total": int(w64[0]),
                 "permute_calls": int(w64[1])}
 
+    def sync(self):
+        """Wait for the current stream and raise if a bounded wait of the
+        expert kernel ran out since the previous check (dg_sync)."""
+        self._check(self.lib.dg_sync(self.ctx, _stream()))
+
     def cache_len(self, req: int) -> int:
         return self.lib.dg_cache_len(self.ctx, req)
 
@@ -297,11 +302,67 @@ class Engine:
                                              ("idx", "w", "cnt", "off", "perm", "slot")]))
         return out
 
+    def test_forward(self, reqs, canvas, committed, step, n_steps, seeds, blocks, stats=None,
+                     confidence: str = "prob", candidate: str = "argmax"):
+        """dg_denoise_step, returning the residual stream after the embedding
+        and after every layer (fp32 [n_layers + 1][rows][d]) and every
+        layer's expert choices (int32 [n_layers][rows][top_k])."""
+        c = self.cfg
+        rows = len(reqs) * c.canvas
+        dev = self.kv.device
+        hs = torch.empty((c.n_layers + 1, rows, c.d_model), dtype=torch.float32, device=dev)
+        idx = torch.empty((max(1, c.n_layers), rows, c.top_k), dtype=torch.int32, device=dev)
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence, 0.0, None,
+                       candidate)
+        self._check(self.lib.dg_test_forward(self.ctx, _stream(), ctypes.byref(a), hs.data_ptr(),
+                                             idx.data_ptr()))
+        return hs, idx[:c.n_layers]
+
+    def test_sample(self, reqs, stats_in: torch.Tensor, canvas, committed, step, n_steps, seeds, blocks,
+                    stats=None, confidence: str = "prob", stop_entropy: float = 0.0, stop=None,
+                    candidate: str = "argmax"):
+        """The sampler alone, fed per-row statistics stats_in (int32 [rows][10]
+        in the dg_row_stats layout)."""
+        assert stats_in.is_cuda and stats_in.is_contiguous() and stats_in.dtype == torch.int32
+        a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
+                       stop_entropy, stop, candidate)
+        self._check(self.lib.dg_test_sample(self.ctx, _stream(), ctypes.byref(a), stats_in.data_ptr()))
+
+    def test_attention(self, req: int, layer: int, q: torch.Tensor, causal: bool) -> torch.Tensor:
+        """Attention of q (bf16 [n][Hq][dh], rotated) over cache rows
+        [0, len + n) of (req, layer); returns bf16 [n][Hq*dh]."""
+        assert q.dtype == torch.bfloat16 and q.is_cuda and q.is_contiguous()
+        n = q.shape[0]
+        o = torch.empty((n, self.cfg.n_q_heads * self.cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+        self._check(self.lib.dg_test_attention(self.ctx, _stream(), req, layer, q.data_ptr(), n, int(causal),
+                                               o.data_ptr()))
+        return o
+
     def test_head(self, reqs, h, canvas, committed, step, n_steps, seeds, blocks, stats=None,
                   confidence: str = "prob", stop_entropy: float = 0.0, stop=None, candidate: str = "argmax"):
         a = self._args(reqs, canvas, committed, step, n_steps, seeds, blocks, stats, confidence,
                        stop_entropy, stop, candidate)
         self._check(self.lib.dg_test_head(self.ctx, _stream(), ctypes.byref(a), h.data_ptr()))
+
+
+def stats_tensor(max_logit, log_z, held_logit, argmax, entropy=None, sample=None, sample_logit=None):
+    """Pack per-row statistics (host arrays) into an int32 [rows][10] CPU
+    tensor in the dg_row_stats layout (floats stored as float32 bits)."""
+    import numpy as np
+    rows = len(max_logit)
+    out = np.zeros((rows, B.ROW_STATS_BYTES // 4), np.int32)
+    f = out.view(np.float32)
+    f[:, 0] = np.asarray(max_logit, np.float32)
+    f[:, 1] = np.asarray(log_z, np.float32)
+    f[:, 2] = np.asarray(held_logit, np.float32)
+    out[:, 4] = np.asarray(argmax, np.int32)
+    if entropy is not None:
+        f[:, 6] = np.asarray(entropy, np.float32)
+    if sample is not None:
+        out[:, 7] = np.asarray(sample, np.int32)
+    if sample_logit is not None:
+        f[:, 8] = np.asarray(sample_logit, np.float32)
+    return torch.from_numpy(out)
 
 
 def stats_fields(stats: torch.Tensor) -> Dict[str, torch.Tensor]:

@@ -226,7 +226,9 @@ size_t dg_workspace_bytes(const dg_config *cfg);
 
 /* Validate cfg, copy the weight pointer table and bind the caller's KV cache
  * (max_requests * dg_kv_cache_bytes) and workspace (dg_workspace_bytes).
- * Every request slot starts empty (cache length 0). */
+ * The workspace must be zero-filled when the context is created (the
+ * kernels' arrival counters and the wait-timeout counter read by dg_sync
+ * start from it). Every request slot starts empty (cache length 0). */
 dg_status dg_create(const dg_config *cfg, const dg_weights *w, void *d_kv_cache,
                     void *d_workspace, size_t workspace_bytes, dg_ctx **out);
 void dg_destroy(dg_ctx *ctx);
@@ -292,6 +294,16 @@ dg_status dg_reset(dg_ctx *ctx, int32_t req);
 /* Set a slot's committed length without running the encoder, for callers that
  * fill the cache rows themselves (e.g. a restored snapshot of the cache). */
 dg_status dg_set_cache_len(dg_ctx *ctx, int32_t req, int32_t len);
+
+/* Wait for the work enqueued on stream, then check the kernels' own error
+ * report. The grouped-expert kernel is one persistent grid whose down-
+ * projection items wait, with a bounded poll, for the gate/up items of
+ * their row chunk (all of which are dequeued earlier, so in a correct run
+ * every wait ends). If any such wait ran out since the previous dg_sync (or
+ * since dg_create), the outputs of the steps in between are unspecified:
+ * the context becomes sticky and DG_EHIP is returned with a message. A HIP
+ * error while waiting is also DG_EHIP. Blocks the calling thread. */
+dg_status dg_sync(dg_ctx *ctx, void *stream);
 
 /* Last error message of the context ("" if none). */
 const char *dg_last_error(const dg_ctx *ctx);

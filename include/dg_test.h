@@ -84,6 +84,39 @@ dg_status dg_test_route(dg_ctx *ctx, void *stream, const float *d_z, int32_t row
  * canvas / committed / stats as dg_denoise_step. */
 dg_status dg_test_head(dg_ctx *ctx, void *stream, const dg_step_args *a, const float *d_h);
 
+/* The denoising step of dg_denoise_step, same arguments and effects, with
+ * the residual stream copied out after the embedding and after every layer:
+ * d_h_layers is device fp32 [n_layers + 1][n_req * canvas][d_model] (entry 0
+ * the embedding rows, entry l + 1 the rows after layer l), and, when
+ * d_idx_layers is not NULL, each layer's expert choices, device int32
+ * [n_layers][n_req * canvas][top_k] (descending router logit). The copies
+ * are extra work on the stream; the kernels and their order are those of
+ * dg_denoise_step (explainer §3.2: the bidirectional decoder pass over the
+ * canvas). DG_EINVAL if d_h_layers is NULL. */
+dg_status dg_test_forward(dg_ctx *ctx, void *stream, const dg_step_args *a, float *d_h_layers,
+                          int32_t *d_idx_layers);
+
+/* The confidence sampler of dg_denoise_step (explainer §3.3) fed given
+ * per-position statistics instead of the LM head's: d_in is device
+ * dg_row_stats [n_req * canvas], of which max_logit, log_z, held_logit,
+ * argmax, entropy, sample and sample_logit are read (as the LM head would
+ * have written them). Canvas, committed mask, d_stats (conf, accepted) and
+ * d_stop are updated exactly as by dg_denoise_step with the same arguments,
+ * including the per-slot previous-argmax state of adaptive stopping. */
+dg_status dg_test_sample(dg_ctx *ctx, void *stream, const dg_step_args *a, const dg_row_stats *d_in);
+
+/* Canvas attention alone (explainer §3.2; aiboss88.com, "hybrid attention"):
+ * the n query rows d_q (device bf16 [n][n_q_heads][head_dim], already
+ * rotated) of request slot req at positions len..len+n-1 (len =
+ * dg_cache_len) attend, per query head h with kv head h*Hkv/Hq, to the
+ * cache rows [0, len + n) of layer `layer` (K rotated; V in the cache's
+ * block order; rows [len, len+n) are the block's own rows, written by the
+ * caller). causal = 0: no mask; causal = 1: query i sees keys < len + i + 1.
+ * Scale 1/sqrt(head_dim). d_o: device bf16 [n][n_q_heads * head_dim].
+ * Needs n <= max_rows and len + n <= max_ctx. */
+dg_status dg_test_attention(dg_ctx *ctx, void *stream, int32_t req, int32_t layer, const void *d_q, int32_t n,
+                            int32_t causal, void *d_o);
+
 /* Per-stage timing. While enabled, every launch of a stage is bracketed by a
  * pair of hipEvents recorded on the call's stream; dg_timing_read waits for
  * the last recorded event, adds the elapsed times into ms[stage] and

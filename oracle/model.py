@@ -202,16 +202,12 @@ def moe(u: np.ndarray, idx: np.ndarray, w: np.ndarray, lw: Dict, n_experts: int,
 # ----------------------------------------------------------------------------
 
 def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np.ndarray,
-                  n_prefix: int, causal: bool, keep: Optional[Dict] = None,
-                  idx_override: Optional[np.ndarray] = None):
+                  n_prefix: int, causal: bool, keep: Optional[Dict] = None):
     """One pre-norm attention + MoE layer on n rows at positions n_prefix..n_prefix+n-1.
 
     cache_k, cache_v: [>= n_prefix, Hkv, dh] prefix rows (K already rotated).
     Returns (new h, k rows [n, Hkv, dh] rotated, v rows). `keep`, when given,
-    receives the intermediates by name. `idx_override` (test harness only)
-    imposes the expert choice of another implementation, taken where its
-    router logits are tied within floating-point noise; the routing weights
-    are still the softmax of this oracle's own logits at those experts.
+    receives the intermediates by name.
     """
     n, d = h.shape
     Hq, Hkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -230,11 +226,6 @@ def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np
     u2 = rms_norm(h1, lw["moe_norm"], cfg.rms_eps)
     z = u2 @ f64(lw["w_router"]).T
     idx, w = route(z, cfg.top_k)
-    if idx_override is not None:
-        idx = np.asarray(idx_override, np.int64)
-        sel = np.take_along_axis(z, idx, axis=1)
-        ex = np.exp(sel - sel.max(axis=1, keepdims=True))
-        w = ex / ex.sum(axis=1, keepdims=True)
     pinfo = permutation(idx, cfg.n_experts)
     h2 = h1 + moe(u2, idx, w, lw, cfg.n_experts, pinfo)
     if keep is not None:
@@ -248,8 +239,17 @@ def layer_forward(h: np.ndarray, lw: Dict, cfg, cache_k: np.ndarray, cache_v: np
 # LM head statistics and the confidence sampler
 # ----------------------------------------------------------------------------
 
-def tau_at(step: int, n_steps: int, tau_first: float, tau_last: float) -> float:
-    """Temperature falling linearly from tau_first (step 1) to tau_last (step S)."""
+def tau_at(step: int, n_steps: int, tau_first: float, tau_last: float, precision: str = "float64"):
+    """Temperature falling linearly from tau_first (step 1) to tau_last (step S).
+
+    precision "float32" evaluates tau_first + ((tau_last - tau_first) * (s-1)) / (S-1)
+    in IEEE float32, operation by operation (the precision of a float32
+    implementation of the same schedule)."""
+    if precision == "float32":
+        f = np.float32
+        if n_steps <= 1:
+            return f(tau_first)
+        return f(f(tau_first) + f(f(f(tau_last) - f(tau_first)) * f(step - 1)) / f(n_steps - 1))
     if n_steps <= 1:
         return float(tau_first)
     return float(tau_first) + (float(tau_last) - float(tau_first)) * (step - 1) / (n_steps - 1)
@@ -329,7 +329,7 @@ def adaptive_stop(H: np.ndarray, a: np.ndarray, a_prev: Optional[np.ndarray],
 def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
            n_steps: int, seed: int, block: int, request: int, vocab: int,
            confidence: str = "prob", H: Optional[np.ndarray] = None, stop: bool = False,
-           drawn: Optional[tuple] = None):
+           drawn: Optional[tuple] = None, precision: str = "float64"):
     """Confidence-ordered acceptance with uniform re-noise.
 
     Candidate y_i: the held token if position i is committed, else the argmax
@@ -344,17 +344,21 @@ def sample(x: np.ndarray, m: np.ndarray, M, a, logZ, gx, tau: float, step: int,
     uniform id from Philox at counter (i, step, block, request). When the
     block stops early (`stop`), the step acts as the last one: every position
     is accepted.
+    precision "float32" takes the statistics, tau and every operation of the
+    confidence in IEEE float32, so that the ranking is decided in the
+    precision of a float32 implementation fed the same statistics.
     Returns (new x, new committed mask, c, accepted-set boolean mask).
     """
     C = x.shape[0]
     committed = np.asarray(m).astype(bool)
     cand, Lc = (a, M) if drawn is None else drawn
     y = np.where(committed, x, cand)
+    ft = np.float32 if precision == "float32" else np.float64
     if confidence == "prob":
-        Ly = np.where(committed, gx, Lc)
-        c = (Ly - M) / tau - logZ
+        Ly = np.where(committed, np.asarray(gx, ft), np.asarray(Lc, ft))
+        c = (Ly - np.asarray(M, ft)) / ft(tau) - np.asarray(logZ, ft)
     elif confidence == "entropy":
-        c = -np.asarray(H, np.float64)
+        c = -np.asarray(H, ft)
     else:
         raise ValueError(confidence)
     k_s = C if stop else commit_count(step, n_steps, C)

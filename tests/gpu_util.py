@@ -3,6 +3,7 @@ for the oracle, and compare with explicit tolerances."""
 import sys
 
 import numpy as np
+import scipy.special
 import torch
 
 from block_discrete_diffusion_dg_amd import synth
@@ -92,3 +93,35 @@ def tie_gap_ok(keys, k, band):
     if k <= 0 or k >= len(s):
         return True
     return (s[k - 1] - s[k]) > band
+
+
+def moe_with_experts(keep, lw, cfg, idx):
+    """The oracle's layer output with another implementation's expert choice
+    imposed: keep holds the oracle's own intermediates of the layer (h_mid,
+    u_moe, z); the routing weights are the softmax of the oracle's own logits
+    at the imposed experts. Used only where the two choices differ inside
+    the router's tie band (the integer decision is then the kernel's)."""
+    idx = np.asarray(idx, np.int64)
+    sel = np.take_along_axis(keep["z"], idx, axis=1)
+    w = scipy.special.softmax(sel, axis=1)
+    return keep["h_mid"] + om.moe(keep["u_moe"], idx, w, lw, cfg.n_experts)
+
+
+def router_band(u, w_router):
+    """Per row: the largest change of a gap between two router logits that
+    rounding the router's input row u to bf16 can cause. Each element moves by
+    at most half an ulp (relative 2^-9), so a logit z_e = sum_k u_k W_ek moves
+    by at most 2^-9 sum_k |u_k W_ek|, and a gap by twice the largest such sum.
+    A bound fixed by the arithmetic (bf16 operands), not by measured errors."""
+    return 2.0 ** -8 * (np.abs(np.asarray(u, np.float64)) @ np.abs(om.f64(w_router)).T).max(axis=1)
+
+
+def router_swaps(idx_gpu, z_or, top_k, band):
+    """Rows whose expert sets differ; asserts each lies inside its tie band
+    (the oracle's k-th and (k+1)-th logits closer than band[t])."""
+    swaps = []
+    for t in range(idx_gpu.shape[0]):
+        if set(np.asarray(idx_gpu[t]).tolist()) != set(np.argsort(-z_or[t], kind="stable")[:top_k].tolist()):
+            assert not tie_gap_ok(z_or[t], top_k, band[t]), (t, band[t])
+            swaps.append(t)
+    return swaps

@@ -191,6 +191,36 @@ def _bad_rms_norm(x, gain, eps):
     return x / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps)  # gain dropped
 
 
+def _pin_swiglu():
+    x = np.array([[1.0, 0.0]])
+    got = float(om.swiglu(x, np.array([[20.0, 0.0]]), np.array([[-20.0, 0.0]]), np.array([[1.0]]))[0, 0])
+    d, F_ = 12, 20
+    xr = RNG.normal(size=(4, d))
+    wg, wu, wd = (RNG.normal(size=s) * 0.3 for s in ((F_, d), (F_, d), (d, F_)))
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    want = ((F.silu(t(xr) @ t(wg).T) * (t(xr) @ t(wu).T)) @ t(wd).T).numpy()
+    return abs(got + 400.0 / (1.0 + np.exp(-20.0))) < 1e-9 and np.allclose(om.swiglu(xr, wg, wu, wd), want)
+
+
+def _bad_swiglu_silu_on_up(x, w_gate, w_up, w_down):
+    return (om.silu(x @ om.f64(w_up).T) * (x @ om.f64(w_gate).T)) @ om.f64(w_down).T  # silu on the up branch
+
+
+def _pin_rope_freq():
+    ok = abs(om.rope_angles(np.array([7]), 64, 1e4)[0, 16] - 0.07) < 1e-12
+    ok &= abs(om.rope_angles(np.array([3]), 4, 1e4)[0, 1] - 0.03) < 1e-12
+    x = np.zeros((1, 1, 16))
+    x[0, 0, 4] = 1.0
+    out = om.rope(x, np.array([250]), 1e4)[0, 0]
+    return bool(ok and abs(out[4] - np.cos(2.5)) < 1e-12 and abs(out[12] - np.sin(2.5)) < 1e-12)
+
+
+def _bad_rope_angles_freq(positions, head_dim, theta):
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = np.power(float(theta), -j / head_dim)  # theta^(-j/dh): the factor 2 dropped
+    return np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
+
+
 _real_fp8 = {"e4m3_encode": om_fp8.e4m3_encode}
 
 _real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
@@ -198,6 +228,8 @@ _real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
 
 CASES = [
     ("rope", _bad_rope, _pin_rope),
+    ("rope_angles", _bad_rope_angles_freq, _pin_rope_freq),
+    ("swiglu", _bad_swiglu_silu_on_up, _pin_swiglu),
     ("attention", _bad_attention_scale, _pin_attention),
     ("attention", _bad_attention_gqa, _pin_attention),
     ("route", _bad_route_ties, _pin_route),

@@ -111,6 +111,29 @@ def test_rope_scores_depend_on_relative_position_only():
         assert abs(s - base) < 1e-9 * max(1.0, abs(base))
 
 
+def test_rope_angles_hand_values():
+    # angle(pos, j) = pos * theta^(-2j/dh), worked by hand at theta = 10000:
+    # 10000^(-1/2) = 0.01, 10000^(-1/4) = 0.1, 10000^0 = 1.
+    cases = [(3, 1, 4, 0.03), (5, 2, 8, 0.05), (7, 16, 64, 0.07), (9, 1, 8, 0.9),
+             (11, 0, 128, 11.0), (2, 48, 128, 2e-3)]
+    for pos, j, dh, want in cases:
+        got = om.rope_angles(np.array([pos]), dh, 1e4)[0, j]
+        assert abs(got - want) <= 1e-12 * max(1.0, want), (pos, j, dh, got, want)
+
+
+def test_rope_pair_rotates_by_its_own_frequency():
+    # a unit vector in pair j (components j and j + dh/2) turns by pos * 0.01
+    # for j = dh/4 (theta^(-1/2)); every other pair stays zero.
+    dh, j, pos = 16, 4, 250
+    x = np.zeros((1, 1, dh))
+    x[0, 0, j] = 1.0
+    out = om.rope(x, np.array([pos]), 1e4)[0, 0]
+    ang = pos * 0.01
+    assert abs(out[j] - np.cos(ang)) < 1e-12 and abs(out[j + dh // 2] - np.sin(ang)) < 1e-12
+    rest = np.delete(out, [j, j + dh // 2])
+    assert np.all(rest == 0.0)
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _sdpa_reference(q, k, v, n_prefix, causal):
@@ -250,6 +273,32 @@ def test_moe_grouped_equals_per_token_sum_and_idle_expert_is_inert():
     assert np.array_equal(om.moe(u, idx, w, lw2, E), got)
 
 
+def test_swiglu_matches_torch_composition():
+    # torch's silu (a library routine: x * sigmoid(x)) gating the gate
+    # projection, times the up projection, then the down projection.
+    d, F_ = 24, 40
+    x = RNG.normal(size=(7, d))
+    wg, wu, wd = (RNG.normal(size=s) * 0.3 for s in ((F_, d), (F_, d), (d, F_)))
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    want = (F.silu(t(x) @ t(wg).T) * (t(x) @ t(wu).T)) @ t(wd).T
+    assert np.allclose(om.swiglu(x, wg, wu, wd), want.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_swiglu_gate_and_up_are_not_interchangeable():
+    # one hidden unit with gate pre-activation a = 20 and up pre-activation
+    # b = -20, identity down projection: silu(a) * b = -20 * 20 / (1 + e^-20)
+    # (about -400), whereas silu(b) * a would be about -4e-8.
+    x = np.array([[1.0, 0.0]])
+    wg = np.array([[20.0, 0.0]])
+    wu = np.array([[-20.0, 0.0]])
+    wd = np.array([[1.0]])
+    got = float(om.swiglu(x, wg, wu, wd)[0, 0])
+    assert abs(got - (-400.0 / (1.0 + np.exp(-20.0)))) < 1e-9
+    # silu's closed forms: silu(0) = 0 and silu(2) = 2 sigmoid(2)
+    assert om.silu(np.array([0.0]))[0] == 0.0
+    assert abs(om.silu(np.array([2.0]))[0] - 2.0 / (1.0 + np.exp(-2.0))) < 1e-15
+
+
 # ----------------------------------------------------------------------------- LM head + sampler
 
 def test_row_stats_match_numpy_and_scipy():
@@ -306,6 +355,36 @@ def test_sampler_invariants_over_a_block():
         assert np.array_equal(x2[~acc], noise[~acc])
         x, m = x2, m2
     assert m.all()
+
+
+def test_sampler_float32_precision_agrees_with_float64_off_ties():
+    # the float32 schedule is the float64 one to float32 rounding, exactly
+    # 0.8 and 0.4 (as float32) at the ends
+    for s_, S_ in [(1, 16), (7, 16), (16, 16), (1, 1), (3, 12)]:
+        t32 = om.tau_at(s_, S_, 0.8, 0.4, precision="float32")
+        assert isinstance(t32, np.float32)
+        assert abs(float(t32) - om.tau_at(s_, S_, 0.8, 0.4)) <= 2e-7
+    assert om.tau_at(1, 16, 0.8, 0.4, precision="float32") == np.float32(0.8)
+    assert om.tau_at(16, 16, 0.8, 0.4, precision="float32") == np.float32(0.4)
+    # float32 confidences equal the float64 ones to float32 rounding, and the
+    # accepted set is the same wherever the boundary gap exceeds that rounding
+    V, C = 211, 48
+    for trial in range(20):
+        L = RNG.normal(size=(C, V)) * 3
+        x = RNG.integers(0, V, size=C)
+        m = (RNG.random(C) < 0.4).astype(np.uint8)
+        tau = om.tau_at(4, 9, 0.8, 0.4)
+        M, a, logZ, gx = om.row_stats(L, x, tau)
+        f = lambda v: np.asarray(v, np.float32)
+        _, _, c64, acc64 = om.sample(x, m, M, a, logZ, gx, tau, 4, 9, 1, 0, 0, V)
+        x32, m32, c32, acc32 = om.sample(x, m, f(M), a, f(logZ), f(gx), om.tau_at(4, 9, 0.8, 0.4, "float32"),
+                                         4, 9, 1, 0, 0, V, precision="float32")
+        assert c32.dtype == np.float32
+        assert np.all(np.abs(c32 - c64) <= 1e-5 * (1 + np.abs(c64)))
+        k = om.commit_count(4, 9, C)
+        cs = np.sort(c64)[::-1]
+        if cs[k - 1] - cs[k] > 1e-4 * (1 + abs(cs[k])):
+            assert np.array_equal(acc32, acc64)
 
 
 def test_entropy_closed_forms_and_library():
