@@ -137,6 +137,10 @@ def main():
                     help="override the workload's number of requests (batch-size sweep; 0 = the workload's)")
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the extra measurement with FP8 expert weights")
+    ap.add_argument("--no-selfcond-variant", action="store_true",
+                    help="skip the extra measurement with self-conditioning")
+    ap.add_argument("--graph-steps", type=int, default=50,
+                    help="also time this many graph-launched steps (median reported; 0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=512,
                     help="after the run, copy this many MiB device-to-device with a plain copy "
                          "kernel (reference for hardware byte counters)")
@@ -218,6 +222,21 @@ def main():
     launches = {k: v[1] // args.steps for k, v in stages.items() if v[1]}
     log("stage ms/step: " + ", ".join(f"{k}={v:.3f}" for k, v in stage_ms.items()))
 
+    # graph-launched steps: median of --graph-steps replays
+    graph = None
+    if args.graph_steps:
+        moe_g0 = eng.moe_counters()
+        times = graph_timing(eng, reqs, x, m, S, seeds, blocks, args.warmup, args.graph_steps)
+        eng.sync()
+        if times is not None:
+            t = np.sort(np.array(times))
+            graph = {"median_ms": round(float(np.median(t)), 4), "p10_ms": round(float(t[len(t) // 10]), 4),
+                     "p90_ms": round(float(t[(9 * len(t)) // 10]), 4), "steps": len(t),
+                     "steps_per_s_median": round(1e3 / float(np.median(t)), 3)}
+            log(f"graph-launched: median {graph['median_ms']:.3f} ms/step over {len(t)} replays")
+        if eng.moe_counters()["spin_timeouts"] != moe_g0["spin_timeouts"]:
+            raise RuntimeError("expert kernel waits ran out during the graph-launched steps")
+
     # commit (the +K-1 forward of each block), timed once, then the length restored
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record(stream)
@@ -290,6 +309,7 @@ def main():
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,
         "commit_ms": round(commit_ms, 3),
+        "graph_launched": graph,
     }
     if not args.no_cpu_baseline and args.workload in ("full", "one_layer", "tiny"):
         hw = _HostWeights(layers, embed, final)
@@ -321,7 +341,44 @@ def main():
         if not args.no_fp8_variant:
             out["variants"]["fp8_experts"] = fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds,
                                                          blocks, canvas0, dev)
+        if not args.no_selfcond_variant:
+            out["variants"]["self_conditioning"] = selfcond_variant(args, cfg, wl, layers, embed, final, reqs,
+                                                                    seeds, blocks, canvas0, dev)
     print(json.dumps(out), flush=True)
+
+
+def graph_timing(eng, reqs, x, m, S, seeds, blocks, n_warm, n_timed):
+    """Graph-launched steps: one HIP graph per step index s = 1..S (the
+    step's temperature and commit count are launch arguments, fixed at
+    capture), replayed in block order on the canvas, each replay timed with
+    its own pair of events on the replay stream. Returns the per-step
+    durations in ms (after n_warm untimed replays), or None when capture is
+    not available."""
+    import torch
+    x0, m0 = x.clone(), m.clone()
+    graphs = []
+    try:
+        for s in range(1, S + 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eng.denoise_step(reqs, x, m, s, S, seeds, blocks)
+            graphs.append(g)
+    except Exception as e:  # capture unsupported: report eager timing only
+        log(f"graph capture failed: {e}")
+        return None
+    x.copy_(x0)
+    m.copy_(m0)
+    stream = torch.cuda.current_stream()
+    for i in range(n_warm):
+        graphs[i % S].replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_timed)]
+    torch.cuda.synchronize()
+    for i in range(n_timed):
+        ev[i][0].record(stream)
+        graphs[(n_warm + i) % S].replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 
 def ar_variant(args, eng, reqs, P, denoise_ms):
@@ -375,6 +432,51 @@ def sampled_variant(args, eng, reqs, seeds, blocks, x, m, S):
     return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
             "lmhead_ms": round(stages["lmhead"][0] / max(1, stages["lmhead"][1]), 4),
             "merge_ms": round(stages["merge"][0] / max(1, stages["merge"][1]), 4)}
+
+
+def selfcond_variant(args, cfg, wl, layers, embed, final, reqs, seeds, blocks, canvas0, dev):
+    """The same step with self-conditioning (explainer §3.2): each step's
+    predicted distribution softmax(L) over the whole vocabulary, contracted
+    with the tied embedding and passed through a SwiGLU feed-forward layer of
+    width d_expert, is added to the next step's input embeddings. The pages
+    time it inside their "sampling" stage (explainer §5.2)."""
+    import torch
+    from block_discrete_diffusion_dg_amd import synth
+    from block_discrete_diffusion_dg_amd.engine import Engine
+    P, S, C = wl.prefix, wl.n_steps, cfg.canvas
+    rows = len(reqs) * C
+    sc = synth.make_selfcond_weights(cfg, cfg.d_expert, wl.seed, dev)
+    eng = Engine(cfg, layers, embed, final, max_ctx=P + 2 * C, max_requests=len(reqs), max_rows=rows,
+                 selfcond=sc)
+    for r in reqs:
+        eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
+    x = torch.from_numpy(canvas0).to(dev)
+    m = torch.zeros(rows, dtype=torch.uint8, device=dev)
+
+    def run(n, start):
+        for i in range(n):
+            eng.denoise_step(reqs, x, m, (start + i) % S + 1, S, seeds, blocks)
+
+    run(args.warmup, 0)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(args.steps, args.warmup)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    eng.timing(True)
+    run(args.steps, args.warmup + args.steps)
+    stages = eng.timing_read()
+    eng.timing(False)
+    eng.sync()
+    log(f"self-conditioning: {ms:.3f} ms/step, signal {stages['selfcond'][0] / args.steps:.3f} ms/step")
+    eng.close()
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
+            "canvas_tok_s": round(1e3 / ms * rows, 1), "width": cfg.d_expert,
+            "selfcond_ms_per_step": round(stages["selfcond"][0] / args.steps, 4),
+            "lmhead_ms_per_step": round(stages["lmhead"][0] / args.steps, 4)}
 
 
 def fp8_variant(args, cfg, wl, layers, embed, final, reqs, seeds, blocks, canvas0, dev):

@@ -25,7 +25,7 @@ class DGConfig(ctypes.Structure):
                                      "n_experts", "top_k", "d_expert", "d_shared", "vocab",
                                      "canvas", "max_ctx", "max_requests", "max_rows")] + \
                [(n, c_f32) for n in ("rms_eps", "rope_theta", "tau_first", "tau_last")] + \
-               [("expert_format", c_i32)]
+               [("expert_format", c_i32), ("d_selfcond", c_i32)]
 
 
 WEIGHT_FORMAT = {"bf16": 0, "fp8": 1}
@@ -49,7 +49,8 @@ class DGLayerWeights(ctypes.Structure):
 
 
 class DGWeights(ctypes.Structure):
-    _fields_ = [("embed", c_vp), ("final_norm", c_vp), ("layers", ctypes.POINTER(DGLayerWeights))]
+    _fields_ = [("embed", c_vp), ("final_norm", c_vp), ("layers", ctypes.POINTER(DGLayerWeights)),
+                ("sc_gate", c_vp), ("sc_up", c_vp), ("sc_down", c_vp), ("embed_t", c_vp)]
 
 
 class DGRowStats(ctypes.Structure):
@@ -75,7 +76,7 @@ CANDIDATE = {"argmax": 0, "sample": 1}
 
 WS_FIELDS = ("h", "u", "q", "attn_o", "attn_part", "attn_ml", "rope", "z", "idx", "w", "wslot",
              "cnt", "off", "items", "perm", "slot", "hid", "hid_s", "y", "lm_part", "lm_gpart", "stats", "ids", "ss", "zpart", "sync",
-             "prev", "total")
+             "prev", "sc_p", "sc_qpart", "sc_part", "sc_e", "sc_g", "sc_u", "sc_hid", "sc_out", "sc_state", "total")
 
 
 class DGWsLayout(ctypes.Structure):
@@ -119,7 +120,7 @@ ITEMS_TOUCHED_TOTAL = 410
 ITEMS_PERMUTE_CALLS = 412
 
 STAGES = ("embed", "norm", "qkv", "attn", "oproj", "router", "topk", "permute", "experts",
-          "combine", "lmhead", "merge", "sampler")
+          "combine", "lmhead", "merge", "sampler", "selfcond")
 
 _lib = None
 

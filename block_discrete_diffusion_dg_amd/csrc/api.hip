@@ -61,7 +61,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.slot = take(R * k * 4);
   L.hid = take(R * k * c.d_expert * 2);
   L.hid_s = take(R * c.d_shared * 2);
-  L.y = take(R * k * d * 4 + R * d * 4);  // routed outputs, then the shared expert's
+  L.y = take(R * k * d * 2 + R * d * 4);  // routed outputs (bf16), then the shared expert's (fp32)
   L.lm_part = take(R * (size_t)lmhead_parts(c.vocab) * 16);
   L.lm_gpart = take(R * (size_t)lmhead_parts(c.vocab) * 16);
   L.stats = take(R * sizeof(dg_row_stats));
@@ -70,6 +70,16 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
   L.sync = take((router_sync_words(c.max_rows) + groups) * 4);  // router row blocks, then attention groups
   L.prev = take((size_t)c.max_requests * c.canvas * 4);
+  const size_t Fsc = c.d_selfcond > 0 ? (size_t)c.d_selfcond : 0, on = Fsc > 0 ? 1 : 0;
+  L.sc_p = take(on * R * c.vocab * 2);
+  L.sc_qpart = take(on * R * (c.vocab / 64) * 8);
+  L.sc_part = take(on * (size_t)sc_gemm_splits(c.vocab) * R * d * 4);
+  L.sc_e = take(on * R * d * 2);
+  L.sc_g = take(R * Fsc * 4);
+  L.sc_u = take(R * Fsc * 4);
+  L.sc_hid = take(R * Fsc * 2);
+  L.sc_out = take(on * R * d * 4);
+  L.sc_state = take(on * (size_t)c.max_requests * c.canvas * d * 4);
   L.total = o;
   return L;
 }
@@ -98,6 +108,7 @@ const char* check_config(const dg_config& c) {
     return "rms_eps >= 0, rope_theta > 0 and temperatures > 0 required";
   if (c.expert_format != DG_WEIGHTS_BF16 && c.expert_format != DG_WEIGHTS_FP8)
     return "expert_format must be DG_WEIGHTS_BF16 or DG_WEIGHTS_FP8";
+  if (c.d_selfcond < 0 || c.d_selfcond % 64) return "d_selfcond must be 0 or a positive multiple of 64";
   return nullptr;
 }
 
@@ -108,6 +119,7 @@ struct dg_ctx {
   std::vector<LayerW> layers;
   const bf16_t* embed;
   const bf16_t* final_norm;
+  const bf16_t *sc_gate = nullptr, *sc_up = nullptr, *sc_down = nullptr, *embed_t = nullptr;
   KvGeom kv;
   char* ws;
   dg_ws_layout lay;
@@ -115,6 +127,9 @@ struct dg_ctx {
   // per slot: 1 once a denoising step of the current block has left its
   // argmax in the workspace (adaptive stopping compares against it)
   std::vector<uint8_t> prev_valid;
+  // per slot: 1 once a denoising step of the current block has left its
+  // self-conditioning signal in the workspace
+  std::vector<uint8_t> sc_valid;
   // expert-kernel waits that ran out, as last read by dg_sync (the counter
   // starts at zero in the zero-filled workspace)
   int32_t timeouts_seen = 0;
@@ -230,8 +245,8 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,
                                        g.n_experts, g.top_k, u, c->buf<float>(L.z), c->buf<float>(L.zpart),
                                        c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w), &rp));
-  float* y = c->buf<float>(L.y);
-  float* ys = y + (size_t)g.max_rows * g.top_k * d;
+  bf16_t* y = c->buf<bf16_t>(L.y);
+  float* ys = reinterpret_cast<float*>(y + (size_t)g.max_rows * g.top_k * d);
   STAGE(DG_STAGE_EXPERTS,
         launch_moe_experts(s, u, rows, d, g.d_expert, g.d_shared, g.n_experts, g.top_k, c->buf<int32_t>(L.perm),
                            c->buf<int32_t>(L.cnt), c->buf<int32_t>(L.off), c->buf<float>(L.w),
@@ -248,13 +263,15 @@ const bf16_t* gain_after(const dg_ctx* c, int l) {
 }
 
 // Embedding rows plus the pre-norm of the first layer (or the final norm when
-// the model has no layers).
-void run_embed(dg_ctx* c, hipStream_t s, const int32_t* ids, int rows, bool to_head) {
+// the model has no layers); with sc, the slots' self-conditioning signals
+// are added first.
+void run_embed(dg_ctx* c, hipStream_t s, const int32_t* ids, int rows, bool to_head,
+               const SelfCondIn* sc = nullptr) {
   const dg_config& g = c->cfg;
   const bf16_t* gain = g.n_layers > 0 ? c->layers[0].attn_norm : (to_head ? c->final_norm : nullptr);
   if (!gain) gain = c->final_norm;
   launch_embed(s, ids, rows, c->embed, g.d_model, g.vocab, c->buf<float>(c->lay.h), gain, g.rms_eps,
-               c->buf<bf16_t>(c->lay.u));
+               c->buf<bf16_t>(c->lay.u), sc);
 }
 
 // Causal encoder pass over rows whose embeddings/pre-norm are in h/u: K/V of
@@ -280,9 +297,11 @@ void run_lm_stats(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   const bool drawn = a->candidate == DG_CAND_SAMPLE;
   GumbelDraw gd{make_sample_table(a->n_req, a->seed, a->block, a->req), g.canvas, a->step, 1.0f / tau,
                 c->buf<float4>(L.lm_gpart)};
+  const SelfCondOut so{c->buf<bf16_t>(L.sc_p), c->buf<float2>(L.sc_qpart)};
   STAGE(DG_STAGE_LMHEAD, launch_lmhead(s, c->buf<bf16_t>(L.u), rows, g.d_model, c->embed, g.vocab, a->d_canvas,
                                       tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
-                                      (int)(sizeof(dg_row_stats) / sizeof(float)), drawn ? &gd : nullptr));
+                                      (int)(sizeof(dg_row_stats) / sizeof(float)), drawn ? &gd : nullptr,
+                                      g.d_selfcond > 0 ? &so : nullptr));
   STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats,
                                         drawn ? c->buf<float4>(L.lm_gpart) : nullptr));
 }
@@ -307,10 +326,39 @@ void run_sampler(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
                                          a->step, k_s, tau, a->seed, a->block, a->req, a->d_stats, mode));
 }
 
-// LM-head statistics, merge and sampler over the rows in u (already final-normed).
+ReqTable make_table(dg_ctx* c, int n_req, const int32_t* req, int rows_per_req);
+
+// Self-conditioning signal of the step (the LM head left the unnormalised
+// distribution in sc_p / sc_qpart): normalise, contract with the embedding
+// over the vocabulary, the feed-forward layer, then store each row's signal
+// under its request slot for the slot's next step.
+void run_selfcond(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
+  const dg_config& g = c->cfg;
+  const dg_ws_layout& L = c->lay;
+  const int rows = a->n_req * g.canvas, d = g.d_model, F = g.d_selfcond;
+  c->stage_begin(s, DG_STAGE_SELFCOND);
+  launch_sc_norm(s, c->buf<bf16_t>(L.sc_p), c->buf<float2>(L.sc_qpart), rows, g.vocab);
+  launch_sc_gemm(s, c->buf<bf16_t>(L.sc_p), rows, g.vocab, c->embed_t, d, c->buf<float>(L.sc_part));
+  launch_sc_merge(s, c->buf<float>(L.sc_part), sc_gemm_splits(g.vocab), rows, d, c->buf<bf16_t>(L.sc_e));
+  launch_zero_f32(s, c->buf<float>(L.sc_g), (int64_t)rows * F);
+  launch_zero_f32(s, c->buf<float>(L.sc_u), (int64_t)rows * F);
+  launch_zero_f32(s, c->buf<float>(L.sc_out), (int64_t)rows * d);
+  launch_resid(s, c->buf<bf16_t>(L.sc_e), rows, d, c->sc_gate, F, c->buf<float>(L.sc_g), nullptr);
+  launch_resid(s, c->buf<bf16_t>(L.sc_e), rows, d, c->sc_up, F, c->buf<float>(L.sc_u), nullptr);
+  launch_swiglu_act(s, c->buf<float>(L.sc_g), c->buf<float>(L.sc_u), c->buf<bf16_t>(L.sc_hid), (int64_t)rows * F);
+  launch_resid(s, c->buf<bf16_t>(L.sc_hid), rows, F, c->sc_down, d, c->buf<float>(L.sc_out), nullptr);
+  const ReqTable rt = make_table(c, a->n_req, a->req, g.canvas);
+  launch_sc_store(s, c->buf<float>(L.sc_out), rt, d, c->buf<float>(L.sc_state));
+  c->stage_end();
+  for (int r = 0; r < a->n_req; ++r) c->sc_valid[a->req[r]] = 1;
+}
+
+// LM-head statistics, merge and sampler over the rows in u (already
+// final-normed), then the self-conditioning signal for the next step.
 void run_head(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   run_lm_stats(c, s, a);
   run_sampler(c, s, a);
+  if (c->cfg.d_selfcond > 0) run_selfcond(c, s, a);
 }
 
 dg_status check_ctx(dg_ctx* c) {
@@ -394,6 +442,16 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
   c->ws = (char*)d_workspace;
   c->embed = (const bf16_t*)w->embed;
   c->final_norm = (const bf16_t*)w->final_norm;
+  if (cfg->d_selfcond > 0) {
+    if (!w->sc_gate || !w->sc_up || !w->sc_down || !w->embed_t) {
+      delete c;
+      return DG_EINVAL;
+    }
+    c->sc_gate = (const bf16_t*)w->sc_gate;
+    c->sc_up = (const bf16_t*)w->sc_up;
+    c->sc_down = (const bf16_t*)w->sc_down;
+    c->embed_t = (const bf16_t*)w->embed_t;
+  }
   c->layers.resize(cfg->n_layers);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dg_layer_weights& s = w->layers[l];
@@ -422,6 +480,7 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
   c->kv.head_dim = cfg->head_dim;
   c->len.assign(cfg->max_requests, 0);
   c->prev_valid.assign(cfg->max_requests, 0);
+  c->sc_valid.assign(cfg->max_requests, 0);
   *out = c;
   return DG_OK;
 }
@@ -457,6 +516,7 @@ dg_status dg_reset(dg_ctx* c, int32_t req) {
   if (!c || req < 0 || req >= c->cfg.max_requests) return DG_EINVAL;
   c->len[req] = 0;
   c->prev_valid[req] = 0;
+  c->sc_valid[req] = 0;
   return DG_OK;
 }
 
@@ -537,7 +597,7 @@ dg_status dg_ar_step(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req,
   dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
   launch_lmhead(s, c->buf<bf16_t>(L.u), n_req, g.d_model, c->embed, g.vocab, d_tokens, 1.0f,
                 c->buf<float4>(L.lm_part), &stats[0].held_logit, (int)(sizeof(dg_row_stats) / sizeof(float)),
-                nullptr);
+                nullptr, nullptr);
   launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), n_req, 1.0f, stats, nullptr);
   const hipError_t ce = hipMemcpy2DAsync(d_next, sizeof(int32_t), &stats[0].argmax, sizeof(dg_row_stats),
                                          sizeof(int32_t), n_req, hipMemcpyDeviceToDevice, s);
@@ -553,7 +613,7 @@ dg_status dg_init_canvas(dg_ctx* c, void* stream, const dg_step_args* a) {
   if (st) return st;
   st = check_step_args(c, a, false);
   if (st) return st;
-  for (int r = 0; r < a->n_req; ++r) c->prev_valid[a->req[r]] = 0;  // a new block
+  for (int r = 0; r < a->n_req; ++r) c->prev_valid[a->req[r]] = c->sc_valid[a->req[r]] = 0;  // a new block
   launch_init_canvas((hipStream_t)stream, a->n_req, c->cfg.canvas, c->cfg.vocab, a->d_canvas,
                      a->d_committed, a->seed, a->block, a->req);
   return c->check_hip("dg_init_canvas");
@@ -586,8 +646,14 @@ dg_status denoise(dg_ctx* c, void* stream, const dg_step_args* a, float* d_h_lay
       (void)hipMemcpyAsync((char*)d_h_layers + (size_t)at * h_bytes, c->buf<float>(L.h), h_bytes,
                            hipMemcpyDeviceToDevice, s);
   };
+  SelfCondIn sci{nullptr, rt, 0u};
+  if (g.d_selfcond > 0) {
+    sci.state = c->buf<float>(L.sc_state);
+    for (int r = 0; r < a->n_req; ++r)
+      if (c->sc_valid[a->req[r]]) sci.valid |= 1u << r;
+  }
   STAGE(DG_STAGE_EMBED, launch_rope_table(s, rt, g.head_dim, g.rope_theta, c->buf<float2>(L.rope));
-        run_embed(c, s, a->d_canvas, rows, true));
+        run_embed(c, s, a->d_canvas, rows, true, g.d_selfcond > 0 ? &sci : nullptr));
   copy_h(0);
   const size_t idx_bytes = (size_t)rows * g.top_k * sizeof(int32_t);
   for (int l = 0; l < g.n_layers; ++l) {
@@ -634,7 +700,7 @@ dg_status dg_commit_block(dg_ctx* c, void* stream, int32_t n_req, const int32_t*
   if (st) return st;
   for (int r = 0; r < n_req; ++r) {
     c->len[req[r]] += g.canvas;
-    c->prev_valid[req[r]] = 0;  // the next block starts without a previous step
+    c->prev_valid[req[r]] = c->sc_valid[req[r]] = 0;  // the next block starts without a previous step
   }
   return DG_OK;
 }

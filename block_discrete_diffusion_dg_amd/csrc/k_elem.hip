@@ -10,7 +10,9 @@
 
 namespace {
 
-// h[row] = E[ids[row]] in fp32 and u[row] = bf16(RMSNorm(h[row]) * gain).
+// h[row] = E[ids[row]] (+ the request slot's self-conditioning signal, when
+// sc.state is set and the request's bit of sc.valid is) in fp32, and
+// u[row] = bf16(RMSNorm(h[row]) * gain).
 // E is fragment-major (it is also the LM head's streamed matrix): 8
 // consecutive elements of a row are contiguous, so the row is gathered in
 // 16-byte pieces through pack_index. Ids outside [0, V) are clamped (no fault).
@@ -18,21 +20,42 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
                                                     const bf16_t* __restrict__ E, int d, int V,
                                                     float* __restrict__ h,
                                                     const bf16_t* __restrict__ gain, float eps,
-                                                    bf16_t* __restrict__ u) {
+                                                    bf16_t* __restrict__ u, SelfCondIn sc) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   int id = ids[row];
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);
   float* dst = h + (int64_t)row * d;
+  const float* add = nullptr;
+  if (sc.state) {
+    const int r = row / sc.rt.rows_per_req, i = row % sc.rt.rows_per_req;
+    if ((sc.valid >> r) & 1u) add = sc.state + ((int64_t)sc.rt.slot[r] * sc.rt.rows_per_req + i) * d;
+  }
   float ss = 0.f;
   for (int c = tid * 8; c < d; c += 256 * 8) {
     const u32x4 v = ld16(E + pack_index(id, c, d));
+    float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = __uint_as_float(v[j] << 16), b = __uint_as_float(v[j] & 0xffff0000u);
-      dst[c + 2 * j] = a;
-      dst[c + 2 * j + 1] = b;
-      ss += a * a + b * b;
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+    if (add) {
+      const float4 a0 = *reinterpret_cast<const float4*>(add + c);
+      const float4 a1 = *reinterpret_cast<const float4*>(add + c + 4);
+      x[0] += a0.x;
+      x[1] += a0.y;
+      x[2] += a0.z;
+      x[3] += a0.w;
+      x[4] += a1.x;
+      x[5] += a1.y;
+      x[6] += a1.z;
+      x[7] += a1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dst[c + j] = x[j];
+      ss += x[j] * x[j];
     }
   }
   ss = wave_sum(ss);
@@ -40,13 +63,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   __syncthreads();
   const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
   for (int c = tid * 8; c < d; c += 256 * 8) {
-    const u32x4 v = ld16(E + pack_index(id, c, d));
+    // the thread reads back the elements it wrote above
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a = __uint_as_float(v[j] << 16), b = __uint_as_float(v[j] & 0xffff0000u);
-      o[j] = pack_bf16x2(a * inv * bf2f(gain[c + 2 * j]), b * inv * bf2f(gain[c + 2 * j + 1]));
-    }
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(dst[c + 2 * j] * inv * bf2f(gain[c + 2 * j]), dst[c + 2 * j + 1] * inv * bf2f(gain[c + 2 * j + 1]));
     *reinterpret_cast<u32x4*>(u + (int64_t)row * d + c) = o;
   }
 }
@@ -186,8 +207,9 @@ void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k
 }
 
 void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
-                  float* h, const bf16_t* gain, float eps, bf16_t* u) {
-  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, ids, embed, d, V, h, gain, eps, u);
+                  float* h, const bf16_t* gain, float eps, bf16_t* u, const SelfCondIn* sc) {
+  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, ids, embed, d, V, h, gain, eps, u,
+                     sc ? *sc : SelfCondIn{});
 }
 
 void launch_rmsnorm(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,

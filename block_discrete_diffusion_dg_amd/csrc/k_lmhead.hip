@@ -32,50 +32,33 @@ constexpr int LM_FRAGS = LM_ROWS / 16 + LM_COLS / 16;  // 1 KB fragments per ste
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// part[row][nt] = (max, sum 2^t, first argmax bits, sum 2^t t) over the 256
-// columns of tile nt, t = (L - max) * k2, k2 = log2(e) / tau; the lane holding the column
-// of the row's held token writes that logit to held_logit[row * held_stride].
-// Requires K % 128 == 0 and V % 256 == 0 (the configuration check enforces
-// d % 256 == 0 and V % 256 == 0).
-// With GUMBEL the epilogue also draws each row's sampled candidate over the
-// tile: the column with the largest L / tau + G (G the Gumbel noise of the
-// row's canvas position and that column, lowest column on ties) goes to
-// gpart[row][nt] = (key, column bits, its logit, 0).
-template <bool GUMBEL>
-__global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
-                                                     const bf16_t* __restrict__ E, int V,
-                                                     const int32_t* __restrict__ held, float k2,
-                                                     float4* __restrict__ part, float* __restrict__ held_logit,
-                                                     int held_stride, GumbelDraw gd) {
-  // four distinct objects: the compiler then orders each buffer's LDS reads
-  // only after the copies into that buffer
-  __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
-  __shared__ __align__(16) u32x4 r1[LM_FRAGS][64];
-  __shared__ __align__(16) u32x4 r2[LM_FRAGS][64];
-  __shared__ __align__(16) u32x4 r3[LM_FRAGS][64];
-  const int NT = V / LM_COLS, MC = div_up(rows, LM_ROWS);
-  int nt, mc;
-  xcd_tile_coords(NT, MC, nt, mc);
+// The 256 x 256 tile's K loop on the ring of four LDS buffers: acc[nb][mt]
+// of wave w = A rows row0 + 128(w/4) + 16mt + 4(lane/16) .. +3 against
+// columns 64(w%4) + 16nb + lane%16 of the fragment-major matrix W (its first
+// column block at W, K columns), over the nst 32-wide K-steps st0 ..
+// st0 + nst - 1. A is row-major with lda columns; rows past nrows repeat
+// the last row.
+__device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int lda, int row0, int nrows,
+                                              const bf16_t* __restrict__ W, int nst, int st0, f32x4 (&acc)[4][8],
+                                              u32x4 (&r0)[LM_FRAGS][64], u32x4 (&r1)[LM_FRAGS][64],
+                                              u32x4 (&r2)[LM_FRAGS][64], u32x4 (&r3)[LM_FRAGS][64]) {
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave >> 2, cq = wave & 3;  // the wave's row half and column quarter
-  const int row0 = mc * LM_ROWS, nrows = min(LM_ROWS, rows - row0);
-  const int c0 = nt * LM_COLS;
-
+  const int K = lda;
   // Fragments of a step: token-row block b at b (lane (g, i) holds row 16b + i,
   // reduction indices 8g .. 8g+7 of the step; rows past the end repeat the
-  // last row), vocabulary block b at 16 + b (the packed embedding's 512
+  // last row), column block b at 16 + b (the packed matrix's 512
   // contiguous elements of that block and step). Wave w copies token-row
-  // blocks w, w + 8 and vocabulary blocks w, w + 8.
-  const bf16_t* const srcA0 = A + (int64_t)(row0 + min(16 * wave + l16, nrows - 1)) * K + 8 * grp;
-  const bf16_t* const srcA1 = A + (int64_t)(row0 + min(16 * (wave + 8) + l16, nrows - 1)) * K + 8 * grp;
-  const bf16_t* const srcW0 = E + (int64_t)(c0 + 16 * wave) * K + lane * 8;
-  const bf16_t* const srcW1 = E + (int64_t)(c0 + 16 * (wave + 8)) * K + lane * 8;
-  const int nst = K / LM_BK;
+  // blocks w, w + 8 and column blocks w, w + 8.
+  const bf16_t* const srcA0 = A + (int64_t)(row0 + min(16 * wave + l16, nrows - 1)) * lda + 8 * grp;
+  const bf16_t* const srcA1 = A + (int64_t)(row0 + min(16 * (wave + 8) + l16, nrows - 1)) * lda + 8 * grp;
+  const bf16_t* const srcW0 = W + (int64_t)(16 * wave) * K + lane * 8;
+  const bf16_t* const srcW1 = W + (int64_t)(16 * (wave + 8)) * K + lane * 8;
   // steps past the end reload the last step (in bounds; never used), so every
   // step issues the same four copies and the wait counts stay static
   auto copy = [&](u32x4 (&buf)[LM_FRAGS][64], int st) {
-    st = min(st, nst - 1);
+    st = st0 + min(st, nst - 1);
     const bf16_t* pa0 = srcA0 + st * LM_BK;
     const bf16_t* pa1 = srcA1 + st * LM_BK;
     const int64_t wo = (int64_t)(st >> 1) * 1024 + (st & 1) * 512;
@@ -86,7 +69,6 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
     __builtin_amdgcn_global_load_lds(pw0, (__attribute__((address_space(3))) void*)&buf[16 + wave][0], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(pw1, (__attribute__((address_space(3))) void*)&buf[24 + wave][0], 16, 0, 0);
   };
-  f32x4 acc[4][8];  // [column block][row block] of the wave
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -133,6 +115,45 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+}
+
+// part[row][nt] = (max, sum 2^t, first argmax bits, sum 2^t t) over the 256
+// columns of tile nt, t = (L - max) * k2, k2 = log2(e) / tau; the lane holding the column
+// of the row's held token writes that logit to held_logit[row * held_stride].
+// Requires K % 128 == 0 and V % 256 == 0 (the configuration check enforces
+// d % 256 == 0 and V % 256 == 0).
+// With GUMBEL the epilogue also draws each row's sampled candidate over the
+// tile: the column with the largest L / tau + G (G the Gumbel noise of the
+// row's canvas position and that column, lowest column on ties) goes to
+// gpart[row][nt] = (key, column bits, its logit, 0).
+// With SC (self-conditioning) the epilogue also writes, for every row and
+// 64-column quarter of the tile, p_v = exp(L_v - m) (bf16, temperature 1, m
+// the quarter's maximum) to sc.p[row][v] and (m, sum of p_v in fp32) to
+// sc.qpart[row][v / 64]: the unnormalised predicted distribution that
+// sc_norm_kernel normalises.
+template <bool GUMBEL, bool SC>
+__global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
+                                                     const bf16_t* __restrict__ E, int V,
+                                                     const int32_t* __restrict__ held, float k2,
+                                                     float4* __restrict__ part, float* __restrict__ held_logit,
+                                                     int held_stride, GumbelDraw gd, SelfCondOut sc) {
+  // four distinct objects: the compiler then orders each buffer's LDS reads
+  // only after the copies into that buffer
+  __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r1[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r2[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r3[LM_FRAGS][64];
+  const int NT = V / LM_COLS, MC = div_up(rows, LM_ROWS);
+  int nt, mc;
+  xcd_tile_coords(NT, MC, nt, mc);
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave >> 2, cq = wave & 3;  // the wave's row half and column quarter
+  const int row0 = mc * LM_ROWS, nrows = min(LM_ROWS, rows - row0);
+  const int c0 = nt * LM_COLS;
+
+  f32x4 acc[4][8];  // [column block][row block] of the wave
+  ring_gemm_256(A, K, row0, nrows, E + (int64_t)c0 * K, K / LM_BK, 0, acc, r0, r1, r2, r3);
 
   // Epilogue in the ring's memory: red[4][256] (max, sum, argmax, entropy
   // sum) per column quarter and row, and the rows' held tokens.
@@ -171,6 +192,23 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
       if (l16 == 0)
         red[cq * LM_ROWS + 128 * rh + 16 * mt + 4 * grp + r] = float4{m[mt][r], z, __int_as_float(ix), zt};
     }
+  if constexpr (SC) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 128 * rh + 16 * mt + 4 * grp + r;
+        float z1 = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const float pv = __builtin_amdgcn_exp2f((acc[nb][mt][r] - m[mt][r]) * 1.4426950408889634f);
+          z1 += pv;
+          if (row < rows) sc.p[(int64_t)row * V + cw + 16 * nb + l16] = f2bf(pv);
+        }
+        z1 = row16_sum(z1);
+        if (l16 == 0 && row < rows) sc.qpart[(int64_t)row * (V / 64) + (cw >> 6)] = float2{m[mt][r], z1};
+      }
+  }
   float4* red2 = reinterpret_cast<float4*>(&r2[0][0]);  // [4][256] sampled-candidate partials
   if constexpr (GUMBEL) {
     // one Philox call per (lane, row) gives the noise of the lane's four
@@ -252,22 +290,80 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
   }
 }
 
+// Self-conditioning contraction over the vocabulary, split over K:
+// part[split][row][col] = sum over v in the split's range of P[row][v] ET[col][v],
+// P the normalised predicted distribution (bf16 [rows][V]), ET the tied
+// embedding transposed ([d][V], fragment-major). Work-group (column tile nt
+// of 256, split) of a grid of (d/256) x nsplit; each split covers nst
+// 32-wide steps of V.
+__global__ __launch_bounds__(512) void sc_gemm_kernel(const bf16_t* __restrict__ P, int rows, int V,
+                                                      const bf16_t* __restrict__ ET, int d, int nst,
+                                                      float* __restrict__ part) {
+  __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r1[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r2[LM_FRAGS][64];
+  __shared__ __align__(16) u32x4 r3[LM_FRAGS][64];
+  const int NT = d / LM_COLS;
+  const int nt = blockIdx.x % NT, split = blockIdx.x / NT;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rh = wave >> 2, cq = wave & 3;
+  const int c0 = nt * LM_COLS;
+  for (int row0 = 0; row0 < rows; row0 += LM_ROWS) {
+    const int nrows = min(LM_ROWS, rows - row0);
+    f32x4 acc[4][8];
+    ring_gemm_256(P, V, row0, nrows, ET + (int64_t)c0 * V, nst, split * nst, acc, r0, r1, r2, r3);
+    float* out = part + (int64_t)split * rows * d;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 128 * rh + 16 * mt + 4 * grp + r;
+        if (row < rows)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) out[(int64_t)row * d + c0 + 64 * cq + 16 * nb + l16] = acc[nb][mt][r];
+      }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+
+int sc_gemm_splits(int V) {
+  // enough splits for about one work-group per compute unit at d = 2048;
+  // each split a multiple of four 32-wide steps (the ring's unrolled loop)
+  int ns = 32;
+  while (ns > 1 && (V / 32) % (4 * ns)) ns >>= 1;
+  return ns;
+}
+
+void launch_sc_gemm(hipStream_t s, const bf16_t* p, int rows, int V, const bf16_t* et, int d, float* part) {
+  const int ns = sc_gemm_splits(V);
+  const int nst = V / 32 / ns;
+  hipLaunchKernelGGL(sc_gemm_kernel, dim3((d / LM_COLS) * ns), dim3(512), 0, s, p, rows, V, et, d, nst, part);
+}
 
 int lmhead_parts(int V) { return V / LM_COLS; }
 
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
                    const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
-                   const GumbelDraw* gumbel) {
+                   const GumbelDraw* gumbel, const SelfCondOut* sc) {
   const float k2 = 1.4426950408889634f / tau;
   const int NT = V / LM_COLS;
   const dim3 grid(NT * div_up(rows, LM_ROWS));
-  if (gumbel)
-    hipLaunchKernelGGL(lmhead_kernel<true>, grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part, held_logit,
-                       held_stride, *gumbel);
+  const GumbelDraw gd = gumbel ? *gumbel : GumbelDraw{};
+  const SelfCondOut so = sc ? *sc : SelfCondOut{};
+#define DG_LMHEAD(G_, S_)                                                                                          \
+  hipLaunchKernelGGL((lmhead_kernel<G_, S_>), grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part, held_logit, \
+                     held_stride, gd, so)
+  if (gumbel && sc)
+    DG_LMHEAD(true, true);
+  else if (gumbel)
+    DG_LMHEAD(true, false);
+  else if (sc)
+    DG_LMHEAD(false, true);
   else
-    hipLaunchKernelGGL(lmhead_kernel<false>, grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part,
-                       held_logit, held_stride, GumbelDraw{});
+    DG_LMHEAD(false, false);
+#undef DG_LMHEAD
 }

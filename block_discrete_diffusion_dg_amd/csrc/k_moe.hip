@@ -7,8 +7,8 @@
 // chunk) is one work item, of one of two kinds:
 //   gate/up:  hid[slot][f] = silu(x W_gate[f]) * (x W_up[f])   (bf16; 64 columns f)
 //   (weights bf16, or FP8 codes with per-row scales widened to bf16 in the tile)
-//   down:     y[slot][c]   = w_slot * (hid[slot] W_down[c])     (fp32, 128 columns c;
-//                                                              shared: ys[t][c])
+//   down:     y[slot][c]   = w_slot * (hid[slot] W_down[c])     (bf16, 128 columns c;
+//                                                              shared: ys[t][c], fp32)
 // The permutation kernel writes the exclusive item offsets of both kinds and
 // the chunk offsets per group, and zeroes the queue head and the per-chunk
 // completion counters. Work-groups take items from the queue: all gate/up
@@ -42,7 +42,8 @@ struct MoeArgs {
   const void *wg, *wu, *wd, *sg, *su, *sd;  // fragment-major weights (bf16, or FP8 codes)
   ExpertScales sc;                          // FP8 row scales (unused for bf16)
   bf16_t *hid, *hid_s;
-  float *y, *ys;
+  bf16_t* y;  // routed outputs [slots][d], weighted, rounded to bf16
+  float* ys;  // shared expert's outputs [rows][d]
 };
 
 // Start of weight row `row` of a fragment-major matrix with K columns (rows
@@ -245,7 +246,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       __syncthreads();
       const int K = shared ? p.Fs : p.F;
       const bf16_t* A = shared ? p.hid_s : p.hid + (int64_t)base * p.F;
-      float* out = shared ? p.ys : p.y + (int64_t)base * p.d;
+      float* outs = p.ys;                              // shared: fp32 rows
+      bf16_t* outr = p.y + (int64_t)base * p.d;        // routed: bf16 slots
       // routing weights of the chunk's slots, staged while the weights stream
       if (threadIdx.x < T::CH)
         s_w[threadIdx.x] = (!shared && threadIdx.x < nrows) ? p.wts[p.widx[base + row0 + threadIdx.x]] : 1.0f;
@@ -260,17 +262,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
         f32x4 acc0[MTI], acc1[MTI];
         stream_tile<MTI, true, EXPERT_DW, 2, W8>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
                                          Sd, W8 ? Sd + 16 : nullptr, K, acc0, acc1, lds);
+        if (shared) {
 #pragma unroll
-        for (int mt = 0; mt < MTI; ++mt)
+          for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = 16 * mt + 4 * grp + r;
-            if (row0 + q < n) {
-              float* o = out + (int64_t)(row0 + q) * p.d + c0 + l16;
-              o[0] = acc0[mt][r] * s_w[q];
-              o[16] = acc1[mt][r] * s_w[q];
+            for (int r = 0; r < 4; ++r) {
+              const int q = 16 * mt + 4 * grp + r;
+              if (row0 + q < n) {
+                float* o = outs + (int64_t)(row0 + q) * p.d + c0 + l16;
+                o[0] = acc0[mt][r];
+                o[16] = acc1[mt][r];
+              }
             }
-          }
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MTI; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int q = 16 * mt + 4 * grp + r;
+              if (row0 + q < n) {
+                bf16_t* o = outr + (int64_t)(row0 + q) * p.d + c0 + l16;
+                o[0] = f2bf(acc0[mt][r] * s_w[q]);
+                o[16] = f2bf(acc1[mt][r] * s_w[q]);
+              }
+            }
+        }
       };
       if (MT >= 8 && nrows > 64)
         down(std::integral_constant<int, (MT >= 8 ? 8 : MT)>{});
@@ -287,7 +303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
 // the next layer (or the final norm) on the row just completed.
 __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ ys,
-                                                          const float* __restrict__ y,
+                                                          const bf16_t* __restrict__ y,
                                                           const int32_t* __restrict__ slot, int d,
                                                           int k, const bf16_t* __restrict__ next_gain,
                                                           float eps, bf16_t* __restrict__ u) {
@@ -305,11 +321,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
     if (c >= d) break;
     float4 acc = *reinterpret_cast<const float4*>(ys + (int64_t)t * d + c);
     for (int j = 0; j < k; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)sl[j] * d + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      const u32x2 v = *reinterpret_cast<const u32x2*>(y + (int64_t)sl[j] * d + c);
+      acc.x += __uint_as_float(v.x << 16);
+      acc.y += __uint_as_float(v.x & 0xffff0000u);
+      acc.z += __uint_as_float(v.y << 16);
+      acc.w += __uint_as_float(v.y & 0xffff0000u);
     }
     float4* hp = reinterpret_cast<float4*>(h + (int64_t)t * d + c);
     float4 x = *hp;
@@ -391,7 +407,7 @@ void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, 
                         const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
                         const int32_t* widx, int32_t* items, const void* wg, const void* wu, const void* wd,
                         const void* sg, const void* su, const void* sd, const ExpertScales* fp8, bf16_t* hid,
-                        bf16_t* hid_s, float* y, float* ys) {
+                        bf16_t* hid_s, bf16_t* y, float* ys) {
   MoeArgs p{u,  rows, d,  F,  Fs, E,  perm, cnt, off, wts, widx, items, wg, wu, wd, sg,
             su, sd,   fp8 ? *fp8 : ExpertScales{}, hid, hid_s, y, ys};
   const int ch = moe_rows_per_chunk(rows, E, k);
@@ -401,7 +417,7 @@ void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, 
     launch_experts_fmt<false>(s, p, ch);
 }
 
-void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y, const int32_t* slot,
+void launch_moe_combine(hipStream_t s, float* h, const float* ys, const bf16_t* y, const int32_t* slot,
                         int rows, int d, int k, const bf16_t* next_gain, float eps, bf16_t* u) {
   hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps, u);
 }

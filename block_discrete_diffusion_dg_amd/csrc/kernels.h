@@ -7,8 +7,15 @@
 #include "philox.h"
 
 // k_elem.hip
+// Self-conditioning signal added to the input embeddings: state
+// [slots][rows_per_req][d] fp32, read for request r when bit r of valid is set.
+struct SelfCondIn {
+  const float* state;
+  ReqTable rt;
+  uint32_t valid;
+};
 void launch_embed(hipStream_t s, const int32_t* ids, int rows, const bf16_t* embed, int d, int V,
-                  float* h, const bf16_t* gain, float eps, bf16_t* u);
+                  float* h, const bf16_t* gain, float eps, bf16_t* u, const SelfCondIn* sc);
 void launch_rmsnorm(hipStream_t s, const float* h, const bf16_t* gain, int rows, int d, float eps,
                     bf16_t* u);
 void launch_rope_table(hipStream_t s, const ReqTable& rt, int dh, float theta, float2* cs);
@@ -38,10 +45,33 @@ struct GumbelDraw {
   float k1;
   float4* gpart;
 };
+// Self-conditioning outputs of the LM head: p [rows][V] bf16 exp(L - m) per
+// 64-column quarter, qpart [rows][V/64] (m, sum of exp) per quarter.
+struct SelfCondOut {
+  bf16_t* p;
+  float2* qpart;
+};
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
                    const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
-                   const GumbelDraw* gumbel);
+                   const GumbelDraw* gumbel, const SelfCondOut* sc);
 int lmhead_parts(int V);
+// Self-conditioning: part[split][rows][d] = P[:, split range] ET[:, split range]^T
+// (P bf16 [rows][V] normalised, ET fragment-major [d][V]); sc_gemm_splits(V) splits.
+int sc_gemm_splits(int V);
+void launch_sc_gemm(hipStream_t s, const bf16_t* p, int rows, int V, const bf16_t* et, int d, float* part);
+
+// k_selfcond.hip
+// p[row][v] *= exp(m_q - M) / Z1 (q = v / 64) with M = max_q m_q and
+// Z1 = sum_q exp(m_q - M) z_q from qpart: the normalised softmax(L) in bf16.
+void launch_sc_norm(hipStream_t s, bf16_t* p, const float2* qpart, int rows, int V);
+// e[row][c] = bf16(sum over splits of part[split][row][c]) (split order).
+void launch_sc_merge(hipStream_t s, const float* part, int nsplit, int rows, int d, bf16_t* e);
+// x[i] = 0 for i < n (fp32; a fill kernel, no memset node under capture).
+void launch_zero_f32(hipStream_t s, float* x, int64_t n);
+// hid[i] = bf16(silu(g[i]) * u[i]) for i < n.
+void launch_swiglu_act(hipStream_t s, const float* g, const float* u, bf16_t* hid, int64_t n);
+// state[slot[r]][i][c] = out[r * C + i][c] for the requests of the table.
+void launch_sc_store(hipStream_t s, const float* out, const ReqTable& rt, int d, float* state);
 
 // k_attn.hip
 int attn_splits(const ReqTable& rt, int Hq, int Hkv, int max_rows);
@@ -88,8 +118,8 @@ void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, 
                         const int32_t* perm, const int32_t* cnt, const int32_t* off, const float* wts,
                         const int32_t* widx, int32_t* items, const void* wg, const void* wu, const void* wd,
                         const void* sg, const void* su, const void* sd, const ExpertScales* fp8, bf16_t* hid,
-                        bf16_t* hid_s, float* y, float* ys);
-void launch_moe_combine(hipStream_t s, float* h, const float* ys, const float* y,
+                        bf16_t* hid_s, bf16_t* y, float* ys);
+void launch_moe_combine(hipStream_t s, float* h, const float* ys, const bf16_t* y,
                         const int32_t* slot, int rows, int d, int k, const bf16_t* next_gain,
                         float eps, bf16_t* u);
 

@@ -86,7 +86,9 @@ class Engine:
     def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
                  embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
                  max_requests: int = 1, max_rows: Optional[int] = None,
-                 expert_format: str = "bf16"):
+                 expert_format: str = "bf16", selfcond: Optional[Dict[str, torch.Tensor]] = None):
+        """selfcond: the self-conditioning feed-forward layer (sc_gate, sc_up
+        [F][d], sc_down [d][F], bf16, row-major), or None for none."""
         self.lib = B.load()
         self.cfg = cfg
         dev = embed.device
@@ -101,10 +103,19 @@ class Engine:
         c.rms_eps, c.rope_theta = cfg.rms_eps, cfg.rope_theta
         c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
         c.expert_format = B.WEIGHT_FORMAT[expert_format]
+        c.d_selfcond = 0 if selfcond is None else selfcond["sc_gate"].shape[0]
         self.expert_format = expert_format
         self.c_cfg = c
+        sc_ptrs = [None] * 4
+        self._keep = []
+        if selfcond is not None:
+            # the contraction over the vocabulary streams the transposed embedding
+            embed_t = pack_weight(embed.t().contiguous())
+            packed = [pack_weight(selfcond[n].contiguous()) for n in ("sc_gate", "sc_up", "sc_down")]
+            self._keep += packed + [embed_t]
+            sc_ptrs = [t.data_ptr() for t in packed] + [embed_t.data_ptr()]
         embed = pack_weight(embed)  # the tied LM head streams it fragment-major
-        self._keep = [embed, final_norm]
+        self._keep += [embed, final_norm]
         arr = (B.DGLayerWeights * max(1, len(layers)))()
         for i, lw in enumerate(layers):
             for name in LAYER_TENSORS:
@@ -119,7 +130,7 @@ class Engine:
                 self._keep.append(t)
                 setattr(arr[i], name, t.data_ptr())
         self._layer_arr = arr
-        w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr)
+        w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr, *sc_ptrs)
         kv_bytes = self.lib.dg_kv_cache_bytes(ctypes.byref(c))
         ws_bytes = self.lib.dg_workspace_bytes(ctypes.byref(c))
         if ws_bytes == 0:

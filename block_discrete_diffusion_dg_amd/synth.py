@@ -217,6 +217,22 @@ def make_embedding(cfg: ModelConfig, model_seed: int = 0, device="cpu") -> torch
                          cfg.weight_std, device)
 
 
+SELFCOND_TENSORS = ("sc_gate", "sc_up", "sc_down")
+
+
+def selfcond_shapes(cfg: ModelConfig, width: int) -> Dict[str, tuple]:
+    """The self-conditioning feed-forward layer: a SwiGLU block d -> width -> d."""
+    d = cfg.d_model
+    return {"sc_gate": (width, d), "sc_up": (width, d), "sc_down": (d, width)}
+
+
+def make_selfcond_weights(cfg: ModelConfig, width: int, model_seed: int = 0,
+                          device="cpu") -> Dict[str, torch.Tensor]:
+    """bf16 weights of the self-conditioning feed-forward layer ([out][in])."""
+    return {name: hashed_normal(shape, tensor_seed(model_seed, -2, name), cfg.weight_std, device)
+            for name, shape in selfcond_shapes(cfg, width).items()}
+
+
 def make_final_norm(cfg: ModelConfig, model_seed: int = 0, device="cpu",
                     gain_jitter: float = 0.0) -> torch.Tensor:
     return norm_gain(cfg.d_model, tensor_seed(model_seed, -1, "final_norm"), gain_jitter,

@@ -72,6 +72,8 @@ typedef struct dg_config {
   int32_t max_rows;      /* largest number of rows one call processes */
   float rms_eps, rope_theta, tau_first, tau_last;
   int32_t expert_format; /* dg_weight_format of the expert matrices (0 = bf16) */
+  int32_t d_selfcond;    /* width of the self-conditioning feed-forward layer
+                            (a multiple of 64); 0 = no self-conditioning */
 } dg_config;
 
 /* Storage of the routed and shared expert matrices (w_gate, w_up, w_down,
@@ -103,10 +105,22 @@ typedef struct dg_layer_weights {
 
 /* embed [V][d] is also the LM head (tied), fragment-major (dg_pack_weight
  * of the row-major [V][d] matrix); final_norm [d];
- * layers: host array of n_layers entries (copied by dg_create). */
+ * layers: host array of n_layers entries (copied by dg_create).
+ * Self-conditioning (explainer §3.2; only with d_selfcond > 0, else NULL):
+ * the predicted clean-token distribution of a denoising step, p_i =
+ * softmax(L_i) at temperature 1, goes through the tied embedding, e_i =
+ * sum_v p_iv E_v, and the SwiGLU layer s_i = (silu(e_i W_g^T) * e_i W_u^T)
+ * W_d^T, which is added to the input embedding of position i at the next
+ * denoising step of the same block:
+ *   sc_gate, sc_up [d_selfcond][d], sc_down [d][d_selfcond]: bf16,
+ *     fragment-major (dg_pack_weight);
+ *   embed_t: the embedding transposed, [d][V] (dg_pack_weight of the
+ *     row-major [d][V] matrix), the operand of the contraction over the
+ *     vocabulary (a second copy of the embedding, d * V * 2 bytes). */
 typedef struct dg_weights {
   const void *embed, *final_norm;
   const dg_layer_weights *layers;
+  const void *sc_gate, *sc_up, *sc_down, *embed_t;
 } dg_weights;
 
 /* Per-position statistics of a denoising step (optional output). */
@@ -247,7 +261,8 @@ dg_status dg_prefill(dg_ctx *ctx, void *stream, int32_t req, const int32_t *d_id
 dg_status dg_init_canvas(dg_ctx *ctx, void *stream, const dg_step_args *a);
 
 /* One denoising step over n_req canvases (explainer §3.1-§3.3):
- *   embed the canvas; for each layer: RMSNorm, QKV projection, RoPE at
+ *   embed the canvas (plus, with self-conditioning, the signal of the
+ *   slot's previous step of the same block); for each layer: RMSNorm, QKV projection, RoPE at
  *   positions len..len+C-1, attention of every canvas position over
  *   [cached prefix ; canvas] with no mask, output projection + residual,
  *   RMSNorm, router top-k softmax, token->expert permutation, grouped SwiGLU
@@ -262,6 +277,10 @@ dg_status dg_init_canvas(dg_ctx *ctx, void *stream, const dg_step_args *a);
  *     k_s = canvas instead when the block stops early (stop_entropy),
  *     the k_s positions of highest c_i (ties: lower i) take y_i and are marked
  *     committed; all others get a fresh uniform id and are cleared.
+ *   with self-conditioning, the step's own signal s_i (see dg_weights) is
+ *   kept per request slot for its next step; dg_init_canvas,
+ *   dg_commit_block and dg_reset of a slot forget it (the first step of a
+ *   block adds nothing).
  * The canvas K/V rows are written to cache rows [len, len+C) as scratch; the
  * cache length does not change and rows [0, len) are only read.
  * Needs len + C <= max_ctx for every request (else DG_ECAPACITY). */

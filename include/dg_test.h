@@ -33,7 +33,8 @@ extern "C" {
  *   slot     int32 [rows][k]         slot of each (token, choice)
  *   hid      bf16 [rows*k][F]        routed expert SwiGLU activations
  *   hid_s    bf16 [rows][Fs]         shared expert SwiGLU activations
- *   y        fp32 [rows*k][d]        routed expert outputs (weighted)
+ *   y        bf16 [rows*k][d]        routed expert outputs (weighted), then
+ *            fp32 [rows][d]          the shared expert's outputs
  *   lm_gpart float4 [rows][V/256]    sampled-candidate partials per
  *                                    vocabulary tile (key, id, logit, 0)
  *   stats    dg_row_stats [rows]     per-row LM-head statistics
@@ -57,9 +58,21 @@ extern "C" {
 #define DG_ITEMS_TOUCHED_TOTAL 410
 #define DG_ITEMS_PERMUTE_CALLS 412
 
+/* Self-conditioning buffers (size 0 without it; F = d_selfcond):
+ *   sc_p     bf16 [rows][V]          exp(L - m) per 64-column quarter, then
+ *                                    normalised in place to softmax(L)
+ *   sc_qpart float2 [rows][V/64]     (m, sum of exp) per quarter
+ *   sc_part  fp32 [splits][rows][d]  partial sums of the contraction with E
+ *   sc_e     bf16 [rows][d]          expected embedding e = p E
+ *   sc_g, sc_u fp32 [rows][F]        gate and up products
+ *   sc_hid   bf16 [rows][F]          SwiGLU activations
+ *   sc_out   fp32 [rows][d]          the signal of the step's rows
+ *   sc_state fp32 [max_requests][canvas][d]  each slot's signal for its
+ *                                    next step */
 typedef struct dg_ws_layout {
   size_t h, u, q, attn_o, attn_part, attn_ml, rope, z, idx, w, wslot, cnt, off, items, perm,
-      slot, hid, hid_s, y, lm_part, lm_gpart, stats, ids, ss, zpart, sync, prev, total;
+      slot, hid, hid_s, y, lm_part, lm_gpart, stats, ids, ss, zpart, sync, prev, sc_p, sc_qpart, sc_part, sc_e,
+      sc_g, sc_u, sc_hid, sc_out, sc_state, total;
 } dg_ws_layout;
 
 dg_status dg_workspace_layout(const dg_config *cfg, dg_ws_layout *out);
@@ -136,6 +149,7 @@ enum {
   DG_STAGE_LMHEAD,      /* LM head with fused vocabulary statistics */
   DG_STAGE_MERGE,       /* vocabulary statistics merge */
   DG_STAGE_SAMPLER,     /* confidence sampler / initial canvas */
+  DG_STAGE_SELFCOND,    /* self-conditioning signal for the next step */
   DG_STAGE_COUNT
 };
 dg_status dg_timing_enable(dg_ctx *ctx, int32_t enable);

@@ -44,7 +44,12 @@ Readings where the pages are silent:
   candidate = held token for committed positions, greedy argmax otherwise
   (or a sample of softmax(L/tau) by Gumbel-max, from counter-based uniforms);
   cumulative schedule k_s = floor(s * C / S);
-  committed positions hold their token until they fall out of the top-k_s.
+  committed positions hold their token until they fall out of the top-k_s;
+  self-conditioning (optional): the previous step's predicted distribution
+  p_i = softmax(L_i) (the network's own prediction, temperature 1) through
+  the tied embedding, e_i = sum_v p_iv E_v, then a SwiGLU feed-forward layer
+  d -> F_sc -> d, added to the next step's input embedding of position i;
+  nothing is added at the first step of a block.
 """
 from __future__ import annotations
 
@@ -260,6 +265,29 @@ def commit_count(step: int, n_steps: int, canvas: int) -> int:
     return (step * canvas) // n_steps
 
 
+def expected_embedding(L: np.ndarray, embed, chunk: int = 32768) -> np.ndarray:
+    """e_i = sum_v p_iv E_v with p_i = softmax(L_i) over the whole vocabulary:
+    the predicted clean-token distribution passed through the embedding
+    matrix (explainer §3.2, self-conditioning). float64 [n, d]."""
+    L = np.asarray(L, np.float64)
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    V = L.shape[1]
+    e = np.zeros((L.shape[0], embed.shape[1]), np.float64)
+    for v0 in range(0, V, chunk):
+        e += p[:, v0:v0 + chunk] @ f64(embed[v0:v0 + chunk])
+    return e
+
+
+def self_condition(L: np.ndarray, embed, sc: Dict, chunk: int = 32768) -> np.ndarray:
+    """Self-conditioning signal of a step (explainer §3.2): the expected
+    embedding under the step's predicted distribution, through a small
+    feed-forward layer (SwiGLU, weights sc_gate, sc_up [F_sc][d], sc_down
+    [d][F_sc]). Added to the next step's input embedding."""
+    e = expected_embedding(L, embed, chunk)
+    return swiglu(e, sc["sc_gate"], sc["sc_up"], sc["sc_down"])
+
+
 def logits(h: np.ndarray, final_norm, embed, cfg, chunk: int = 32768) -> np.ndarray:
     """RMSNorm(h) E^T over the whole vocabulary (tied LM head), float64 [n, V]."""
     hf = rms_norm(h, final_norm, cfg.rms_eps)
@@ -393,9 +421,14 @@ class Request:
 
 
 def forward_rows(weights, cfg, req: Request, ids: np.ndarray, causal: bool,
-                 keep_layers: Optional[List[Dict]] = None, stop_layer: Optional[int] = None):
-    """Embed ids and run the layer stack at positions req.length.. (no cache write)."""
+                 keep_layers: Optional[List[Dict]] = None, stop_layer: Optional[int] = None,
+                 sc_prev: Optional[np.ndarray] = None):
+    """Embed ids and run the layer stack at positions req.length.. (no cache
+    write). sc_prev, when given, is added to the input embeddings
+    (self-conditioning from the previous denoising step)."""
     h = f64(weights.embed[ids])
+    if sc_prev is not None:
+        h = h + sc_prev
     P = req.length
     ks, vs = [], []
     for l in range(cfg.n_layers if stop_layer is None else stop_layer):
@@ -437,17 +470,22 @@ def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step:
                  n_steps: int, seed: int, block: int, request: int,
                  keep: Optional[Dict] = None, confidence: str = "prob",
                  stop_entropy: float = 0.0, a_prev: Optional[np.ndarray] = None,
-                 candidate: str = "argmax"):
+                 candidate: str = "argmax", sc: Optional[Dict] = None,
+                 sc_prev: Optional[np.ndarray] = None):
     """One denoising step of one request's canvas.
 
     The canvas attends bidirectionally to itself and to the cached prefix; the
     LM head gives per-row statistics; the sampler accepts the top-k_s positions
     and re-noises the rest. The cache is read, never written. With
     stop_entropy > 0 the step checks adaptive stopping against a_prev, the
-    argmax of the previous step (None at the first step of a block).
+    argmax of the previous step (None at the first step of a block). With
+    self-conditioning weights sc, sc_prev (the previous step's signal, None
+    at the first step of a block) is added to the input embeddings and this
+    step's signal is left in keep["sc"].
     """
     layers = [] if keep is not None else None
-    h, _, _ = forward_rows(weights, cfg, req, np.asarray(x), causal=False, keep_layers=layers)
+    h, _, _ = forward_rows(weights, cfg, req, np.asarray(x), causal=False, keep_layers=layers,
+                           sc_prev=sc_prev)
     tau = tau_at(step, n_steps, cfg.tau_first, cfg.tau_last)
     L = logits(h, weights.final_norm, weights.embed, cfg)
     M, a, logZ, gx = row_stats(L, np.asarray(x), tau)
@@ -459,7 +497,8 @@ def denoise_step(weights, cfg, req: Request, x: np.ndarray, m: np.ndarray, step:
                                      drawn=drawn)
     if keep is not None:
         keep.update(layers=layers, h=h, logits=L, M=M, a=a, logZ=logZ, gx=gx, c=c,
-                    accept=accept, tau=tau, H=H, stop=stop, drawn=drawn)
+                    accept=accept, tau=tau, H=H, stop=stop, drawn=drawn,
+                    sc=self_condition(L, weights.embed, sc) if sc is not None else None)
     return x_new, m_new
 
 
@@ -482,17 +521,23 @@ def ar_step(weights, cfg, req: Request, token: int):
 
 
 def generate_block(weights, cfg, req: Request, n_steps: int, seed: int, block: int,
-                   request: int, confidence: str = "prob", stop_entropy: float = 0.0):
+                   request: int, confidence: str = "prob", stop_entropy: float = 0.0,
+                   sc: Optional[Dict] = None):
     """Denoise one block from uniform noise for at most n_steps (fewer when
-    adaptive stopping fires), then commit it. Returns (x, m, steps taken)."""
+    adaptive stopping fires), then commit it. With self-conditioning weights
+    sc, each step after the first adds the previous step's signal to its
+    input. Returns (x, m, steps taken)."""
     x, m = init_canvas(seed, block, request, cfg.canvas, cfg.vocab)
     a_prev = None
+    sc_prev = None
     taken = 0
     for s in range(1, n_steps + 1):
         keep: Dict = {}
         x, m = denoise_step(weights, cfg, req, x, m, s, n_steps, seed, block, request, keep=keep,
-                            confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev)
+                            confidence=confidence, stop_entropy=stop_entropy, a_prev=a_prev,
+                            sc=sc, sc_prev=sc_prev)
         a_prev = keep["a"]
+        sc_prev = keep["sc"]
         taken = s
         if keep["stop"]:
             break

@@ -77,12 +77,20 @@ class HostWeights:
         return self._final.cpu()
 
 
-def make_engine(cfg, max_ctx, max_requests=1, max_rows=None, gain_jitter=0.1, seed=0, expert_format="bf16"):
+def make_selfcond(cfg, width, seed=0):
+    """Self-conditioning weights on the GPU, scaled by 32 (exact in bf16) so
+    that the signal is not negligible next to the embeddings."""
+    return {k: (v * 32).to(torch.bfloat16) for k, v in synth.make_selfcond_weights(cfg, width, seed, "cuda").items()}
+
+
+def make_engine(cfg, max_ctx, max_requests=1, max_rows=None, gain_jitter=0.1, seed=0, expert_format="bf16",
+                selfcond=None):
     say(f"[engine] {cfg.name} L={cfg.n_layers} d={cfg.d_model} V={cfg.vocab} max_ctx={max_ctx} "
-        f"experts={expert_format}")
+        f"experts={expert_format} selfcond={None if selfcond is None else selfcond['sc_gate'].shape[0]}")
     layers, embed, final = gpu_weights(cfg, seed, gain_jitter)
     torch.cuda.synchronize()
-    eng = Engine(cfg, layers, embed, final, max_ctx, max_requests, max_rows, expert_format=expert_format)
+    eng = Engine(cfg, layers, embed, final, max_ctx, max_requests, max_rows, expert_format=expert_format,
+                 selfcond=selfcond)
     return eng, HostWeights(layers, embed, final, expert_format)
 
 

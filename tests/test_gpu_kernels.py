@@ -17,8 +17,8 @@ from block_discrete_diffusion_dg_amd import synth
 from block_discrete_diffusion_dg_amd.engine import Engine, stats_fields
 from oracle import model as om
 from oracle.philox import uniform_ids
-from tests.gpu_util import (REL_TOL, HostWeights, make_engine, max_rel, moe_with_experts, router_band,
-                            router_swaps, say, tie_gap_ok)
+from tests.gpu_util import (REL_TOL, HostWeights, make_engine, make_selfcond, max_rel, moe_with_experts,
+                            router_band, router_swaps, say, tie_gap_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -386,6 +386,36 @@ def test_sampler_fed_the_oracles_statistics(model, n_req, confidence, candidate)
         assert mo.sum() == om.commit_count(step, n_steps, C)
 
 
+@pytest.mark.parametrize("model,n_req,width", [(synth.TINY, 2, 64), (synth.FULL, 1, 704)])
+def test_self_conditioning_signal(model, n_req, width):
+    """The self-conditioning signal a step leaves for its slot's next step:
+    the expected embedding under softmax(L) (temperature 1, the whole
+    vocabulary) through the SwiGLU feed-forward layer, against the oracle on
+    the same bf16 final-normed rows."""
+    say(f"[selfcond] V={model.vocab} d={model.d_model} width={width} n_req={n_req}")
+    C = model.canvas
+    rows = n_req * C
+    sc = make_selfcond(model, width, 3)
+    cfg0 = dataclasses.replace(model, n_layers=0)
+    eng, hw = make_engine(cfg0, max_ctx=4 * C, max_requests=n_req + 1, max_rows=rows, selfcond=sc)
+    h, canvas, committed = _head_case(model, n_req, 2, 8, seed=17)
+    reqs = [n_req - r for r in range(n_req)]  # slots in reverse order: the signal is stored per slot
+    eng.test_head(reqs, h.cuda(), canvas.cuda(), committed.cuda(), 2, 8, [5] * n_req, [0] * n_req)
+    torch.cuda.synchronize()
+    u_gpu = eng.ws_view("u", torch.bfloat16, (rows, model.d_model)).cpu()
+    L_u = om.f64(u_gpu) @ om.f64(hw.embed).T
+    sc_cpu = {k: v.cpu() for k, v in sc.items()}
+    want = om.self_condition(L_u, hw.embed, sc_cpu)
+    state = eng.ws_view("sc_state", torch.float32, (n_req + 1, C, model.d_model)).cpu()
+    e_gpu = om.f64(eng.ws_view("sc_e", torch.bfloat16, (rows, model.d_model)).cpu())
+    err_e = max_rel(e_gpu, om.expected_embedding(L_u, hw.embed))
+    errs = [max_rel(om.f64(state[reqs[r]]), want[r * C:(r + 1) * C]) for r in range(n_req)]
+    say(f"  expected embedding error {err_e:.2e}; signal errors {[f'{e:.2e}' for e in errs]}; "
+        f"max |s| {np.abs(want).max():.3e}")
+    assert err_e <= REL_TOL and max(errs) <= REL_TOL
+    assert np.abs(want).max() > 1e-6
+
+
 # ------------------------------------------------------------------------ attention alone
 
 @pytest.mark.parametrize("model,P,n,causal", [(synth.TINY, 64, 32, False), (synth.TINY, 75, 37, True),
@@ -520,10 +550,12 @@ def test_layer_parity(name, causal, P, C, over, fmt):
     # experts on identical operands: the GPU's MoE-normed rows and routing weights
     w_gpu = om.f64(eng.ws_view("w", torch.float32, (C, cfg.top_k)).cpu())
     slot_gpu = eng.ws_view("slot", torch.int32, (C, cfg.top_k)).cpu().numpy()
-    y = om.f64(eng.ws_view("y", torch.float32, (eng.max_rows * cfg.top_k + eng.max_rows,
-                                                 cfg.d_model)).cpu())
+    n_slots = eng.max_rows * cfg.top_k
+    y = om.f64(eng.ws_view("y", torch.bfloat16, (n_slots, cfg.d_model)).cpu())
+    ys = om.f64(eng.ws[eng.layout.y + n_slots * cfg.d_model * 2:][:eng.max_rows * cfg.d_model * 4]
+                .view(torch.float32).view(eng.max_rows, cfg.d_model).cpu())
     ys_ref = om.swiglu(u2, lw["ws_gate"], lw["ws_up"], lw["ws_down"])
-    assert max_rel(y[eng.max_rows * cfg.top_k:][:C], ys_ref) <= REL_TOL
+    assert max_rel(ys[:C], ys_ref) <= REL_TOL
     for t in range(0, C, max(1, C // 16)):
         for j in range(cfg.top_k):
             e = idx_gpu[t, j]

@@ -221,15 +221,38 @@ def _bad_rope_angles_freq(positions, head_dim, theta):
     return np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
 
 
+def _pin_expected_embedding():
+    V, d = 50, 6
+    E = RNG.normal(size=(V, d))
+    L = np.full((1, V), -1e4)
+    L[0, 3], L[0, 40] = np.log(3.0), 0.0
+    two = np.allclose(om.expected_embedding(L, E, chunk=16)[0], 0.75 * E[3] + 0.25 * E[40], atol=1e-12)
+    uni = np.allclose(om.expected_embedding(np.zeros((1, V)), E, chunk=16)[0], E.mean(0), atol=1e-12)
+    return bool(two and uni)
+
+
+def _bad_expected_embedding_tau(L, embed, chunk=32768):
+    return _real["expected_embedding"](np.asarray(L, np.float64) / 0.8, embed, chunk)  # sampler temperature
+
+
+def _bad_expected_embedding_unnormalised(L, embed, chunk=32768):
+    L = np.asarray(L, np.float64)
+    p = np.exp(L - L.max(axis=1, keepdims=True))  # softmax without its denominator
+    return p @ om.f64(embed)
+
+
 _real_fp8 = {"e4m3_encode": om_fp8.e4m3_encode}
 
 _real = {"attention": om.attention, "moe": om.moe, "row_stats": om.row_stats,
+         "expected_embedding": om.expected_embedding,
          "row_entropy": om.row_entropy, "gumbel_candidates": om.gumbel_candidates}
 
 CASES = [
     ("rope", _bad_rope, _pin_rope),
     ("rope_angles", _bad_rope_angles_freq, _pin_rope_freq),
     ("swiglu", _bad_swiglu_silu_on_up, _pin_swiglu),
+    ("expected_embedding", _bad_expected_embedding_tau, _pin_expected_embedding),
+    ("expected_embedding", _bad_expected_embedding_unnormalised, _pin_expected_embedding),
     ("attention", _bad_attention_scale, _pin_attention),
     ("attention", _bad_attention_gqa, _pin_attention),
     ("route", _bad_route_ties, _pin_route),

@@ -387,6 +387,61 @@ def test_sampler_float32_precision_agrees_with_float64_off_ties():
             assert np.array_equal(acc32, acc64)
 
 
+# ----------------------------------------------------------------------------- self-conditioning
+
+def test_expected_embedding_closed_forms():
+    V, d = 300, 12
+    E = RNG.normal(size=(V, d)) * 0.5
+    # equal logits: the uniform distribution gives the mean embedding row
+    assert np.allclose(om.expected_embedding(np.full((2, V), 0.7), E, chunk=64), E.mean(0)[None].repeat(2, 0),
+                       rtol=1e-12, atol=1e-14)
+    # one logit far above the rest: a one-hot distribution picks that row
+    L = RNG.normal(size=(3, V))
+    L[np.arange(3), [5, 77, 299]] += 800.0
+    assert np.allclose(om.expected_embedding(L, E, chunk=64), E[[5, 77, 299]], rtol=0, atol=1e-12)
+    # two tokens with odds 3 : 1 (temperature 1): 3/4 E_a + 1/4 E_b
+    L = np.full((1, V), -1e4)
+    L[0, 10], L[0, 200] = np.log(3.0), 0.0
+    assert np.allclose(om.expected_embedding(L, E, chunk=64)[0], 0.75 * E[10] + 0.25 * E[200], atol=1e-12)
+    # random rows: scipy's softmax times E
+    L = RNG.normal(size=(4, V)) * 3
+    assert np.allclose(om.expected_embedding(L, E, chunk=64), scipy.special.softmax(L, axis=1) @ E,
+                       rtol=1e-12, atol=1e-14)
+
+
+def test_self_condition_is_the_feed_forward_layer_of_the_expected_embedding():
+    V, d, F_ = 200, 16, 24
+    E = RNG.normal(size=(V, d)) * 0.3
+    sc = {"sc_gate": RNG.normal(size=(F_, d)), "sc_up": RNG.normal(size=(F_, d)), "sc_down": RNG.normal(size=(d, F_))}
+    L = RNG.normal(size=(5, V)) * 2
+    e = scipy.special.softmax(L, axis=1) @ E
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    want = (F.silu(t(e) @ t(sc["sc_gate"]).T) * (t(e) @ t(sc["sc_up"]).T)) @ t(sc["sc_down"]).T
+    assert np.allclose(om.self_condition(L, E, sc), want.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_self_conditioning_in_the_loop():
+    # zero layers: logits = RMSNorm(E[x] + s) E^T, with s added only after the first step
+    cfg, hw = _tiny_model(n_layers=0)
+    sc = synth.make_selfcond_weights(cfg, 64, 0)
+    sc = {k: v.float() * 40.0 for k, v in sc.items()}  # large enough to move the logits
+    req = om.Request(cfg, 128)
+    x, m = om.init_canvas(5, 0, 0, cfg.canvas, cfg.vocab)
+    k1, k1_plain = {}, {}
+    x1, m1 = om.denoise_step(hw, cfg, req, x, m, 1, 4, 5, 0, 0, keep=k1, sc=sc, sc_prev=None)
+    om.denoise_step(hw, cfg, req, x, m, 1, 4, 5, 0, 0, keep=k1_plain)
+    assert np.array_equal(k1["logits"], k1_plain["logits"])  # nothing added at the first step
+    E = om.f64(hw.embed)
+    assert np.allclose(k1["sc"], om.self_condition(k1["logits"], hw.embed, sc), rtol=1e-12, atol=1e-14)
+    k2 = {}
+    om.denoise_step(hw, cfg, req, x1, m1, 2, 4, 5, 0, 0, keep=k2, sc=sc, sc_prev=k1["sc"])
+    g = om.f64(hw.final_norm)
+    h_in = torch.from_numpy(E[x1] + k1["sc"])
+    hf = F.rms_norm(h_in, (cfg.d_model,), torch.from_numpy(g), eps=cfg.rms_eps).numpy()
+    assert np.allclose(k2["logits"], hf @ E.T, rtol=1e-10, atol=1e-12)
+    assert np.abs(k2["logits"] - hf @ E.T).max() < 1e-9 < np.abs(k1["sc"]).max()
+
+
 def test_entropy_closed_forms_and_library():
     tau = 0.7
     # equal logits: the uniform distribution, H = log V
