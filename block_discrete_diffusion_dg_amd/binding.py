@@ -25,7 +25,7 @@ class DGConfig(ctypes.Structure):
                                      "n_experts", "top_k", "d_expert", "d_shared", "vocab",
                                      "canvas", "max_ctx", "max_requests", "max_rows")] + \
                [(n, c_f32) for n in ("rms_eps", "rope_theta", "tau_first", "tau_last")] + \
-               [("expert_format", c_i32), ("d_selfcond", c_i32)]
+               [("expert_format", c_i32), ("d_selfcond", c_i32), ("lmhead_format", c_i32)]
 
 
 WEIGHT_FORMAT = {"bf16": 0, "fp8": 1}
@@ -50,7 +50,8 @@ class DGLayerWeights(ctypes.Structure):
 
 class DGWeights(ctypes.Structure):
     _fields_ = [("embed", c_vp), ("final_norm", c_vp), ("layers", ctypes.POINTER(DGLayerWeights)),
-                ("sc_gate", c_vp), ("sc_up", c_vp), ("sc_down", c_vp), ("embed_t", c_vp)]
+                ("sc_gate", c_vp), ("sc_up", c_vp), ("sc_down", c_vp), ("embed_t", c_vp),
+                ("embed_fp8", c_vp), ("embed_scale", c_vp)]
 
 
 class DGRowStats(ctypes.Structure):
@@ -92,6 +93,7 @@ SIGNATURES = {
     "dg_destroy": (None, [c_vp]),
     "dg_pack_weight": (c_i32, [c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_quantize_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
+    "dg_quantize_fp8_lmhead": (c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.c_int64, c_i32]),
     "dg_prefill": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32]),
     "dg_ar_step": (c_i32, [c_vp, c_vp, c_i32, ctypes.POINTER(c_i32), c_vp, c_vp]),
     "dg_init_canvas": (c_i32, [c_vp, c_vp, ctypes.POINTER(DGStepArgs)]),

@@ -100,15 +100,15 @@ const char* check_config(const dg_config& c) {
   if (c.canvas <= 0 || c.canvas % 16 || c.canvas > 1024) return "canvas must be a multiple of 16, at most 1024";
   if (c.max_requests <= 0) return "max_requests must be positive";
   if (c.max_rows < c.canvas || c.max_rows > DG_MAX_REQ * c.canvas)
-    return "max_rows must lie in [canvas, 16*canvas]";
-  if (permute_lds_bytes(c.max_rows, c.n_experts, c.top_k) > 57344)
-    return "12 * n_experts * ceil(max_rows/64) must not exceed 56 KiB (routing tables in LDS)";
+    return "max_rows must lie in [canvas, 32*canvas]";
   if (c.max_ctx < 2 * c.canvas || c.max_ctx % 32) return "max_ctx must be a multiple of 32 holding at least two blocks";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f) || !(c.tau_first > 0.f) || !(c.tau_last > 0.f))
     return "rms_eps >= 0, rope_theta > 0 and temperatures > 0 required";
   if (c.expert_format != DG_WEIGHTS_BF16 && c.expert_format != DG_WEIGHTS_FP8)
     return "expert_format must be DG_WEIGHTS_BF16 or DG_WEIGHTS_FP8";
   if (c.d_selfcond < 0 || c.d_selfcond % 64) return "d_selfcond must be 0 or a positive multiple of 64";
+  if (c.lmhead_format != DG_WEIGHTS_BF16 && c.lmhead_format != DG_WEIGHTS_FP8)
+    return "lmhead_format must be DG_WEIGHTS_BF16 or DG_WEIGHTS_FP8";
   return nullptr;
 }
 
@@ -120,6 +120,8 @@ struct dg_ctx {
   const bf16_t* embed;
   const bf16_t* final_norm;
   const bf16_t *sc_gate = nullptr, *sc_up = nullptr, *sc_down = nullptr, *embed_t = nullptr;
+  LmFp8 lm8{nullptr, nullptr};  // FP8 LM-head weights (lmhead_format == DG_WEIGHTS_FP8)
+  const LmFp8* lm_fp8() const { return lm8.codes ? &lm8 : nullptr; }
   KvGeom kv;
   char* ws;
   dg_ws_layout lay;
@@ -301,7 +303,7 @@ void run_lm_stats(dg_ctx* c, hipStream_t s, const dg_step_args* a) {
   STAGE(DG_STAGE_LMHEAD, launch_lmhead(s, c->buf<bf16_t>(L.u), rows, g.d_model, c->embed, g.vocab, a->d_canvas,
                                       tau, c->buf<float4>(L.lm_part), &stats[0].held_logit,
                                       (int)(sizeof(dg_row_stats) / sizeof(float)), drawn ? &gd : nullptr,
-                                      g.d_selfcond > 0 ? &so : nullptr));
+                                      g.d_selfcond > 0 ? &so : nullptr, c->lm_fp8()));
   STAGE(DG_STAGE_MERGE, launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), rows, tau, stats,
                                         drawn ? c->buf<float4>(L.lm_gpart) : nullptr));
 }
@@ -371,7 +373,7 @@ dg_status check_step_args(dg_ctx* c, const dg_step_args* a, bool need_step) {
   const dg_config& g = c->cfg;
   if (!a || a->n_req <= 0 || a->n_req > DG_MAX_REQ || !a->req || !a->d_canvas || !a->d_committed ||
       !a->seed || !a->block)
-    return c->fail(DG_EINVAL, "step args: null pointer or n_req outside 1..16");
+    return c->fail(DG_EINVAL, "step args: null pointer or n_req outside 1..32");
   if (a->n_req * g.canvas > g.max_rows) return c->fail(DG_ECAPACITY, "n_req * canvas exceeds max_rows");
   for (int r = 0; r < a->n_req; ++r) {
     if (a->req[r] < 0 || a->req[r] >= g.max_requests) return c->fail(DG_EINVAL, "request slot out of range");
@@ -442,6 +444,13 @@ dg_status dg_create(const dg_config* cfg, const dg_weights* w, void* d_kv_cache,
   c->ws = (char*)d_workspace;
   c->embed = (const bf16_t*)w->embed;
   c->final_norm = (const bf16_t*)w->final_norm;
+  if (cfg->lmhead_format == DG_WEIGHTS_FP8) {
+    if (!w->embed_fp8 || !w->embed_scale) {
+      delete c;
+      return DG_EINVAL;
+    }
+    c->lm8 = LmFp8{(const uint8_t*)w->embed_fp8, w->embed_scale};
+  }
   if (cfg->d_selfcond > 0) {
     if (!w->sc_gate || !w->sc_up || !w->sc_down || !w->embed_t) {
       delete c;
@@ -503,7 +512,17 @@ dg_status dg_quantize_fp8(void* stream, const void* d_src, void* d_dst, float* d
   const char* d0 = (const char*)d_dst;
   const int64_t src_bytes = n * (int64_t)k * 2, dst_bytes = n * (int64_t)k;
   if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return DG_EINVAL;  // overlapping buffers
-  launch_quant_fp8((hipStream_t)stream, (const bf16_t*)d_src, (uint8_t*)d_dst, d_scale, n, k);
+  launch_quant_fp8((hipStream_t)stream, (const bf16_t*)d_src, (uint8_t*)d_dst, d_scale, n, k, false);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
+}
+
+dg_status dg_quantize_fp8_lmhead(void* stream, const void* d_src, void* d_dst, float* d_scale, int64_t n, int32_t k) {
+  if (!d_src || !d_dst || !d_scale || n <= 0 || k <= 0 || n % 16 != 0 || k % 64 != 0) return DG_EINVAL;
+  const char* s0 = (const char*)d_src;
+  const char* d0 = (const char*)d_dst;
+  const int64_t src_bytes = n * (int64_t)k * 2, dst_bytes = n * (int64_t)k;
+  if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return DG_EINVAL;  // overlapping buffers
+  launch_quant_fp8((hipStream_t)stream, (const bf16_t*)d_src, (uint8_t*)d_dst, d_scale, n, k, true);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
 }
 
@@ -579,7 +598,7 @@ dg_status dg_ar_step(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req,
   if (st) return st;
   const dg_config& g = c->cfg;
   if (n_req <= 0 || n_req > DG_MAX_REQ || !req || !d_tokens || !d_next)
-    return c->fail(DG_EINVAL, "ar_step: null pointer or n_req outside 1..16");
+    return c->fail(DG_EINVAL, "ar_step: null pointer or n_req outside 1..32");
   if (n_req > g.max_rows) return c->fail(DG_ECAPACITY, "ar_step: n_req exceeds max_rows");
   for (int r = 0; r < n_req; ++r) {
     if (req[r] < 0 || req[r] >= g.max_requests) return c->fail(DG_EINVAL, "ar_step: slot out of range");
@@ -597,7 +616,7 @@ dg_status dg_ar_step(dg_ctx* c, void* stream, int32_t n_req, const int32_t* req,
   dg_row_stats* stats = c->buf<dg_row_stats>(L.stats);
   launch_lmhead(s, c->buf<bf16_t>(L.u), n_req, g.d_model, c->embed, g.vocab, d_tokens, 1.0f,
                 c->buf<float4>(L.lm_part), &stats[0].held_logit, (int)(sizeof(dg_row_stats) / sizeof(float)),
-                nullptr, nullptr);
+                nullptr, nullptr, c->lm_fp8());
   launch_lm_merge(s, c->buf<float4>(L.lm_part), lmhead_parts(g.vocab), n_req, 1.0f, stats, nullptr);
   const hipError_t ce = hipMemcpy2DAsync(d_next, sizeof(int32_t), &stats[0].argmax, sizeof(dg_row_stats),
                                          sizeof(int32_t), n_req, hipMemcpyDeviceToDevice, s);

@@ -11,7 +11,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-#define DG_MAX_REQ 16       // requests batched into one call
+#define DG_MAX_REQ 32       // requests batched into one call
 
 // Expert work list (int32 words in the workspace "items" buffer), written by
 // the permutation kernel and consumed by the expert kernel. Groups: 0 = the

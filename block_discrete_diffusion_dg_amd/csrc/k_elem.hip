@@ -168,6 +168,8 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 // (e = 0 for a zero row; 448 = 0.875 * 2^9), and dst holds the E4M3 code of
 // src * 2^-e (exact scaling) of every element at its pack8_index position.
 // Each lane encodes 8 consecutive elements (8 contiguous bytes of dst).
+// LM: codes in the step-major LM-head layout (lm8_index) instead of pack8_index.
+template <bool LM>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                         float* __restrict__ scale, int64_t n, int k) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -188,15 +190,18 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const bf16_t* __restrict
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) w[j >> 2] |= e4m3_code(ldexpf(bf2f(r[c0 + j]), -e)) << (8 * (j & 3));
-    *reinterpret_cast<u32x2*>(dst + pack8_index(row, c0, k)) = u32x2{w[0], w[1]};
+    *reinterpret_cast<u32x2*>(dst + (LM ? lm8_index(row, c0, n) : pack8_index(row, c0, k))) = u32x2{w[0], w[1]};
   }
 }
 
 }  // namespace
 
-void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k) {
+void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k, bool lmhead) {
   const int64_t blocks = (n + 3) / 4;
-  hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, scale, n, k);
+  if (lmhead)
+    hipLaunchKernelGGL(quant_fp8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, scale, n, k);
+  else
+    hipLaunchKernelGGL(quant_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, scale, n, k);
 }
 
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k) {

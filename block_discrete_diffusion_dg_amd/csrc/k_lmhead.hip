@@ -22,6 +22,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "philox.h"
+#include "stream.h"
 
 namespace {
 
@@ -34,14 +35,22 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 
 // The 256 x 256 tile's K loop on the ring of four LDS buffers: acc[nb][mt]
 // of wave w = A rows row0 + 128(w/4) + 16mt + 4(lane/16) .. +3 against
-// columns 64(w%4) + 16nb + lane%16 of the fragment-major matrix W (its first
-// column block at W, K columns), over the nst 32-wide K-steps st0 ..
-// st0 + nst - 1. A is row-major with lda columns; rows past nrows repeat
-// the last row.
+// columns 64(w%4) + 16nb + lane%16 of the matrix W, over the nst 32-wide
+// K-steps st0 .. st0 + nst - 1. A is row-major with lda (= K) columns; rows
+// past nrows repeat the last row.
+// bf16 W: fragment-major (pack_index), W points at the tile's first column
+// block. W8: FP8 codes in the step-major layout (lm8_index) of a matrix with
+// n_w rows, W8 points at the tile's first block inside step 0 (byte c0 * 32),
+// w8s at the tile's 256 row scales; each step's 16 blocks are 8 KB of
+// consecutive bytes, copied by one load-to-LDS operation per wave, and the
+// codes are widened to bf16 times the row scale as they are read.
+template <bool W8>
 __device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int lda, int row0, int nrows,
-                                              const bf16_t* __restrict__ W, int nst, int st0, f32x4 (&acc)[4][8],
-                                              u32x4 (&r0)[LM_FRAGS][64], u32x4 (&r1)[LM_FRAGS][64],
-                                              u32x4 (&r2)[LM_FRAGS][64], u32x4 (&r3)[LM_FRAGS][64]) {
+                                              const bf16_t* __restrict__ W, const uint8_t* __restrict__ W8b,
+                                              const float* __restrict__ w8s, int64_t n_w, int nst, int st0,
+                                              f32x4 (&acc)[4][8], u32x4 (&r0)[LM_FRAGS][64],
+                                              u32x4 (&r1)[LM_FRAGS][64], u32x4 (&r2)[LM_FRAGS][64],
+                                              u32x4 (&r3)[LM_FRAGS][64]) {
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rh = wave >> 2, cq = wave & 3;  // the wave's row half and column quarter
@@ -49,25 +58,35 @@ __device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int 
   // Fragments of a step: token-row block b at b (lane (g, i) holds row 16b + i,
   // reduction indices 8g .. 8g+7 of the step; rows past the end repeat the
   // last row), column block b at 16 + b (the packed matrix's 512
-  // contiguous elements of that block and step). Wave w copies token-row
-  // blocks w, w + 8 and column blocks w, w + 8.
+  // contiguous elements of that block and step; with W8 the 16 blocks' codes
+  // fill entries 16 .. 23, 512 bytes a block). Wave w copies token-row
+  // blocks w, w + 8 and column blocks w, w + 8 (W8: bytes 1024w .. +1023).
   const bf16_t* const srcA0 = A + (int64_t)(row0 + min(16 * wave + l16, nrows - 1)) * lda + 8 * grp;
   const bf16_t* const srcA1 = A + (int64_t)(row0 + min(16 * (wave + 8) + l16, nrows - 1)) * lda + 8 * grp;
-  const bf16_t* const srcW0 = W + (int64_t)(16 * wave) * K + lane * 8;
-  const bf16_t* const srcW1 = W + (int64_t)(16 * (wave + 8)) * K + lane * 8;
+  const bf16_t* const srcW0 = W8 ? nullptr : W + (int64_t)(16 * wave) * K + lane * 8;
+  const bf16_t* const srcW1 = W8 ? nullptr : W + (int64_t)(16 * (wave + 8)) * K + lane * 8;
+  const uint8_t* const src8 = W8 ? W8b + 1024 * wave + 16 * lane : nullptr;
+  float sc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) sc[nb] = W8 ? w8s[16 * (4 * cq + nb) + l16] : 1.0f;
   // steps past the end reload the last step (in bounds; never used), so every
-  // step issues the same four copies and the wait counts stay static
+  // step issues the same copies and the wait counts stay static
   auto copy = [&](u32x4 (&buf)[LM_FRAGS][64], int st) {
     st = st0 + min(st, nst - 1);
     const bf16_t* pa0 = srcA0 + st * LM_BK;
     const bf16_t* pa1 = srcA1 + st * LM_BK;
-    const int64_t wo = (int64_t)(st >> 1) * 1024 + (st & 1) * 512;
-    const bf16_t* pw0 = srcW0 + wo;
-    const bf16_t* pw1 = srcW1 + wo;
     __builtin_amdgcn_global_load_lds(pa0, (__attribute__((address_space(3))) void*)&buf[wave][0], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(pa1, (__attribute__((address_space(3))) void*)&buf[wave + 8][0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pw0, (__attribute__((address_space(3))) void*)&buf[16 + wave][0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(pw1, (__attribute__((address_space(3))) void*)&buf[24 + wave][0], 16, 0, 0);
+    if constexpr (W8) {
+      __builtin_amdgcn_global_load_lds(src8 + (int64_t)st * n_w * 32,
+                                       (__attribute__((address_space(3))) void*)&buf[16 + wave][0], 16, 0, 0);
+    } else {
+      const int64_t wo = (int64_t)(st >> 1) * 1024 + (st & 1) * 512;
+      __builtin_amdgcn_global_load_lds(srcW0 + wo, (__attribute__((address_space(3))) void*)&buf[16 + wave][0], 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(srcW1 + wo, (__attribute__((address_space(3))) void*)&buf[24 + wave][0], 16,
+                                       0, 0);
+    }
   };
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
@@ -76,7 +95,15 @@ __device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int 
   auto compute = [&](const u32x4 (&buf)[LM_FRAGS][64]) {
     u32x4 wf[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) wf[nb] = buf[16 + 4 * cq + nb][lane];
+    for (int nb = 0; nb < 4; ++nb) {
+      if constexpr (W8) {
+        const int b = 4 * cq + nb;  // block b: bytes 512b .. of entries 16 ..
+        const u32x2 c = reinterpret_cast<const u32x2*>(&buf[16][0])[64 * b + lane];
+        wf[nb] = widen_fp8(c.x, c.y, sc[nb]);
+      } else {
+        wf[nb] = buf[16 + 4 * cq + nb][lane];
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const u32x4 af = buf[8 * rh + mt][lane];
@@ -85,13 +112,14 @@ __device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int 
     }
   };
   // Step st: wait until this wave's copies of step st have landed (the two
-  // later steps may still be in flight), then a barrier without a memory
-  // fence (a fence would wait for every copy in flight): after it, every
-  // wave's copies of step st are in place and every wave has finished step
-  // st - 1, whose buffer the next copy reuses.
+  // later steps' copies may still be in flight: four per step, three with
+  // W8), then a barrier without a memory fence (a fence would wait for every
+  // copy in flight): after it, every wave's copies of step st are in place
+  // and every wave has finished step st - 1, whose buffer the next copy
+  // reuses.
   auto sync = [&]() {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(W8 ? 6 : 8));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -131,12 +159,14 @@ __device__ __forceinline__ void ring_gemm_256(const bf16_t* __restrict__ A, int 
 // the quarter's maximum) to sc.p[row][v] and (m, sum of p_v in fp32) to
 // sc.qpart[row][v / 64]: the unnormalised predicted distribution that
 // sc_norm_kernel normalises.
-template <bool GUMBEL, bool SC>
+// With W8 the embedding is read as FP8 codes (lm8_index layout) with row
+// scales instead (the tied LM head's weights at reduced precision).
+template <bool GUMBEL, bool SC, bool W8>
 __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ A, int rows, int K,
                                                      const bf16_t* __restrict__ E, int V,
                                                      const int32_t* __restrict__ held, float k2,
                                                      float4* __restrict__ part, float* __restrict__ held_logit,
-                                                     int held_stride, GumbelDraw gd, SelfCondOut sc) {
+                                                     int held_stride, GumbelDraw gd, SelfCondOut sc, LmFp8 e8) {
   // four distinct objects: the compiler then orders each buffer's LDS reads
   // only after the copies into that buffer
   __shared__ __align__(16) u32x4 r0[LM_FRAGS][64];
@@ -153,7 +183,8 @@ __global__ __launch_bounds__(512) void lmhead_kernel(const bf16_t* __restrict__ 
   const int c0 = nt * LM_COLS;
 
   f32x4 acc[4][8];  // [column block][row block] of the wave
-  ring_gemm_256(A, K, row0, nrows, E + (int64_t)c0 * K, K / LM_BK, 0, acc, r0, r1, r2, r3);
+  ring_gemm_256<W8>(A, K, row0, nrows, E + (int64_t)c0 * K, W8 ? e8.codes + (int64_t)c0 * 32 : nullptr,
+                    W8 ? e8.scale + c0 : nullptr, V, K / LM_BK, 0, acc, r0, r1, r2, r3);
 
   // Epilogue in the ring's memory: red[4][256] (max, sum, argmax, entropy
   // sum) per column quarter and row, and the rows' held tokens.
@@ -312,7 +343,8 @@ __global__ __launch_bounds__(512) void sc_gemm_kernel(const bf16_t* __restrict__
   for (int row0 = 0; row0 < rows; row0 += LM_ROWS) {
     const int nrows = min(LM_ROWS, rows - row0);
     f32x4 acc[4][8];
-    ring_gemm_256(P, V, row0, nrows, ET + (int64_t)c0 * V, nst, split * nst, acc, r0, r1, r2, r3);
+    ring_gemm_256<false>(P, V, row0, nrows, ET + (int64_t)c0 * V, nullptr, nullptr, 0, nst, split * nst, acc, r0, r1,
+                         r2, r3);
     float* out = part + (int64_t)split * rows * d;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -348,22 +380,30 @@ int lmhead_parts(int V) { return V / LM_COLS; }
 
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
                    const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
-                   const GumbelDraw* gumbel, const SelfCondOut* sc) {
+                   const GumbelDraw* gumbel, const SelfCondOut* sc, const LmFp8* fp8) {
   const float k2 = 1.4426950408889634f / tau;
   const int NT = V / LM_COLS;
   const dim3 grid(NT * div_up(rows, LM_ROWS));
   const GumbelDraw gd = gumbel ? *gumbel : GumbelDraw{};
   const SelfCondOut so = sc ? *sc : SelfCondOut{};
-#define DG_LMHEAD(G_, S_)                                                                                          \
-  hipLaunchKernelGGL((lmhead_kernel<G_, S_>), grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part, held_logit, \
-                     held_stride, gd, so)
-  if (gumbel && sc)
-    DG_LMHEAD(true, true);
-  else if (gumbel)
-    DG_LMHEAD(true, false);
-  else if (sc)
-    DG_LMHEAD(false, true);
-  else
-    DG_LMHEAD(false, false);
+  const LmFp8 e8 = fp8 ? *fp8 : LmFp8{};
+#define DG_LMHEAD(G_, S_, W_)                                                                                  \
+  hipLaunchKernelGGL((lmhead_kernel<G_, S_, W_>), grid, dim3(512), 0, s, a, rows, K, embed, V, held, k2, part, \
+                     held_logit, held_stride, gd, so, e8)
+#define DG_LMHEAD_W(G_, S_)   \
+  if (fp8)                    \
+    DG_LMHEAD(G_, S_, true);  \
+  else                        \
+    DG_LMHEAD(G_, S_, false)
+  if (gumbel && sc) {
+    DG_LMHEAD_W(true, true);
+  } else if (gumbel) {
+    DG_LMHEAD_W(true, false);
+  } else if (sc) {
+    DG_LMHEAD_W(false, true);
+  } else {
+    DG_LMHEAD_W(false, false);
+  }
+#undef DG_LMHEAD_W
 #undef DG_LMHEAD
 }

@@ -128,7 +128,8 @@ __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* 
 
 // Token -> expert permutation and the expert kernel's work list, by one
 // work-group of any size that is a multiple of 256 threads (at least 4
-// waves); nb = ceil(rows / 64) token blocks (nb <= 64):
+// waves); nb = ceil(rows / 64) token blocks. When the (expert, block) tables
+// of all rows fit the LDS budget (permute_max_blocks), in one pass:
 //  1. mask[e][b] = bit set of the tokens of block b that chose expert e
 //     (64-bit LDS atomic OR per (token, choice) pair);
 //  2. one thread per expert: popcounts of its masks, running sum over the
@@ -139,6 +140,10 @@ __device__ __forceinline__ void wave_exclusive_scan(const int32_t* in, int32_t* 
 //  4. every pair (t, j) with expert e = idx[t][j] takes slot
 //     base[e][t/64] + popcount(mask[e][t/64] below t): tokens ascending
 //     inside an expert, three stores per pair (slot[t][j] coalesced).
+// Otherwise (large batches) the counts come from LDS atomics over all pairs
+// first, and steps 1, 2 and 4 run over consecutive chunks of
+// permute_max_blocks token blocks, each chunk's bases starting after the
+// tokens of the same expert in earlier chunks.
 // With `coherent`, idx is read at agent scope (it was written in the same
 // launch, possibly on another XCD). lds: permute_lds_bytes(rows, E, k).
 struct PermuteArgs {
@@ -147,12 +152,19 @@ struct PermuteArgs {
   int32_t *cnt, *off, *perm, *slot, *widx, *items;
 };
 
+// LDS budget of the (expert, token block) tables: 8-byte mask + 4-byte base.
+constexpr int PERMUTE_LDS_BUDGET = 57344;
+__host__ __device__ __forceinline__ int permute_max_blocks(int E) { return PERMUTE_LDS_BUDGET / (12 * E); }
+
 __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, bool coherent) {
   const int rows = a.rows, E = a.E, k = a.k;
-  const int nb = (rows + 63) / 64;
+  const int nb_all = (rows + 63) / 64;
+  const bool chunked = nb_all > permute_max_blocks(E);
+  const int nb = chunked ? permute_max_blocks(E) : nb_all;  // blocks held in the tables at a time
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(lds);  // [E][nb]
   int32_t* base = reinterpret_cast<int32_t*>(mask + (size_t)E * nb);     // [E][nb]
   __shared__ int32_t s_cnt[257];
+  __shared__ int32_t s_run[257];
   __shared__ int32_t s_off[258];
   __shared__ int32_t s_ngu[MOE_MAX_GROUPS], s_ndn[MOE_MAX_GROUPS], s_nch[MOE_MAX_GROUPS];
   __shared__ int32_t s_igu[MOE_MAX_GROUPS + 1], s_idn[MOE_MAX_GROUPS + 1], s_ich[MOE_MAX_GROUPS + 1];
@@ -167,29 +179,46 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
   // expert ids are loaded PB per thread at a time, all issued before any use;
   // when one batch covers every pair, they stay in registers for step 4
   constexpr int PB = 8;
-  const bool one_batch = pairs <= PB * nt;
+  const bool one_batch = !chunked && pairs <= PB * nt;
   int evc[PB];
-  for (int i = tid; i < E * nb; i += nt) mask[i] = 0ull;
-  __syncthreads();
-  for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
-    int ev[PB];
+  if (!chunked) {
+    for (int i = tid; i < E * nb; i += nt) mask[i] = 0ull;
+    __syncthreads();
+    for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
+      int ev[PB];
 #pragma unroll
-    for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+      for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
 #pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      evc[j] = ev[j];
-      const int i = i0 + j * nt, t = i / k;
-      if (i < pairs) atomicOr(&mask[ev[j] * nb + (t >> 6)], 1ull << (t & 63));
+      for (int j = 0; j < PB; ++j) {
+        evc[j] = ev[j];
+        const int i = i0 + j * nt, t = i / k;
+        if (i < pairs) atomicOr(&mask[ev[j] * nb + (t >> 6)], 1ull << (t & 63));
+      }
     }
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += nt) {  // one thread per expert, over its nb masks
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      base[e * nb + b] = run;  // tokens of e in earlier blocks
-      run += __popcll(mask[e * nb + b]);
+    __syncthreads();
+    for (int e = tid; e < E; e += nt) {  // one thread per expert, over its nb masks
+      int run = 0;
+      for (int b = 0; b < nb; ++b) {
+        base[e * nb + b] = run;  // tokens of e in earlier blocks
+        run += __popcll(mask[e * nb + b]);
+      }
+      s_cnt[e] = run;
     }
-    s_cnt[e] = run;
+  } else {
+    // counts over all pairs (the order of the atomics does not matter)
+    for (int e = tid; e < E; e += nt) {
+      s_cnt[e] = 0;
+      s_run[e] = 0;
+    }
+    __syncthreads();
+    for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
+      int ev[PB];
+#pragma unroll
+      for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+        if (i0 + j * nt < pairs) atomicAdd(&s_cnt[ev[j]], 1);
+    }
   }
   __syncthreads();
   // groups: 0 = shared expert (all rows), 1 + e = routed expert e
@@ -206,7 +235,8 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
   if (wave == 2) wave_exclusive_scan(s_ndn, s_idn, E + 1, lane);
   if (wave == 3) wave_exclusive_scan(s_nch, s_ich, E + 1, lane);
   __syncthreads();
-  for (int i = tid; i < E * nb; i += nt) base[i] += s_off[i / nb];
+  if (!chunked)
+    for (int i = tid; i < E * nb; i += nt) base[i] += s_off[i / nb];
   for (int e = tid; e < E; e += nt) {
     a.cnt[e] = s_cnt[e];
     a.off[e] = s_off[e];
@@ -230,6 +260,53 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
   }
   for (int c = tid; c < s_ich[E + 1]; c += nt) a.items[MOE_DONE + c] = 0;
   __syncthreads();  // base is final
+  if (chunked) {
+    // chunks of nb token blocks in order; s_run[e] = tokens of e in earlier chunks
+    for (int c0 = 0; c0 < rows; c0 += 64 * nb) {
+      const int cr = min(64 * nb, rows - c0), cnb = (cr + 63) / 64;
+      for (int i = tid; i < E * cnb; i += nt) mask[i] = 0ull;
+      __syncthreads();
+      const int p0 = c0 * k, p1 = (c0 + cr) * k;
+      for (int i0 = p0 + tid; i0 < p1; i0 += PB * nt) {
+        int ev[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) ev[j] = i0 + j * nt < p1 ? load_idx(i0 + j * nt) : 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const int i = i0 + j * nt, t = i / k - c0;
+          if (i < p1) atomicOr(&mask[ev[j] * cnb + (t >> 6)], 1ull << (t & 63));
+        }
+      }
+      __syncthreads();
+      for (int e = tid; e < E; e += nt) {
+        int run = s_off[e] + s_run[e];
+        for (int b = 0; b < cnb; ++b) {
+          base[e * cnb + b] = run;
+          run += __popcll(mask[e * cnb + b]);
+        }
+        s_run[e] = run - s_off[e];
+      }
+      __syncthreads();
+      for (int i0 = p0 + tid; i0 < p1; i0 += PB * nt) {
+        int ev[PB];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) ev[j] = i0 + j * nt < p1 ? load_idx(i0 + j * nt) : 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+          const int i = i0 + j * nt;
+          if (i >= p1) break;
+          const int t = i / k, e = ev[j], tl = t - c0, b = tl >> 6, l = tl & 63;
+          const unsigned long long below = l == 0 ? 0ull : (mask[e * cnb + b] << (64 - l));
+          const int pos = base[e * cnb + b] + __popcll(below);
+          a.slot[i] = pos;
+          a.perm[pos] = t;
+          a.widx[pos] = i;
+        }
+      }
+      __syncthreads();  // the tables are reused by the next chunk
+    }
+    return;
+  }
   for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
     int ev[PB];
 #pragma unroll
@@ -488,8 +565,8 @@ void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, c
 }
 
 // Dynamic LDS of the permutation kernel: mask (8 B) and base (4 B) per
-// (expert, 64-token block).
+// (expert, 64-token block), for at most permute_max_blocks(E) blocks at a time.
 size_t permute_lds_bytes(int rows, int E, int k) {
   (void)k;
-  return (size_t)E * ((rows + 63) / 64) * 12;
+  return (size_t)E * std::min((rows + 63) / 64, permute_max_blocks(E)) * 12;
 }

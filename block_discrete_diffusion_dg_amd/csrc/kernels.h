@@ -23,7 +23,9 @@ void launch_init_canvas(hipStream_t s, int n_req, int C, int V, int32_t* canvas,
                         const uint64_t* seeds_host, const int32_t* blocks_host,
                         const int32_t* slots_host);
 void launch_pack(hipStream_t s, const bf16_t* src, bf16_t* dst, int64_t n, int k);
-void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k);
+// FP8 codes in the expert layout (pack8_index) or, with lmhead, the LM head's
+// step-major layout (lm8_index).
+void launch_quant_fp8(hipStream_t s, const bf16_t* src, uint8_t* dst, float* scale, int64_t n, int k, bool lmhead);
 
 // k_dense.hip (weight-streaming dense projections)
 // launch_qkv also zeroes the n_sync arrival counters of the layer's router
@@ -51,9 +53,15 @@ struct SelfCondOut {
   bf16_t* p;
   float2* qpart;
 };
+// FP8 LM-head weights: codes in the lm8_index layout and per-row scales
+// (embed8 == nullptr: the bf16 fragment-major embed).
+struct LmFp8 {
+  const uint8_t* codes;
+  const float* scale;
+};
 void launch_lmhead(hipStream_t s, const bf16_t* a, int rows, int K, const bf16_t* embed, int V,
                    const int32_t* held, float tau, float4* part, float* held_logit, int held_stride,
-                   const GumbelDraw* gumbel, const SelfCondOut* sc);
+                   const GumbelDraw* gumbel, const SelfCondOut* sc, const LmFp8* fp8);
 int lmhead_parts(int V);
 // Self-conditioning: part[split][rows][d] = P[:, split range] ET[:, split range]^T
 // (P bf16 [rows][V] normalised, ET fragment-major [d][V]); sc_gemm_splits(V) splits.

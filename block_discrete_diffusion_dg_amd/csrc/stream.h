@@ -65,6 +65,15 @@ __host__ __device__ __forceinline__ int64_t pack8_index(int64_t n, int64_t k, in
   return (n >> 4) * 16 * K + (k >> 6) * 1024 + (((kk & 31) >> 3) * 16 + (n & 15)) * 16 + (kk >> 5) * 8 + (kk & 7);
 }
 
+// Byte index of W[n][k] in the step-major FP8 layout of the LM head, for an
+// [N][K] matrix (N % 16 == 0, K % 32 == 0): each 32-wide K-step holds all N
+// rows (N*32 bytes), every 16-row block of it as 512 bytes ordered [lane][8]
+// with lane = 16*((k%32)/8) + n%16 and byte k%8. The 16 blocks one LM-head
+// tile streams per step are then 8 KB of consecutive bytes.
+__host__ __device__ __forceinline__ int64_t lm8_index(int64_t n, int64_t k, int64_t N) {
+  return (k >> 5) * N * 32 + (n >> 4) * 512 + ((((k & 31) >> 3) * 16 + (n & 15)) * 8) + (k & 7);
+}
+
 // Eight E4M3 codes (two words) -> eight bf16 values times scale s.
 __device__ __forceinline__ u32x4 widen_fp8(uint32_t w0, uint32_t w1, float s) {
   const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);

@@ -38,19 +38,21 @@ def pack_weight(t: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def quantize_fp8(t: torch.Tensor):
-    """FP8 (E4M3) codes of a row-major bf16 matrix or expert bank
-    (fragment-major, uint8, same element count) and its fp32 row scales,
-    made on the GPU by dg_quantize_fp8."""
+def quantize_fp8(t: torch.Tensor, lmhead: bool = False):
+    """FP8 (E4M3) codes of a row-major bf16 matrix or expert bank (uint8,
+    same element count; the experts' fragment-major layout, or with lmhead
+    the LM head's step-major layout) and its fp32 row scales, made on the GPU
+    by dg_quantize_fp8 / dg_quantize_fp8_lmhead."""
     assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous()
     k = t.shape[-1]
     n = t.numel() // k
     lib = B.load()
     codes = torch.empty(t.numel(), dtype=torch.uint8, device=t.device)
     scale = torch.empty(n, dtype=torch.float32, device=t.device)
-    st = lib.dg_quantize_fp8(_stream(), t.data_ptr(), codes.data_ptr(), scale.data_ptr(), n, k)
+    fn = lib.dg_quantize_fp8_lmhead if lmhead else lib.dg_quantize_fp8
+    st = fn(_stream(), t.data_ptr(), codes.data_ptr(), scale.data_ptr(), n, k)
     if st != B.DG_OK:
-        raise B.DGError(st, f"dg_quantize_fp8 failed for shape {tuple(t.shape)}")
+        raise B.DGError(st, f"FP8 quantisation failed for shape {tuple(t.shape)}")
     return codes, scale
 
 
@@ -86,9 +88,11 @@ class Engine:
     def __init__(self, cfg: ModelConfig, layers: Sequence[Dict[str, torch.Tensor]],
                  embed: torch.Tensor, final_norm: torch.Tensor, max_ctx: int,
                  max_requests: int = 1, max_rows: Optional[int] = None,
-                 expert_format: str = "bf16", selfcond: Optional[Dict[str, torch.Tensor]] = None):
+                 expert_format: str = "bf16", selfcond: Optional[Dict[str, torch.Tensor]] = None,
+                 lmhead_format: str = "bf16"):
         """selfcond: the self-conditioning feed-forward layer (sc_gate, sc_up
-        [F][d], sc_down [d][F], bf16, row-major), or None for none."""
+        [F][d], sc_down [d][F], bf16, row-major), or None for none.
+        lmhead_format "fp8": the LM head reads an FP8 copy of the embedding."""
         self.lib = B.load()
         self.cfg = cfg
         dev = embed.device
@@ -104,6 +108,8 @@ class Engine:
         c.tau_first, c.tau_last = cfg.tau_first, cfg.tau_last
         c.expert_format = B.WEIGHT_FORMAT[expert_format]
         c.d_selfcond = 0 if selfcond is None else selfcond["sc_gate"].shape[0]
+        c.lmhead_format = B.WEIGHT_FORMAT[lmhead_format]
+        self.lmhead_format = lmhead_format
         self.expert_format = expert_format
         self.c_cfg = c
         sc_ptrs = [None] * 4
@@ -114,6 +120,11 @@ class Engine:
             packed = [pack_weight(selfcond[n].contiguous()) for n in ("sc_gate", "sc_up", "sc_down")]
             self._keep += packed + [embed_t]
             sc_ptrs = [t.data_ptr() for t in packed] + [embed_t.data_ptr()]
+        lm8_ptrs = [None, None]
+        if lmhead_format == "fp8":
+            codes, scale = quantize_fp8(embed, lmhead=True)
+            self._keep += [codes, scale]
+            lm8_ptrs = [codes.data_ptr(), scale.data_ptr()]
         embed = pack_weight(embed)  # the tied LM head streams it fragment-major
         self._keep += [embed, final_norm]
         arr = (B.DGLayerWeights * max(1, len(layers)))()
@@ -130,7 +141,7 @@ class Engine:
                 self._keep.append(t)
                 setattr(arr[i], name, t.data_ptr())
         self._layer_arr = arr
-        w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr, *sc_ptrs)
+        w = B.DGWeights(embed.data_ptr(), final_norm.data_ptr(), arr, *sc_ptrs, *lm8_ptrs)
         kv_bytes = self.lib.dg_kv_cache_bytes(ctypes.byref(c))
         ws_bytes = self.lib.dg_workspace_bytes(ctypes.byref(c))
         if ws_bytes == 0:

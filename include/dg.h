@@ -59,8 +59,7 @@ typedef enum {
  * (n_kv_heads*head_dim) multiples of 128; n_experts <= 128 and a multiple
  * of 8; top_k <= 8; d_expert and d_shared multiples of 64; vocab a multiple
  * of 256; canvas a multiple of 16, at most 1024; canvas <= max_rows <=
- * 16*canvas and 12 * n_experts * ceil(max_rows/64) <= 57344 (routing tables
- * held in LDS: max_rows <= 2368 for 128 experts).
+ * 32*canvas (up to 32 requests of one block each per call).
  * tau_first / tau_last: temperature at the first / last step, falling
  * linearly (explainer §3.3: 0.8 -> 0.4). */
 typedef struct dg_config {
@@ -74,6 +73,8 @@ typedef struct dg_config {
   int32_t expert_format; /* dg_weight_format of the expert matrices (0 = bf16) */
   int32_t d_selfcond;    /* width of the self-conditioning feed-forward layer
                             (a multiple of 64); 0 = no self-conditioning */
+  int32_t lmhead_format; /* dg_weight_format of the LM head's copy of the
+                            embedding (0 = bf16: the embedding itself) */
 } dg_config;
 
 /* Storage of the routed and shared expert matrices (w_gate, w_up, w_down,
@@ -121,6 +122,12 @@ typedef struct dg_weights {
   const void *embed, *final_norm;
   const dg_layer_weights *layers;
   const void *sc_gate, *sc_up, *sc_down, *embed_t;
+  /* lmhead_format == DG_WEIGHTS_FP8 only (else NULL): the LM head reads
+   * E4M3 codes of the embedding with one power-of-two scale per vocabulary
+   * row, as made by dg_quantize_fp8_lmhead (embed_fp8 [V*d] bytes,
+   * embed_scale [V] fp32); the input embedding stays the bf16 embed. */
+  const void *embed_fp8;
+  const float *embed_scale;
 } dg_weights;
 
 /* Per-position statistics of a denoising step (optional output). */
@@ -223,6 +230,18 @@ dg_status dg_pack_weight(void *stream, const void *d_src, void *d_dst, int64_t n
 dg_status dg_quantize_fp8(void *stream, const void *d_src, void *d_dst, float *d_scale, int64_t n,
                           int32_t k);
 
+/* FP8 copy of a row-major bf16 matrix W [n][k] for the LM head
+ * (lmhead_format = DG_WEIGHTS_FP8; the explainer's step timings, §5.2, are
+ * at FP8 precision): the same codes and row scales as dg_quantize_fp8, in
+ * the LM head's step-major layout: byte (k/32)*n*32 + (row/16)*512 +
+ * (16*((k%32)/8) + row%16)*8 + k%8, so that every 32-wide K-step of 256
+ * consecutive rows is 8 KB of consecutive bytes. Needs n % 16 == 0,
+ * k % 64 == 0, finite weights and non-overlapping buffers, else DG_EINVAL
+ * with nothing launched. Asynchronous on stream; the caller owns all three
+ * buffers. */
+dg_status dg_quantize_fp8_lmhead(void *stream, const void *d_src, void *d_dst, float *d_scale, int64_t n,
+                                 int32_t k);
+
 /* Bytes of KV cache for ONE request slot:
  * n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2.
  * Layout of the whole cache: [req][layer][K|V][kv_head] planes of
@@ -298,7 +317,7 @@ dg_status dg_commit_block(dg_ctx *ctx, void *stream, int32_t n_req, const int32_
  * d_tokens[r] (device int32 [n_req]) at position len of slot req[r] appends
  * that token's K/V rows (len += 1), and the LM head over its row gives
  * d_next[r] (device int32 [n_req]) = the greedy argmax, lowest id on ties.
- * Needs 1 <= n_req <= min(16, max_rows), distinct slots and len + 1 <=
+ * Needs 1 <= n_req <= min(32, max_rows), distinct slots and len + 1 <=
  * max_ctx (else DG_EINVAL / DG_ECAPACITY, nothing launched). The workspace's
  * first n_req LM-head statistics rows are overwritten. */
 dg_status dg_ar_step(dg_ctx *ctx, void *stream, int32_t n_req, const int32_t *req, const int32_t *d_tokens,

@@ -84,13 +84,14 @@ def make_selfcond(cfg, width, seed=0):
 
 
 def make_engine(cfg, max_ctx, max_requests=1, max_rows=None, gain_jitter=0.1, seed=0, expert_format="bf16",
-                selfcond=None):
+                selfcond=None, lmhead_format="bf16"):
     say(f"[engine] {cfg.name} L={cfg.n_layers} d={cfg.d_model} V={cfg.vocab} max_ctx={max_ctx} "
-        f"experts={expert_format} selfcond={None if selfcond is None else selfcond['sc_gate'].shape[0]}")
+        f"experts={expert_format} selfcond={None if selfcond is None else selfcond['sc_gate'].shape[0]} "
+        f"lmhead={lmhead_format}")
     layers, embed, final = gpu_weights(cfg, seed, gain_jitter)
     torch.cuda.synchronize()
     eng = Engine(cfg, layers, embed, final, max_ctx, max_requests, max_rows, expert_format=expert_format,
-                 selfcond=selfcond)
+                 selfcond=selfcond, lmhead_format=lmhead_format)
     return eng, HostWeights(layers, embed, final, expert_format)
 
 

@@ -232,3 +232,4 @@ def test_fp8_experts_need_their_scales(lib):
         setattr(layers[0], n, 0x2000)
     assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws, ctypes.byref(h)) == B.DG_OK
     lib.dg_destroy(h)
+

@@ -23,9 +23,10 @@ from tests.gpu_util import (REL_TOL, HostWeights, make_engine, make_selfcond, ma
 pytestmark = pytest.mark.gpu
 
 
-def _zero_layer_engine(cfg, max_rows, max_requests=1):
+def _zero_layer_engine(cfg, max_rows, max_requests=1, lmhead_format="bf16"):
     cfg0 = dataclasses.replace(cfg, n_layers=0)
-    return make_engine(cfg0, max_ctx=4 * cfg.canvas, max_requests=max_requests, max_rows=max_rows)
+    return make_engine(cfg0, max_ctx=4 * cfg.canvas, max_requests=max_requests, max_rows=max_rows,
+                       lmhead_format=lmhead_format)
 
 
 # ------------------------------------------------------------------------ generator
@@ -77,8 +78,11 @@ def _router_logits(rows, E, seed):
     return z
 
 
+# 5003 and 8192 rows exceed the permutation's LDS tables (2368 rows of 128
+# experts) and take its chunked form; 8192 rows is 32 requests of one block.
 @pytest.mark.parametrize("model,rows", [(synth.TINY, 32), (synth.TINY, 37), (synth.FULL, 256),
-                                        (synth.FULL, 2048), (synth.FULL, 5)])
+                                        (synth.FULL, 2048), (synth.FULL, 5), (synth.FULL, 5003),
+                                        (synth.FULL, 8192)])
 def test_route_bit_exact(model, rows):
     say(f"[route] E={model.n_experts} k={model.top_k} rows={rows}")
     eng, _ = _zero_layer_engine(model, max_rows=max(rows, model.canvas))
@@ -144,6 +148,37 @@ def test_quantize_fp8_bit_exact(which):
     assert np.array_equal(codes, want_codes)
 
 
+def _unpack_lm8(codes, n, k):
+    """Row-major [n][k] view of the LM head's step-major FP8 bytes (the
+    layout dg.h documents for dg_quantize_fp8_lmhead)."""
+    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    idx = (kk >> 5) * n * 32 + (nn >> 4) * 512 + (((kk & 31) >> 3) * 16 + (nn & 15)) * 8 + (kk & 7)
+    return codes[idx]
+
+
+@pytest.mark.parametrize("which", ["tiny_embed", "edges"])
+def test_quantize_fp8_lmhead_bit_exact(which):
+    from block_discrete_diffusion_dg_amd.engine import quantize_fp8
+    from oracle import fp8
+    say(f"[fp8 lm] quantize {which}")
+    if which == "tiny_embed":
+        w = synth.make_embedding(synth.TINY, 0)
+    else:
+        rng = np.random.default_rng(5)
+        w = rng.standard_normal((48, 192)).astype(np.float32) * 0.02
+        w[0] = 0.0
+        w[1, 3] = 448.0
+        w[2, 70] = -449.0
+        w[3] = rng.standard_normal(192) * 1e-6
+        w = torch.from_numpy(w).to(torch.bfloat16)
+    n, k = w.shape
+    codes, scale = quantize_fp8(w.contiguous().cuda(), lmhead=True)
+    torch.cuda.synchronize()
+    want_codes, want_e = fp8.quantize_rows(om.f64(w))
+    assert np.array_equal(scale.cpu().double().numpy(), np.exp2(want_e.astype(np.float64)))
+    assert np.array_equal(_unpack_lm8(codes.cpu().numpy(), n, k), want_codes)
+
+
 # ------------------------------------------------------------------------ LM head + sampler
 
 def _head_case(model, n_req, step, n_steps, seed=3):
@@ -155,12 +190,22 @@ def _head_case(model, n_req, step, n_steps, seed=3):
     return h, canvas, committed
 
 
-@pytest.mark.parametrize("model,n_req", [(synth.TINY, 1), (synth.TINY, 3), (synth.FULL, 1)])
-def test_head_statistics_and_sampler(model, n_req):
-    say(f"[head] V={model.vocab} d={model.d_model} n_req={n_req}")
+# The FP8 case at full width uses 16,384 vocabulary rows: the tile is the
+# full model's (K = 2048), and the oracle's dequantisation of all 262,144
+# rows would take minutes.
+@pytest.mark.parametrize("model,n_req,lm", [(synth.TINY, 1, "bf16"), (synth.TINY, 3, "bf16"), (synth.FULL, 1, "bf16"),
+                                           (synth.TINY, 2, "fp8"),
+                                           (dataclasses.replace(synth.FULL, vocab=16384), 1, "fp8")])
+def test_head_statistics_and_sampler(model, n_req, lm):
+    """With lm "fp8" the LM head reads E4M3 codes of the embedding; the oracle
+    multiplies with its own dequantisation of the same bf16 embedding."""
+    say(f"[head] V={model.vocab} d={model.d_model} n_req={n_req} lmhead={lm}")
     C = model.canvas
     rows = n_req * C
-    eng, hw = _zero_layer_engine(model, max_rows=rows, max_requests=n_req)
+    eng, hw = _zero_layer_engine(model, max_rows=rows, max_requests=n_req, lmhead_format=lm)
+    if lm == "fp8":
+        from oracle import fp8
+        hw = HostWeights([], torch.from_numpy(fp8.dequantize_bank(om.f64(hw.embed))), hw.final_norm)
     step, n_steps = 5, 16
     h, canvas, committed = _head_case(model, n_req, step, n_steps)
     reqs = list(range(n_req))
@@ -477,7 +522,8 @@ def _cache_rows(eng, slot, layer, lo, hi):
 # shapes, plus the full-width layer with a 32,768-token prefix (the
 # long-context workload's attention) and with 2,048 rows in one call (the
 # batch workload's tokens per step: ~128 rows per expert, several 128-row
-# chunks for hot experts), and a small layer whose projection widths (K = 768
+# chunks for hot experts) and with 4,096 rows (16 requests' worth: the fused
+# router's permutation then runs in chunks), and a small layer whose projection widths (K = 768
 # and 384) are not a power-of-two multiple of 256, so the dense projections
 # take their streaming-tile form instead of the split-K form.
 @pytest.mark.parametrize("name,causal,P,C,over,fmt", [
@@ -486,6 +532,7 @@ def _cache_rows(eng, slot, layer, lo, hi):
     ("one_layer", True, None, None, None, "bf16"),
     ("one_layer", False, 32768, None, None, "bf16"),
     ("one_layer", False, None, 2048, None, "bf16"),
+    ("one_layer", False, None, 4096, None, "bf16"),
     ("tiny", False, None, None, {"d_model": 768, "n_q_heads": 6}, "bf16"),
     ("tiny", False, None, None, None, "fp8"),
     ("one_layer", False, None, None, None, "fp8"),

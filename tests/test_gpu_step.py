@@ -13,7 +13,7 @@ from block_discrete_diffusion_dg_amd import synth
 from block_discrete_diffusion_dg_amd.engine import stats_fields
 from oracle import model as om
 from oracle import philox as philox_mod
-from tests.gpu_util import (REL_TOL, make_engine, max_rel, moe_with_experts, router_band, router_swaps, say,
+from tests.gpu_util import (REL_TOL, make_engine, make_selfcond, max_rel, moe_with_experts, router_band, router_swaps, say,
                             tie_gap_ok)
 
 pytestmark = pytest.mark.gpu
