@@ -104,6 +104,7 @@ SIGNATURES = {
     "dg_set_cache_len": (c_i32, [c_vp, c_i32, c_i32]),
     "dg_last_error": (ctypes.c_char_p, [c_vp]),
     "dg_sync": (c_i32, [c_vp, c_vp]),
+    "dg_route_noalloc": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "dg_workspace_layout": (c_i32, [ctypes.POINTER(DGConfig), ctypes.POINTER(DGWsLayout)]),
     "dg_test_layer": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_i32]),
     "dg_test_route": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
@@ -120,6 +121,7 @@ SIGNATURES = {
 ITEMS_SPIN_TIMEOUTS = 409
 ITEMS_TOUCHED_TOTAL = 410
 ITEMS_PERMUTE_CALLS = 412
+ROUTE_NOALLOC_MAX_ROWS = 2368  # DG_ROUTE_NOALLOC_MAX_ROWS (include/dg.h)
 
 STAGES = ("embed", "norm", "qkv", "attn", "oproj", "router", "topk", "permute", "experts",
           "combine", "lmhead", "merge", "sampler", "selfcond")

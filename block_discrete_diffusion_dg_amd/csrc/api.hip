@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -859,3 +860,58 @@ dg_status dg_timing_read(dg_ctx* c, double* ms, int32_t* launches, int32_t n_sta
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- routing without allocation
+
+// Scratch of dg_route_noalloc: the permutation kernel's work-list words and
+// its slot -> (token, choice) index, sized for DG_ROUTE_NOALLOC_MAX_ROWS rows
+// of 128 experts top-8. One copy per GPU, shared by every call on that GPU.
+constexpr size_t ROUTE_ITEMS_WORDS = (size_t)MOE_DONE + 1024;
+constexpr size_t ROUTE_SCRATCH_BYTES = ROUTE_ITEMS_WORDS * 4 + (size_t)DG_ROUTE_NOALLOC_MAX_ROWS * 8 * 4;
+static __device__ __align__(256) unsigned char scratch[ROUTE_SCRATCH_BYTES];
+
+namespace {
+// Device address of `scratch` on each GPU, taken once per device with that
+// device current (the host-side name is not a device address).
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;
+
+void* scratch_on_current_device(hipError_t& err) {
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" dg_status dg_route_noalloc(void* stream, const float* d_z, int32_t rows, int32_t n_experts, int32_t top_k,
+                                      int32_t* d_idx, float* d_w, int32_t* d_cnt, int32_t* d_off, int32_t* d_perm,
+                                      int32_t* d_slot) {
+  if (!d_z || !d_idx || !d_w || !d_cnt || !d_off || !d_perm || !d_slot || rows <= 0 || n_experts <= 0 ||
+      n_experts > 128 || n_experts % 8 || top_k <= 0 || top_k > 8 || top_k > n_experts)
+    return DG_EINVAL;
+  if (rows > DG_ROUTE_NOALLOC_MAX_ROWS || permute_lds_bytes(rows, n_experts, top_k) > 57344 ||
+      (size_t)MOE_DONE + moe_chunk_bound(rows, n_experts, top_k) > ROUTE_ITEMS_WORDS)
+    return DG_ECAPACITY;
+  hipError_t err = hipSuccess;
+  char* base = static_cast<char*>(scratch_on_current_device(err));
+  if (!base) return DG_EHIP;
+  int32_t* items = reinterpret_cast<int32_t*>(base);
+  int32_t* widx = reinterpret_cast<int32_t*>(base + ROUTE_ITEMS_WORDS * 4);
+  hipStream_t s = (hipStream_t)stream;
+  launch_topk(s, d_z, rows, n_experts, top_k, d_idx, d_w);
+  // the expert work list the permutation also writes is scratch here: one
+  // 64-column gate/up tile, one shared tile and one down tile per chunk
+  const RouterPermute rp{moe_rows_per_chunk(rows, n_experts, top_k), 1, 1, 1, d_cnt, d_off, d_perm, d_slot, widx,
+                         items};
+  launch_permute(s, d_idx, rows, n_experts, top_k, rp);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_EHIP;
+}

@@ -346,6 +346,37 @@ dg_status dg_sync(dg_ctx *ctx, void *stream);
 /* Last error message of the context ("" if none). */
 const char *dg_last_error(const dg_ctx *ctx);
 
+/* MoE routing without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses
+ * that forbid allocation). The same kernels as the router and permutation of
+ * a denoising step (explainer §2.1: 8 of 128 experts per token), run on
+ * given router logits, with no context and no workspace:
+ *   d_z     device fp32 [rows][n_experts] router logits (read);
+ *   d_idx   device int32 [rows][top_k]: the top_k experts of each row in
+ *           descending logit, ties to the lower expert id;
+ *   d_w     device fp32 [rows][top_k]: softmax over the selected logits;
+ *   d_cnt   device int32 [n_experts]: rows per expert;
+ *   d_off   device int32 [n_experts + 1]: exclusive prefix sum of d_cnt;
+ *   d_perm  device int32 [rows * top_k]: token of each expert slot, grouped
+ *           by expert, tokens ascending inside an expert;
+ *   d_slot  device int32 [rows][top_k]: slot in d_perm of each choice.
+ * The caller owns and passes every input and output. The kernels' other
+ * buffers (the permutation's work-list words and slot index, about 80 KB)
+ * live in a static device array that the library holds on each GPU it runs
+ * on until the process ends; this call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine). Nothing in that array needs
+ * clearing between calls. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and give unspecified results. Needs 1 <= rows <=
+ * DG_ROUTE_NOALLOC_MAX_ROWS, n_experts a multiple of 8 at most 128 and
+ * 1 <= top_k <= min(8, n_experts), else DG_EINVAL (bad argument) or
+ * DG_ECAPACITY (more rows than the static array holds), with nothing
+ * launched. A launch failure returns DG_EHIP. Asynchronous on stream. */
+#define DG_ROUTE_NOALLOC_MAX_ROWS 2368
+dg_status dg_route_noalloc(void *stream, const float *d_z, int32_t rows, int32_t n_experts, int32_t top_k,
+                           int32_t *d_idx, float *d_w, int32_t *d_cnt, int32_t *d_off, int32_t *d_perm,
+                           int32_t *d_slot);
+
 #ifdef __cplusplus
 }
 #endif

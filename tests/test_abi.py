@@ -233,3 +233,13 @@ def test_fp8_experts_need_their_scales(lib):
     assert lib.dg_create(ctypes.byref(c), ctypes.byref(w), 0x1000, 0x1000, ws, ctypes.byref(h)) == B.DG_OK
     lib.dg_destroy(h)
 
+def test_route_noalloc_rejects_sizes_and_arguments_on_the_host(lib):
+    # every check runs before any HIP call: fake addresses are safe here
+    p = 0x100000
+    rows_max = B.ROUTE_NOALLOC_MAX_ROWS
+    assert lib.dg_route_noalloc(None, p, rows_max + 1, 128, 8, p, p, p, p, p, p) == B.DG_ECAPACITY
+    assert lib.dg_route_noalloc(None, p, 0, 128, 8, p, p, p, p, p, p) == B.DG_EINVAL
+    assert lib.dg_route_noalloc(None, p, 16, 129, 8, p, p, p, p, p, p) == B.DG_EINVAL
+    assert lib.dg_route_noalloc(None, p, 16, 124, 8, p, p, p, p, p, p) == B.DG_EINVAL  # not a multiple of 8
+    assert lib.dg_route_noalloc(None, p, 16, 8, 9, p, p, p, p, p, p) == B.DG_EINVAL
+    assert lib.dg_route_noalloc(None, p, 16, 128, 8, p, p, None, p, p, p) == B.DG_EINVAL
