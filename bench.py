@@ -137,6 +137,8 @@ def main():
                     help="override the workload's number of requests (batch-size sweep; 0 = the workload's)")
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the extra measurement with FP8 expert weights")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="measure the headline step only (no sampled-candidate, AR, FP8 or self-conditioning runs)")
     ap.add_argument("--no-selfcond-variant", action="store_true",
                     help="skip the extra measurement with self-conditioning")
     ap.add_argument("--graph-steps", type=int, default=50,
@@ -277,6 +279,9 @@ def main():
     lm_traffic = traffic_for("lmhead", f"lmhead_{wl.name}_traffic")
     if "lmhead" in kernels:
         kernels["lmhead"]["traffic"] = round(lm_traffic) if lm_traffic is not None else None
+    attn_traffic = traffic_for("attn", f"attn_{wl.name}_traffic")
+    if "attn" in kernels:
+        kernels["attn"]["traffic"] = round(attn_traffic) if attn_traffic is not None else None
     steps_per_s = 1e3 / ms
     out = {
         "metric": METRIC,
@@ -335,7 +340,7 @@ def main():
         # reaches on this GPU in the same run
         out["roofline"]["peak_measured"] = round(copy_gbs, 1)
         out["roofline"]["frac_measured"] = round(out["roofline"]["achieved"] / copy_gbs, 4)
-    if args.workload == "full" and not args.n_req:
+    if args.workload == "full" and not args.n_req and not args.no_variants:
         out["variants"] = {"sampled_candidates": sampled_variant(args, eng, reqs, seeds, blocks, x, m, S),
                            "ar_step": ar_variant(args, eng, reqs, P, ms)}
         if not args.no_fp8_variant:

@@ -3,6 +3,8 @@
   python -m block_discrete_diffusion_dg_amd.profiles stats <kernel_stats.csv> <out.md> --command "<cmd>"
   python -m block_discrete_diffusion_dg_amd.profiles traffic <fetch_csv> <write_csv> <out_stem>
       --kernel <name regex> --copy-bytes N --command-fetch "<cmd>" --command-write "<cmd>"
+  python -m block_discrete_diffusion_dg_amd.profiles mfma <counter_csv> <out.md> --command "<cmd>"
+      (counters MfmaUtil, MfmaFlopsBF16, GRBM_GUI_ACTIVE per dispatch)
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) into HBM
 bytes per launch of one kernel, scaled by what the same counter reads for a
@@ -27,7 +29,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "moe_experts": ["csrc/k_moe.hip", "csrc/stream.h", "csrc/common.h"],
     "lmhead": ["csrc/k_lmhead.hip", "csrc/common.h"],
+    "attn": ["csrc/k_attn.hip", "csrc/common.h"],
 }
+
+# Kernel classes of the matrix-core summary: (label, name pattern).
+MFMA_CLASSES = [("attention (attn_kernel)", r"attn_kernel"), ("LM head (lmhead_kernel)", r"lmhead_kernel"),
+                ("experts (moe_experts_kernel)", r"moe_experts_kernel"), ("QKV (qkv_sk_kernel)", r"qkv_sk_kernel"),
+                ("O-proj (resid_sk_kernel)", r"resid_sk_kernel"), ("router (router_kernel)", r"router_kernel")]
+GPU_CLOCK_HZ = 2.4e9  # MI355X peak engine clock, for cycles -> time
 
 
 def source_hash(kernel: str) -> str:
@@ -126,6 +135,40 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_stem: str, kernel: str
     return rec
 
 
+def summarize_mfma(csv_path: str, out_md: str, command: str) -> dict:
+    """Per kernel class: mean MfmaUtil (percent of SIMD cycles with the matrix
+    core busy while the dispatch ran), bf16 MFMA flops per dispatch, and the
+    GPU-active cycles per dispatch (time at the peak clock)."""
+    per = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        per[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    lines = ["# Matrix-core use per kernel (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             "MfmaUtil is rocprofv3's derived metric: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs over "
+             "GRBM_GUI_ACTIVE times the SIMD count, during each dispatch (counters serialise the dispatches). "
+             "MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. Rate = flops / (active cycles / 2.4 GHz); "
+             "the dense bf16 peak is 2.5 PFLOP/s.", "",
+             "| kernel | dispatches | MfmaUtil % | bf16 GFLOP per dispatch | active us per dispatch | TFLOP/s | of peak |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for label, pat in MFMA_CLASSES:
+        rx = re.compile(pat)
+        util = [v for k, vs in per["MfmaUtil"].items() if rx.search(k) for v in vs]
+        flops = [v for k, vs in per["MfmaFlopsBF16"].items() if rx.search(k) for v in vs]
+        act = [v for k, vs in per["GRBM_GUI_ACTIVE"].items() if rx.search(k) for v in vs]
+        if not util:
+            continue
+        u, f, a = sum(util) / len(util), sum(flops) / max(1, len(flops)), sum(act) / max(1, len(act))
+        t = a / GPU_CLOCK_HZ
+        rate = f / t / 1e12 if t > 0 else 0.0
+        out[label] = {"dispatches": len(util), "mfma_util_pct": u, "gflop": f / 1e9, "active_us": t * 1e6,
+                      "tflops": rate}
+        lines.append(f"| {label} | {len(util)} | {u:.1f} | {f / 1e9:.3f} | {t * 1e6:.1f} | {rate:.0f} | "
+                     f"{rate / 2500:.3f} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out
+
+
 def traffic_for(kernel: str, stem: str):
     """HBM bytes per launch recorded for `kernel`, or None when no record
     exists or the kernel's sources changed since it was taken."""
@@ -157,9 +200,15 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("out")
+    m.add_argument("--command", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
         summarize_stats(a.csv, a.out, a.command)
+    elif a.cmd == "mfma":
+        print(json.dumps(summarize_mfma(a.csv, a.out, a.command), indent=1))
     else:
         print(json.dumps(summarize_traffic(a.fetch_csv, a.write_csv, a.out_stem, a.kernel, a.kernel_regex,
                                            a.copy_bytes, a.command_fetch, a.command_write), indent=1))
