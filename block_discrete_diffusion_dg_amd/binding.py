@@ -9,7 +9,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+# The in-tree build; DG_LIB_PATH names another build of the same library
+# (the host-side sanitizer build of the ABI tests).
+LIB_PATH = os.environ.get("DG_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
 
 DG_OK, DG_EINVAL, DG_ECAPACITY, DG_EHIP, DG_ESTATE = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "DG_OK", -1: "DG_EINVAL", -2: "DG_ECAPACITY", -3: "DG_EHIP", -4: "DG_ESTATE"}

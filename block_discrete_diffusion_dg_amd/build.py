@@ -56,6 +56,34 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def build_asan(verbose: bool = False) -> str:
+    """A copy of the library whose host code (the C ABI: argument checks,
+    workspace carving, launch sequences) is built with AddressSanitizer, in
+    _build/libdg_asan.so for host-side tests; the device code is unchanged.
+    Load it with the sanitizer runtime preloaded."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    objs = []
+    for src in srcs:
+        if os.path.basename(src) == "api.hip":
+            obj = os.path.join(BUILD, "api_asan.o")
+            cmd = [hipcc(), *HIPFLAGS, "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-c", src, "-o", obj]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError("hipcc failed on api.hip (asan):\n" + res.stdout + res.stderr)
+            objs.append(obj)
+        else:
+            objs.append(_compile(src, verbose))
+    out = os.path.join(BUILD, "libdg_asan.so")
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Xarch_host", "-fsanitize=address", *objs,
+           "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed (asan):\n" + res.stdout + res.stderr)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip for gfx950 and link libdg.so next to this file."""
     os.makedirs(BUILD, exist_ok=True)
