@@ -137,6 +137,9 @@ def main():
                     help="override the workload's number of requests (batch-size sweep; 0 = the workload's)")
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the extra measurement with FP8 expert weights")
+    ap.add_argument("--profile", action="store_true",
+                    help="for hardware-counter runs: fill the prefix K/V with random values instead of running "
+                         "the prefill, and skip the block commit, so that only denoising steps are dispatched")
     ap.add_argument("--no-variants", action="store_true",
                     help="measure the headline step only (no sampled-candidate, AR, FP8 or self-conditioning runs)")
     ap.add_argument("--no-selfcond-variant", action="store_true",
@@ -176,8 +179,18 @@ def main():
     seeds = [wl.seed + r for r in reqs]
     blocks = [0] * n_req
     t0 = time.time()
-    for r in reqs:
-        eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
+    if args.profile:
+        # counter runs: random prefix K/V written straight into the cache, so
+        # that only the denoising step's kernels are dispatched
+        for r in reqs:
+            for l in range(cfg.n_layers):
+                k = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), wl.seed + r, l, "k", dev)
+                v = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), wl.seed + r, l, "v", dev)
+                eng.set_cache_rows(r, l, k, v)
+            eng.set_cache_len(r, P)
+    else:
+        for r in reqs:
+            eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
     torch.cuda.synchronize()
     log(f"prefill of {n_req} x {P} tokens: {time.time() - t0:.2f}s")
     x = torch.empty(rows, dtype=torch.int32, device=dev)
@@ -240,14 +253,16 @@ def main():
             raise RuntimeError("expert kernel waits ran out during the graph-launched steps")
 
     # commit (the +K-1 forward of each block), timed once, then the length restored
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    eng.commit_block(reqs, x)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    commit_ms = c0.elapsed_time(c1)
-    for r in reqs:
-        eng.set_cache_len(r, P)
+    commit_ms = None
+    if not args.profile:
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        eng.commit_block(reqs, x)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        commit_ms = c0.elapsed_time(c1)
+        for r in reqs:
+            eng.set_cache_len(r, P)
 
     kinds, per_step = algorithmic_model(cfg, P, rows, touched)
     t_roof = sum(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) for b, f in per_step.values())
@@ -313,7 +328,7 @@ def main():
         "kernel_rooflines": kernels,
         "stages_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,
-        "commit_ms": round(commit_ms, 3),
+        "commit_ms": round(commit_ms, 3) if commit_ms is not None else None,
         "graph_launched": graph,
     }
     if not args.no_cpu_baseline and args.workload in ("full", "one_layer", "tiny"):
