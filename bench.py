@@ -138,8 +138,9 @@ def main():
     ap.add_argument("--no-fp8-variant", action="store_true",
                     help="skip the extra measurement with FP8 expert weights")
     ap.add_argument("--profile", action="store_true",
-                    help="for hardware-counter runs: fill the prefix K/V with random values instead of running "
-                         "the prefill, and skip the block commit, so that only denoising steps are dispatched")
+                    help="for hardware-counter runs: skip the block commit, so that every dispatch after the "
+                         "canvas set-up (init_canvas_kernel) belongs to a denoising step; the prefill runs as "
+                         "usual, so routing and attention see the same inputs as the headline run")
     ap.add_argument("--no-variants", action="store_true",
                     help="measure the headline step only (no sampled-candidate, AR, FP8 or self-conditioning runs)")
     ap.add_argument("--no-selfcond-variant", action="store_true",
@@ -179,18 +180,8 @@ def main():
     seeds = [wl.seed + r for r in reqs]
     blocks = [0] * n_req
     t0 = time.time()
-    if args.profile:
-        # counter runs: random prefix K/V written straight into the cache, so
-        # that only the denoising step's kernels are dispatched
-        for r in reqs:
-            for l in range(cfg.n_layers):
-                k = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), wl.seed + r, l, "k", dev)
-                v = synth.make_random_kv((cfg.n_kv_heads, P, cfg.head_dim), wl.seed + r, l, "v", dev)
-                eng.set_cache_rows(r, l, k, v)
-            eng.set_cache_len(r, P)
-    else:
-        for r in reqs:
-            eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
+    for r in reqs:
+        eng.prefill(r, synth.make_prompt(P, cfg.vocab, wl.seed, r, device=dev))
     torch.cuda.synchronize()
     log(f"prefill of {n_req} x {P} tokens: {time.time() - t0:.2f}s")
     x = torch.empty(rows, dtype=torch.int32, device=dev)

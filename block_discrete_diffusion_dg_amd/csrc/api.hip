@@ -68,7 +68,7 @@ dg_ws_layout make_layout(const dg_config& c) {
   L.stats = take(R * sizeof(dg_row_stats));
   L.ids = take(R * 4);
   L.ss = take(R * (d / 64) * 4);
-  L.zpart = take(4 * (size_t)div_up((int)R, 16) * 16 * E * 4);
+  L.zpart = take(8 * (size_t)div_up((int)R, 16) * 16 * E * 4);
   L.sync = take((router_sync_words(c.max_rows) + groups) * 4);  // router row blocks, then attention groups
   L.prev = take((size_t)c.max_requests * c.canvas * 4);
   const size_t Fsc = c.d_selfcond > 0 ? (size_t)c.d_selfcond : 0, on = Fsc > 0 ? 1 : 0;

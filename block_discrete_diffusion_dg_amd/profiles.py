@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the repository's profiles/ folder.
 
-  python -m block_discrete_diffusion_dg_amd.profiles stats <kernel_stats.csv> <out.md> --command "<cmd>"
+  python -m block_discrete_diffusion_dg_amd.profiles stats <kernel_trace.csv> <out.md> --command "<cmd>"
   python -m block_discrete_diffusion_dg_amd.profiles traffic <fetch_csv> <write_csv> <out_stem>
       --kernel <name regex> --copy-bytes N --command-fetch "<cmd>" --command-write "<cmd>"
   python -m block_discrete_diffusion_dg_amd.profiles mfma <counter_csv> <out.md> --command "<cmd>"
@@ -10,6 +10,12 @@
 bytes per launch of one kernel, scaled by what the same counter reads for a
 plain device copy of known size, and records a hash of the kernel's sources:
 bench.py reports the figure only while the sources still hash the same.
+
+Every summary counts only the dispatches issued after the first dispatch of
+the marker kernel (--after, default init_canvas_kernel): in `bench.py
+--profile` the prefill runs before the canvas is set up, and everything after
+it is denoising steps, so the prefill's launches of the same kernels (2,048
+causal rows) do not enter the per-step averages.
 """
 from __future__ import annotations
 
@@ -37,6 +43,7 @@ MFMA_CLASSES = [("attention (attn_kernel)", r"attn_kernel"), ("LM head (lmhead_k
                 ("experts (moe_experts_kernel)", r"moe_experts_kernel"), ("QKV (qkv_sk_kernel)", r"qkv_sk_kernel"),
                 ("O-proj (resid_sk_kernel)", r"resid_sk_kernel"), ("router (router_kernel)", r"router_kernel")]
 GPU_CLOCK_HZ = 2.4e9  # MI355X peak engine clock, for cycles -> time
+N_XCD = 8  # accelerator complex dies; GRBM_GUI_ACTIVE is summed over them
 
 
 def source_hash(kernel: str) -> str:
@@ -52,39 +59,72 @@ def _short(name: str) -> str:
     return re.sub(r"\(.*", "", name)
 
 
-def summarize_stats(csv_path: str, out_md: str, command: str) -> None:
-    """Library kernels first (per-call time), then one line for everything the
-    host framework launched (weight generation, copies) outside the step."""
-    rows = list(csv.DictReader(open(csv_path)))
-    ours = [r for r in rows if "at::native" not in r["Name"] and "rocclr" not in r["Name"]]
-    other = [r for r in rows if r not in ours]
+MARKER = "init_canvas_kernel"
+
+
+def _dispatch_order(r) -> int:
+    for key in ("Dispatch_Id", "Correlation_Id", "Start_Timestamp"):
+        if r.get(key) not in (None, ""):
+            return int(r[key])
+    raise KeyError("no dispatch id or timestamp column")
+
+
+def after_marker(rows, marker: str = MARKER):
+    """The rows (one per dispatch, or per dispatch and counter) issued after
+    the first dispatch of `marker`, and whether the marker was found (if not,
+    every row is kept)."""
+    marks = [_dispatch_order(r) for r in rows if marker and marker in r["Kernel_Name"]]
+    if not marks:
+        return list(rows), False
+    first = min(marks)
+    return [r for r in rows if _dispatch_order(r) > first], True
+
+
+def _scope_line(found: bool, marker: str) -> str:
+    return (f"Counted: dispatches after the first `{marker}` (the denoising steps; the prefill's launches "
+            "come before it)." if found else f"Counted: every dispatch (no `{marker}` dispatch in the trace).")
+
+
+def summarize_stats(csv_path: str, out_md: str, command: str, marker: str = MARKER) -> dict:
+    """Per-dispatch kernel trace -> per-kernel calls and mean duration: library
+    kernels first, then one line for everything the host framework launched
+    (weight generation, copies)."""
+    rows, found = after_marker(list(csv.DictReader(open(csv_path))), marker)
+    per = defaultdict(list)
+    for r in rows:
+        per[_short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    ours = {k: v for k, v in per.items() if "at::native" not in k and "rocclr" not in k and "__amd" not in k}
+    other = [d for k, v in per.items() if k not in ours for d in v]
     lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
-             f"Command: `{command}`", "",
+             f"Command: `{command}`", "", _scope_line(found, marker), "",
              "Library kernels (the denoising path):", "",
              "| kernel | calls | avg us | total ms |", "|---|---:|---:|---:|"]
-    for r in ours:
-        lines.append(f"| {_short(r['Name'])[:60]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['TotalDurationNs']) / 1e6:.2f} |")
-    tot = sum(float(r["TotalDurationNs"]) for r in other) / 1e6
-    calls = sum(int(r["Calls"]) for r in other)
-    lines += ["", f"Other kernels (PyTorch weight generation and runtime copies before the timed "
-                  f"steps): {calls} calls, {tot:.1f} ms in total."]
+    out = {}
+    for k, v in sorted(ours.items(), key=lambda kv: -sum(kv[1])):
+        out[k] = {"calls": len(v), "avg_us": sum(v) / len(v)}
+        lines.append(f"| {k[:60]} | {len(v)} | {sum(v) / len(v):.2f} | {sum(v) / 1e3:.2f} |")
+    lines += ["", f"Other kernels in the same span (runtime copies and PyTorch): {len(other)} calls, "
+                  f"{sum(other) / 1e3:.1f} ms in total."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
+    return out
 
 
-def _per_dispatch(csv_path: str, counter: str):
+def _per_dispatch(csv_path: str, counter: str, marker: str = MARKER):
+    """Counter values per kernel name, for the dispatches after the marker
+    (the copy probe runs after the timed steps, so it is among them)."""
+    rows, found = after_marker(list(csv.DictReader(open(csv_path))), marker)
     per = defaultdict(list)
-    for r in csv.DictReader(open(csv_path)):
+    for r in rows:
         if r["Counter_Name"] == counter:
             per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return per
+    return per, found
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, out_stem: str, kernel: str, kernel_regex: str,
-                      copy_bytes: int, command_fetch: str, command_write: str) -> dict:
-    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
-    write = _per_dispatch(write_csv, "WRITE_SIZE")
+                      copy_bytes: int, command_fetch: str, command_write: str, marker: str = MARKER) -> dict:
+    fetch, found_f = _per_dispatch(fetch_csv, "FETCH_SIZE", marker)
+    write, found_w = _per_dispatch(write_csv, "WRITE_SIZE", marker)
     pat = re.compile(kernel_regex)
 
     def pick(per):
@@ -105,6 +145,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_stem: str, kernel: str
         "kernel": kernel,
         "kernel_regex": kernel_regex,
         "dispatches": {"fetch": nf, "write": nw},
+        "after_marker": marker if found_f and found_w else None,
         "fetch_kib_per_dispatch": f_kib,
         "write_kib_per_dispatch": w_kib,
         "copy_probe_bytes": copy_bytes,
@@ -122,7 +163,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_stem: str, kernel: str
         json.dump(rec, f, indent=1)
     md = [f"# HBM traffic of {kernel} (rocprofv3 --pmc)", "",
           f"FETCH_SIZE command: `{command_fetch}`", "",
-          f"WRITE_SIZE command: `{command_write}`", "",
+          f"WRITE_SIZE command: `{command_write}`", "", _scope_line(found_f and found_w, marker), "",
           f"- dispatches: {nf} (fetch run), {nw} (write run)",
           f"- FETCH_SIZE: {f_kib:.0f} KiB per dispatch" if f_kib is not None else "- FETCH_SIZE: n/a",
           f"- WRITE_SIZE: {w_kib:.0f} KiB per dispatch" if w_kib is not None else "- WRITE_SIZE: n/a",
@@ -135,19 +176,24 @@ def summarize_traffic(fetch_csv: str, write_csv: str, out_stem: str, kernel: str
     return rec
 
 
-def summarize_mfma(csv_path: str, out_md: str, command: str) -> dict:
+def summarize_mfma(csv_path: str, out_md: str, command: str, marker: str = MARKER) -> dict:
     """Per kernel class: mean MfmaUtil (percent of SIMD cycles with the matrix
     core busy while the dispatch ran), bf16 MFMA flops per dispatch, and the
-    GPU-active cycles per dispatch (time at the peak clock)."""
+    GPU-active cycles per dispatch. GRBM_GUI_ACTIVE counts busy cycles of each
+    of the 8 XCDs and rocprofv3 sums them, so the dispatch's active time is
+    the sum / 8 at the 2.4 GHz peak clock."""
     per = defaultdict(lambda: defaultdict(list))
-    for r in csv.DictReader(open(csv_path)):
+    rows, found = after_marker(list(csv.DictReader(open(csv_path))), marker)
+    for r in rows:
         per[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
     out = {}
     lines = ["# Matrix-core use per kernel (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
              "MfmaUtil is rocprofv3's derived metric: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs over "
              "GRBM_GUI_ACTIVE times the SIMD count, during each dispatch (counters serialise the dispatches). "
-             "MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. Rate = flops / (active cycles / 2.4 GHz); "
-             "the dense bf16 peak is 2.5 PFLOP/s.", "",
+             "MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. GRBM_GUI_ACTIVE is summed over the 8 XCDs, "
+             "so active time = GRBM_GUI_ACTIVE / 8 / 2.4 GHz, and rate = flops / active time; the dense bf16 "
+             "peak is 2.5 PFLOP/s. Collecting counters lengthens short dispatches, so active times run above "
+             "the kernel-trace durations.", "", _scope_line(found, marker), "",
              "| kernel | dispatches | MfmaUtil % | bf16 GFLOP per dispatch | active us per dispatch | TFLOP/s | of peak |",
              "|---|---:|---:|---:|---:|---:|---:|"]
     for label, pat in MFMA_CLASSES:
@@ -158,7 +204,7 @@ def summarize_mfma(csv_path: str, out_md: str, command: str) -> dict:
         if not util:
             continue
         u, f, a = sum(util) / len(util), sum(flops) / max(1, len(flops)), sum(act) / max(1, len(act))
-        t = a / GPU_CLOCK_HZ
+        t = a / N_XCD / GPU_CLOCK_HZ
         rate = f / t / 1e12 if t > 0 else 0.0
         out[label] = {"dispatches": len(util), "mfma_util_pct": u, "gflop": f / 1e9, "active_us": t * 1e6,
                       "tflops": rate}
@@ -191,6 +237,7 @@ def main():
     s.add_argument("csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--after", default=MARKER)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -200,18 +247,20 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    t.add_argument("--after", default=MARKER)
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("out")
     m.add_argument("--command", required=True)
+    m.add_argument("--after", default=MARKER)
     a = ap.parse_args()
     if a.cmd == "stats":
-        summarize_stats(a.csv, a.out, a.command)
+        print(json.dumps(summarize_stats(a.csv, a.out, a.command, a.after), indent=1))
     elif a.cmd == "mfma":
-        print(json.dumps(summarize_mfma(a.csv, a.out, a.command), indent=1))
+        print(json.dumps(summarize_mfma(a.csv, a.out, a.command, a.after), indent=1))
     else:
         print(json.dumps(summarize_traffic(a.fetch_csv, a.write_csv, a.out_stem, a.kernel, a.kernel_regex,
-                                           a.copy_bytes, a.command_fetch, a.command_write), indent=1))
+                                           a.copy_bytes, a.command_fetch, a.command_write, a.after), indent=1))
 
 
 if __name__ == "__main__":
