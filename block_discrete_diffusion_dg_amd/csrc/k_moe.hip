@@ -76,19 +76,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
   using T = StreamTile<MT>;
   __shared__ __align__(16) bf16_t lds[T::LDS_ELEMS];
   __shared__ int32_t s_gu[MOE_MAX_GROUPS + 1], s_dn[MOE_MAX_GROUPS + 1], s_ch[MOE_MAX_GROUPS + 1];
+  __shared__ int32_t s_cnt[MOE_MAX_GROUPS], s_off[MOE_MAX_GROUPS];
   __shared__ float s_w[T::CH];
   __shared__ int s_item;
   const int G = p.E + 1;
+  int32_t* queue = p.items + MOE_QUEUE;
+  // The work-list tables: item and chunk offsets, and each expert's row
+  // count and offset, which every item needs before its weights can stream.
+  // (Taking the first ticket together with these loads made every
+  // work-group hit the queue counter at the same instant: the atomics
+  // serialise, and the launch started ~12 us later.)
   for (int i = threadIdx.x; i <= G; i += 256) {
     s_gu[i] = p.items[MOE_ITEMS_GU + i];
     s_dn[i] = p.items[MOE_ITEMS_DN + i];
     s_ch[i] = p.items[MOE_CHUNKS + i];
+    if (i < p.E) {
+      s_cnt[i] = p.cnt[i];
+      s_off[i] = p.off[i];
+    }
   }
   // weight loads run this many K-steps ahead (for FP8 too: five steps ahead,
   // which would keep as many bytes in flight as bf16, spilled registers and
   // measured slower)
   constexpr int EXPERT_DW = 2;
-  int32_t* queue = p.items + MOE_QUEUE;
   int32_t* done = p.items + MOE_DONE;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, grp = lane >> 4;
   // Gate/up items beyond the first round of the resident grid start only as
@@ -121,8 +131,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
     const int gi = __builtin_amdgcn_readfirstlane(find_group(s_it, G, bl));
     const bool shared = gi == 0;
     const int e = gi - 1;
-    const int n = shared ? p.rows : p.cnt[e];
-    const int base = shared ? 0 : p.off[e];
+    const int n = shared ? p.rows : s_cnt[e];
+    const int base = shared ? 0 : s_off[e];
     const int nmc = div_up(n, T::CH);
     const int local = bl - s_it[gi];
     const int nt = local / nmc, mc = local % nmc;
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       auto gate_up = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 ag[MTI], au[MTI];
-        stream_tile<MTI, true, EXPERT_DW, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0, W1, S0, S1,
+        stream_tile<MTI, true, EXPERT_DW, 2, W8, (MT >= 8)>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, W0, W1, S0, S1,
                                          p.d, ag, au, lds);
         // Publish: stage the 64-column tile in LDS, write whole 128-byte row
         // segments with write-through (agent-coherent) stores, wait until they
@@ -182,7 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
         constexpr int MTI = decltype(mt_tag)::value;
         constexpr int LDF = 33;  // padded fp32 row of the staging tiles
         f32x4 acc[MTI], unused[MTI];
-        stream_tile<MTI, false, EXPERT_DW, 2, W8>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, Wh, nullptr,
+        stream_tile<MTI, false, EXPERT_DW, 2, W8, (MT >= 8)>(p.u, p.d, shared ? nullptr : p.perm + base, row0, nrows, Wh, nullptr,
                                                   Sh, nullptr, p.d, acc, unused, lds);
         __syncthreads();  // the tile's last LDS reads are done
         float* stf = reinterpret_cast<float*>(lds);  // [gate, up][16 MTI][LDF] fp32
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
       auto down = [&](auto mt_tag) {
         constexpr int MTI = decltype(mt_tag)::value;
         f32x4 acc0[MTI], acc1[MTI];
-        stream_tile<MTI, true, EXPERT_DW, 2, W8>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
+        stream_tile<MTI, true, EXPERT_DW, 2, W8, (MT >= 8)>(A, K, nullptr, row0, nrows, wrow<W8>(Wd, wr, K), wrow<W8>(Wd, wr + 16, K),
                                          Sd, W8 ? Sd + 16 : nullptr, K, acc0, acc1, lds);
         if (shared) {
 #pragma unroll

@@ -105,7 +105,9 @@ struct Lcm {
 
 // W8: the blocks hold FP8 codes (pack8_index) and wsc[nb] points at the
 // block's 16 row scales; otherwise bf16 (pack_index) and wsc is unused.
-template <int MT, int NB, int DW = 2, int DA = 2, bool W8 = false>
+// EARLY_W: the first DW steps of weights are issued before the token-row
+// indices are read (costs registers; off where the register budget is tight).
+template <int MT, int NB, int DW = 2, int DA = 2, bool W8 = false, bool EARLY_W = false>
 __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int lda,
                                               const int32_t* __restrict__ rowmap, int row0, int nrows,
                                               const void* const (&w)[NB], const float* const (&wsc)[NB], int K,
@@ -123,6 +125,29 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int nk = K / BK;
+  const char* wl[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wl[nb] = static_cast<const char*>(w[nb]) + lane * 16;
+  u32x4 ra[NA][ACH];
+  u32x4 b[NW][NB][NQ];
+  // Loads of step st (clamped to the last step) into weight register set sw.
+  auto issue_w = [&](int sw, int st) {
+    const int64_t off = (int64_t)min(st, nk - 1) * STEP_BYTES;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b[sw][nb][q] = ld16(wl[nb] + off + q * 1024);
+  };
+  // With EARLY_W the first DW steps of weights go out before anything else:
+  // they depend on nothing, while the token rows wait for their row indices
+  // (a gather through rowmap), so the weight stream starts a memory round
+  // trip sooner.
+  if constexpr (EARLY_W) {
+#pragma unroll
+    for (int j = 0; j < DW; ++j) issue_w(j, j);
+  }
+
   const bf16_t* arow[ACH];
   int aoff[ACH];
 #pragma unroll
@@ -133,32 +158,17 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
     arow[i] = A + (int64_t)row * lda + kc;
     aoff[i] = r * LDA + kc;
   }
-  const int nk = K / BK;
-  const char* wl[NB];
   float sc[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    wl[nb] = static_cast<const char*>(w[nb]) + lane * 16;
-    sc[nb] = W8 ? wsc[nb][l16] : 1.0f;
-  }
+  for (int nb = 0; nb < NB; ++nb) sc[nb] = W8 ? wsc[nb][l16] : 1.0f;
 
-  u32x4 ra[NA][ACH];
-  u32x4 b[NW][NB][NQ];
-
-  // Loads of step st (clamped to the last step) into register sets sa / sw.
-  // A loads go first in each step, so the wait for the next step's A rows
-  // (in-order completion) never waits on weights issued after them.
+  // Loads of step st (clamped to the last step) into A register set sa. In
+  // the loop, A loads go first in each step, so the wait for the next step's
+  // A rows (in-order completion) never waits on weights issued after them.
   auto issue_a = [&](int sa, int st) {
     const int k0 = min(st, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < ACH; ++i) ra[sa][i] = ld16(arow[i] + k0);
-  };
-  auto issue_w = [&](int sw, int st) {
-    const int64_t off = (int64_t)min(st, nk - 1) * STEP_BYTES;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[sw][nb][q] = ld16(wl[nb] + off + q * 1024);
   };
   auto stage = [&](int sa, int buf) {
 #pragma unroll
@@ -191,7 +201,7 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
 #pragma unroll
   for (int j = 0; j < (DA > DW ? DA : DW); ++j) {
     if (j < DA) issue_a(j, j);
-    if (j < DW) issue_w(j, j);
+    if (!EARLY_W && j < DW) issue_w(j, j);
   }
   stage(0, 0);
   __syncthreads();
@@ -215,7 +225,7 @@ __device__ __forceinline__ void stream_tile_n(const bf16_t* __restrict__ A, int 
 
 // One weight row per lane (acc0), or with GATED two (acc0 from w0, acc1 from
 // w1): the single-block and paired forms of stream_tile_n.
-template <int MT, bool GATED, int DW = 2, int DA = 2, bool W8 = false>
+template <int MT, bool GATED, int DW = 2, int DA = 2, bool W8 = false, bool EARLY_W = false>
 __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int lda,
                                             const int32_t* __restrict__ rowmap, int row0, int nrows,
                                             const void* __restrict__ w0, const void* __restrict__ w1,
@@ -225,7 +235,7 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     const void* const w[2] = {w0, w1};
     const float* const ws[2] = {s0, s1};
     f32x4 acc[2][MT];
-    stream_tile_n<MT, 2, DW, DA, W8>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
+    stream_tile_n<MT, 2, DW, DA, W8, EARLY_W>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       acc0[mt] = acc[0][mt];
@@ -235,7 +245,7 @@ __device__ __forceinline__ void stream_tile(const bf16_t* __restrict__ A, int ld
     const void* const w[1] = {w0};
     const float* const ws[1] = {s0};
     f32x4 acc[1][MT];
-    stream_tile_n<MT, 1, DW, DA, W8>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
+    stream_tile_n<MT, 1, DW, DA, W8, EARLY_W>(A, lda, rowmap, row0, nrows, w, ws, K, acc, lds);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc[0][mt];
   }
