@@ -182,12 +182,17 @@ __device__ __forceinline__ void permute_block(const PermuteArgs& a, char* lds, b
   const bool one_batch = !chunked && pairs <= PB * nt;
   int evc[PB];
   if (!chunked) {
+    // with one batch, the ids are loaded before the tables are cleared
+    if (one_batch) {
+#pragma unroll
+      for (int j = 0; j < PB; ++j) evc[j] = load_idx(tid + j * nt);
+    }
     for (int i = tid; i < E * nb; i += nt) mask[i] = 0ull;
     __syncthreads();
     for (int i0 = tid; i0 < pairs; i0 += PB * nt) {
       int ev[PB];
 #pragma unroll
-      for (int j = 0; j < PB; ++j) ev[j] = load_idx(i0 + j * nt);
+      for (int j = 0; j < PB; ++j) ev[j] = one_batch ? evc[j] : load_idx(i0 + j * nt);
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         evc[j] = ev[j];
@@ -495,27 +500,39 @@ __global__ __launch_bounds__(256) void router_kernel(
   // every sum is formed before any store: gfx950 counts stores in the same
   // in-order counter as loads, so a store placed between a load and its use
   // would make that use wait for the store's round trip too.
-  float pv[8][RKS];
+  // Each thread takes two runs of four consecutive experts of one row (E is a
+  // multiple of 8), 16-byte loads.
+  float4 pv[2][RKS];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int i = min(tid + 256 * b, RB * E - 1), t = min(t0 + i / E, rows - 1), e = i % E;
+  for (int b = 0; b < 2; ++b) {
+    const int i = min((tid + 256 * b) * 4, RB * E - 4), t = min(t0 + i / E, rows - 1), e = i % E;
 #pragma unroll
-    for (int q = 0; q < RKS; ++q) pv[b][q] = zpart[((int64_t)q * zs + t) * E + e];
+    for (int q = 0; q < RKS; ++q) pv[b][q] = *reinterpret_cast<const float4*>(zpart + ((int64_t)q * zs + t) * E + e);
   }
-  float zv[8];
+  float4 zv[2];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
+  for (int b = 0; b < 2; ++b) {
     zv[b] = pv[b][0];
 #pragma unroll
-    for (int q = 1; q < RKS; ++q) zv[b] += pv[b][q];
+    for (int q = 1; q < RKS; ++q) {
+      zv[b].x += pv[b][q].x;
+      zv[b].y += pv[b][q].y;
+      zv[b].z += pv[b][q].z;
+      zv[b].w += pv[b][q].w;
+    }
   }
   __syncthreads();  // the dense staging view of zt is no longer read
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int i = tid + 256 * b, r = i / E, t = t0 + r, e = i % E;
+  for (int b = 0; b < 2; ++b) {
+    const int i = (tid + 256 * b) * 4, r = i / E, t = t0 + r, e = i % E;
     if (i < RB * E) {
-      if (t < rows) z[(int64_t)t * E + e] = zv[b];
-      zt[r * (E + 1) + e] = t < rows ? zv[b] : 0.f;
+      const bool live = t < rows;
+      if (live) *reinterpret_cast<float4*>(z + (int64_t)t * E + e) = zv[b];
+      float* zr = zt + r * (E + 1) + e;
+      zr[0] = live ? zv[b].x : 0.f;
+      zr[1] = live ? zv[b].y : 0.f;
+      zr[2] = live ? zv[b].z : 0.f;
+      zr[3] = live ? zv[b].w : 0.f;
     }
   }
   __syncthreads();
