@@ -311,6 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
 // h[t] += ys[t] + sum_j y[slot[t][j]]  (fixed order: deterministic); then, when
 // next_gain is given, u[t] = bf16(RMSNorm(h[t]) * next_gain): the pre-norm of
 // the next layer (or the final norm) on the row just completed.
+template <int MAXV>  // float4 per thread: d <= 1024 * MAXV
 __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
                                                           const float* __restrict__ ys,
                                                           const bf16_t* __restrict__ y,
@@ -322,28 +323,41 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < k) sl[tid] = slot[t * k + tid];
   __syncthreads();
-  constexpr int MAXV = 4;  // float4 per thread: d <= 4096
-  float4 hv[MAXV];
+  constexpr int MAXK = 8;  // k <= 8
+  // Every load is issued before any sum (the k expert rows are independent
+  // loads; a loop over k that adds as it loads would wait for each in turn).
+  float4 ysv[MAXV], hv[MAXV];
+  u32x2 yv[MAXV][MAXK], gv[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = min(tid * 4 + 1024 * i, d - 4);  // clamped: in bounds, unused past d
+    ysv[i] = *reinterpret_cast<const float4*>(ys + (int64_t)t * d + c);
+    hv[i] = *reinterpret_cast<const float4*>(h + (int64_t)t * d + c);
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j)
+      yv[i][j] = *reinterpret_cast<const u32x2*>(y + (int64_t)sl[min(j, k - 1)] * d + c);
+    gv[i] = next_gain ? *reinterpret_cast<const u32x2*>(next_gain + c) : u32x2{0u, 0u};
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c = tid * 4 + 1024 * i;
     if (c >= d) break;
-    float4 acc = *reinterpret_cast<const float4*>(ys + (int64_t)t * d + c);
-    for (int j = 0; j < k; ++j) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(y + (int64_t)sl[j] * d + c);
-      acc.x += __uint_as_float(v.x << 16);
-      acc.y += __uint_as_float(v.x & 0xffff0000u);
-      acc.z += __uint_as_float(v.y << 16);
-      acc.w += __uint_as_float(v.y & 0xffff0000u);
+    float4 acc = ysv[i];
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+      if (j >= k) break;
+      acc.x += __uint_as_float(yv[i][j].x << 16);
+      acc.y += __uint_as_float(yv[i][j].x & 0xffff0000u);
+      acc.z += __uint_as_float(yv[i][j].y << 16);
+      acc.w += __uint_as_float(yv[i][j].y & 0xffff0000u);
     }
-    float4* hp = reinterpret_cast<float4*>(h + (int64_t)t * d + c);
-    float4 x = *hp;
+    float4 x = hv[i];
     x.x += acc.x;
     x.y += acc.y;
     x.z += acc.z;
     x.w += acc.w;
-    *hp = x;
+    *reinterpret_cast<float4*>(h + (int64_t)t * d + c) = x;
     hv[i] = x;
     ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
   }
@@ -358,8 +372,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(float* __restrict__ h,
     const int c = tid * 4 + 1024 * i;
     if (c >= d) break;
     const float4 x = hv[i];
-    const uint32_t lo = pack_bf16x2(x.x * inv * bf2f(next_gain[c]), x.y * inv * bf2f(next_gain[c + 1]));
-    const uint32_t hi = pack_bf16x2(x.z * inv * bf2f(next_gain[c + 2]), x.w * inv * bf2f(next_gain[c + 3]));
+    const uint32_t lo = pack_bf16x2(x.x * inv * __uint_as_float(gv[i].x << 16),
+                                    x.y * inv * __uint_as_float(gv[i].x & 0xffff0000u));
+    const uint32_t hi = pack_bf16x2(x.z * inv * __uint_as_float(gv[i].y << 16),
+                                    x.w * inv * __uint_as_float(gv[i].y & 0xffff0000u));
     *reinterpret_cast<u32x2*>(uo + c) = u32x2{lo, hi};
   }
 }
@@ -429,5 +445,8 @@ void launch_moe_experts(hipStream_t s, const bf16_t* u, int rows, int d, int F, 
 
 void launch_moe_combine(hipStream_t s, float* h, const float* ys, const bf16_t* y, const int32_t* slot,
                         int rows, int d, int k, const bf16_t* next_gain, float eps, bf16_t* u) {
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps, u);
+  if (d <= 2048)
+    hipLaunchKernelGGL(moe_combine_kernel<2>, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps, u);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<4>, dim3(rows), dim3(256), 0, s, h, ys, y, slot, d, k, next_gain, eps, u);
 }
