@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void router_kernel(
     const float* __restrict__ h, const float* __restrict__ ss, const bf16_t* __restrict__ gain, int rows, int d,
     float eps, const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
     float* __restrict__ zpart, int32_t* __restrict__ sync, int32_t* __restrict__ idx, float* __restrict__ w,
-    PermuteArgs pa, int do_permute) {
+    PermuteArgs pa, int do_permute, const char* pf0, const char* pf1, const char* pf2, int64_t pfn) {
   extern __shared__ __align__(16) char rt_lds[];
   const int kq = d / RKS, LDA = kq + 8, nct = d / 64;
   bf16_t* As = reinterpret_cast<bf16_t*>(rt_lds);                    // [RB][LDA]
@@ -490,7 +490,13 @@ __global__ __launch_bounds__(256) void router_kernel(
     if (s_last) __hip_atomic_store(sync + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last) {
+    // leaving early (7 of 8 work-groups, ~13 us before the launch ends): the
+    // shared expert's weights, which the expert launch streams first, are
+    // brought towards the caches meanwhile
+    prefetch_stripe(pf0, pf1, pf2, pfn, rt_lds);
+    return;
+  }
 
   // 5. the last arrival: z = p0 + p1 + ... + p7 in that order, then top-k per
   // row. The block's partial lines are read only here, after all were written,
@@ -563,7 +569,7 @@ void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t*
 
 void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
                    const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
-                   float* w, const RouterPermute* perm) {
+                   float* w, const RouterPermute* perm, const void* const* pf, int64_t pfn) {
   const int kq = d / RKS;
   size_t lds = (size_t)RB * (kq + 8) * 2 + (size_t)RB * (E + 1) * 4 + (size_t)RB * (d / 64) * 4;
   PermuteArgs pa{idx, rows, E, k, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
@@ -572,8 +578,10 @@ void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t*
                      perm->perm, perm->slot, perm->widx, perm->items};
     lds = std::max(lds, permute_lds_bytes(rows, E, k));
   }
+  if (pf) lds = std::max(lds, (size_t)4096);  // prefetch_stripe's scratch: 1 KB a wave
   hipLaunchKernelGGL(router_kernel, dim3(div_up(rows, RB) * RKS), dim3(256), lds, s, h, ss, gain, rows, d, eps, wr,
-                     E, k, u, z, zpart, sync, idx, w, pa, perm ? 1 : 0);
+                     E, k, u, z, zpart, sync, idx, w, pa, perm ? 1 : 0, pf ? (const char*)pf[0] : nullptr,
+                     pf ? (const char*)pf[1] : nullptr, pf ? (const char*)pf[2] : nullptr, pf ? pfn : 0);
 }
 
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, const RouterPermute& p) {

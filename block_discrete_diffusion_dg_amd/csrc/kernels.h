@@ -105,9 +105,11 @@ struct RouterPermute {
 };
 // Router (MoE pre-norm, logits, top-k); with perm, the last row block to
 // finish also runs the permutation (sync needs div_up(rows, 16) + 1 words).
+// pf / pfn: three byte ranges of pfn bytes each (the shared expert's
+// matrices) that work-groups leaving early prefetch (prefetch_stripe).
 void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
                    const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
-                   float* w, const RouterPermute* perm);
+                   float* w, const RouterPermute* perm, const void* const* pf = nullptr, int64_t pfn = 0);
 // The permutation as a launch of its own, from expert ids of an earlier launch.
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, const RouterPermute& p);
 size_t permute_lds_bytes(int rows, int E, int k);
