@@ -163,29 +163,6 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
 
 __host__ __device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
 
-// For a work-group that leaves a launch early while others still run (HBM
-// mostly idle): copy its stripe of up to three equal-sized byte ranges that
-// the next launch reads first into scratch LDS (1 KB a wave) with the
-// load-to-LDS path, so that those lines sit in the memory-side cache when
-// the next launch asks. Best effort: stripes of work-groups that do not leave
-// early are skipped. Waits for its copies before returning (the LDS is the
-// work-group's own until it exits).
-__device__ __forceinline__ void prefetch_stripe(const char* r0, const char* r1, const char* r2, int64_t bytes,
-                                                char* lds_scratch) {
-  if (bytes < 16) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const char* rs[3] = {r0, r1, r2};
-#pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    if (!rs[r]) continue;
-    for (int64_t o = ((int64_t)blockIdx.x * nw + wave) * 1024; o < bytes; o += (int64_t)gridDim.x * nw * 1024)
-      __builtin_amdgcn_global_load_lds(rs[r] + min(o + lane * 16, bytes - 16),
-                                       (__attribute__((address_space(3))) void*)(lds_scratch + wave * 1024), 16, 0,
-                                       0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Work-group id -> (column tile nt, row chunk mc) for a grid of NT * MC
 // work-groups. When NT is a multiple of 8, the row chunks of one column tile
 // get ids 8 apart: dispatch is round-robin over the 8 XCDs, so they run on

@@ -13,6 +13,29 @@ size_t permute_lds_bytes(int rows, int E, int k);
 
 namespace {
 
+// For a work-group that leaves a launch early while others still run (HBM
+// mostly idle): copy its stripe of up to three equal-sized byte ranges that
+// the next launch reads first into scratch LDS (1 KB a wave) with the
+// load-to-LDS path, so that those lines sit in the memory-side cache when
+// the next launch asks. Best effort: stripes of work-groups that do not leave
+// early are skipped. Waits for its copies before returning (the LDS is the
+// work-group's own until it exits).
+__device__ __forceinline__ void prefetch_stripe(const char* r0, const char* r1, const char* r2, int64_t bytes,
+                                                char* lds_scratch) {
+  if (bytes < 16) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const char* rs[3] = {r0, r1, r2};
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    if (!rs[r]) continue;
+    for (int64_t o = ((int64_t)blockIdx.x * nw + wave) * 1024; o < bytes; o += (int64_t)gridDim.x * nw * 1024)
+      __builtin_amdgcn_global_load_lds(rs[r] + min(o + lane * 16, bytes - 16),
+                                       (__attribute__((address_space(3))) void*)(lds_scratch + wave * 1024), 16, 0,
+                                       0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Top-k (k <= 8) of E <= 128 logits for each of RB = 16 rows: every 16-lane
 // group of the work-group's four waves takes one row, lane l16 holding the
 // logits of experts l16 + 16m (m < 8; experts past E read as -inf). Each
