@@ -261,7 +261,10 @@ def main():
     # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
     # plain copy), only while the kernel's sources match the recorded hash
     from block_discrete_diffusion_dg_amd.profiles import traffic_for
-    traffic = traffic_for("moe_experts", f"moe_experts_{wl.name}_traffic")
+    # the counter records are taken on the workloads as defined (a request
+    # count given on the command line is another workload: no record)
+    rec_stem = wl.name if not args.n_req or args.n_req == wl.n_req else None
+    traffic = traffic_for("moe_experts", f"moe_experts_{rec_stem}_traffic") if rec_stem else None
     traffic = round(traffic) if traffic is not None else None
     ex_launch_ms = stages["experts"][0] / max(1, stages["experts"][1])
     achieved = b_ex / (ex_launch_ms * 1e-3)
@@ -282,10 +285,10 @@ def main():
                          "frac": round(max(b / HBM_PEAK, f / MFMA_BF16_PEAK) / t, 4),
                          "bytes_per_launch": round(b), "flops_per_launch": round(f),
                          "avg_launch_ms": round(t * 1e3, 4)}
-    lm_traffic = traffic_for("lmhead", f"lmhead_{wl.name}_traffic")
+    lm_traffic = traffic_for("lmhead", f"lmhead_{rec_stem}_traffic") if rec_stem else None
     if "lmhead" in kernels:
         kernels["lmhead"]["traffic"] = round(lm_traffic) if lm_traffic is not None else None
-    attn_traffic = traffic_for("attn", f"attn_{wl.name}_traffic")
+    attn_traffic = traffic_for("attn", f"attn_{rec_stem}_traffic") if rec_stem else None
     if "attn" in kernels:
         kernels["attn"]["traffic"] = round(attn_traffic) if attn_traffic is not None else None
     steps_per_s = 1e3 / ms

@@ -245,11 +245,16 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
                                      c->buf<float>(L.ss)));
   int32_t* items = c->buf<int32_t>(L.items);
   const RouterPermute rp = permute_outputs(c, rows);
+  // shared-expert prefetch by the router's early leavers: only while the
+  // router is one short round of work-groups (at more rows it lengthened the
+  // router more than it saved)
   const void* const rpf[3] = {w.ws_gate, w.ws_up, w.ws_down};
+  const bool prefetch = rows <= 512;
   STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,
                                        g.n_experts, g.top_k, u, c->buf<float>(L.z), c->buf<float>(L.zpart),
                                        c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w), &rp,
-                                       rpf, (int64_t)g.d_shared * d * (g.expert_format == DG_WEIGHTS_FP8 ? 1 : 2)));
+                                       prefetch ? rpf : nullptr,
+                                       (int64_t)g.d_shared * d * (g.expert_format == DG_WEIGHTS_FP8 ? 1 : 2)));
   bf16_t* y = c->buf<bf16_t>(L.y);
   float* ys = reinterpret_cast<float*>(y + (size_t)g.max_rows * g.top_k * d);
   STAGE(DG_STAGE_EXPERTS,

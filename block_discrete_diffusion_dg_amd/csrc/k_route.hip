@@ -361,35 +361,41 @@ __global__ __launch_bounds__(1024) void permute_kernel(PermuteArgs a) {
 }
 
 // MoE pre-norm, router logits and top-k. Work-group (row block rb of RB = 16
-// rows, K eighth ks) of a grid of ceil(rows/16) x 8 (eighths rather than
-// quarters: each work-group's first loads, which set the pace of the launch,
-// halve, and the launch measured ~1 us faster):
+// rows, K part ks) of a grid of ceil(rows/16) x RKS, d split into RKS parts:
+// eighths for calls of up to 512 rows (each work-group's first loads, which
+// set the pace of such a launch, halve against quarters, ~1 us faster),
+// quarters above (the extra partial lines and the last arrival's longer sum
+// cost more than the shorter first loads save once the launch holds several
+// waves of work-groups):
 //  1. issues every load that depends on nothing at once, in order of use:
-//     the sums of squares of its rows, its eighth of the hidden-state rows
+//     the sums of squares of its rows, its part of the hidden-state rows
 //     and norm gains, and its router weight fragments (expert rows
-//     16*(2w+n) + l16 of wave w, clamped to E-1, over its eighth of d);
+//     16*(2w+n) + l16 of wave w, clamped to E-1, over its part of d);
 //  2. 1/rms of its rows from the output projection's per-64-column sums of
 //     squares (summed in a fixed order);
-//  3. u = bf16(h / rms * gain) on its eighth of d -> workspace (the experts'
+//  3. u = bf16(h / rms * gain) on its part of d -> workspace (the experts'
 //     input rows) and an LDS tile;
-//  4. partial logits of its eighth on the matrix cores, written through to
+//  4. partial logits of its part on the matrix cores, written through to
 //     device-coherent memory, then counts itself in for the row block;
-//  5. the last of the eight to arrive adds the eight partials in eighth
-//     order (deterministic whatever the arrival order), stores z, resets the
+//  5. the last of the RKS to arrive adds the partials in part order
+//     (deterministic whatever the arrival order), stores z, resets the
 //     counter, and selects each row's experts (block_topk16);
 //  6. (with the permutation) the last row block to finish runs it.
-constexpr int RKS = 8;     // K eighths
-constexpr int RSTEPS = 8;  // 32-wide K steps whose weights are loaded at once (an eighth of d = 2048)
+constexpr int ROUTER_EIGHTHS_MAX_ROWS = 512;
 
 __device__ __forceinline__ void store16_coherent(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
 }
 
+template <int RKS>
 __global__ __launch_bounds__(256) void router_kernel(
     const float* __restrict__ h, const float* __restrict__ ss, const bf16_t* __restrict__ gain, int rows, int d,
     float eps, const bf16_t* __restrict__ wr, int E, int k, bf16_t* __restrict__ u, float* __restrict__ z,
     float* __restrict__ zpart, int32_t* __restrict__ sync, int32_t* __restrict__ idx, float* __restrict__ w,
     PermuteArgs pa, int do_permute, const char* pf0, const char* pf1, const char* pf2, int64_t pfn) {
+  // 32-wide K steps whose weight fragments are loaded at once: a whole part
+  // when d = 2048
+  constexpr int RSTEPS = 64 / RKS;
   extern __shared__ __align__(16) char rt_lds[];
   const int kq = d / RKS, LDA = kq + 8, nct = d / 64;
   bf16_t* As = reinterpret_cast<bf16_t*>(rt_lds);                    // [RB][LDA]
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int rb = blockIdx.x / RKS, ks = blockIdx.x % RKS;
   const int t0 = rb * RB, kb = ks * kq, nk = kq / 32;
-  // eighth stride in rows, a multiple of RB: every row block's partials
+  // part stride in rows, a multiple of RB: every row block's partials
   // fill whole 128-byte lines (E % 8 == 0), shared with no other block
   const int zs = div_up(rows, RB) * RB;
 
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
   __syncthreads();
 
-  // 3. normalised rows on this eighth (rows past the end are zero), in
+  // 3. normalised rows on this part (rows past the end are zero), in
   // batches of 8 float4 per thread (the first already loaded)
   for (int i0 = tid * 4; i0 < RB * kq; i0 += 8 * 1024) {
     if (i0 != tid * 4) load_h(i0);
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
   __syncthreads();
 
-  // 4. partial logits: 16 rows x 32 experts per wave over the eighth
+  // 4. partial logits: 16 rows x 32 experts per wave over the part
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int s0 = 0; s0 < nk; s0 += RSTEPS) {
@@ -514,14 +520,15 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
   __syncthreads();
   if (!s_last) {
-    // leaving early (7 of 8 work-groups, ~13 us before the launch ends): the
+    // leaving early (all but one of the RKS work-groups, ~13 us before the
+    // launch ends at 256 rows): the
     // shared expert's weights, which the expert launch streams first, are
     // brought towards the caches meanwhile
     prefetch_stripe(pf0, pf1, pf2, pfn, rt_lds);
     return;
   }
 
-  // 5. the last arrival: z = p0 + p1 + ... + p7 in that order, then top-k per
+  // 5. the last arrival: z = p0 + p1 + ... + p(RKS-1) in that order, then top-k per
   // row. The block's partial lines are read only here, after all were written,
   // and caches start the kernel invalidated: no cache holds a stale copy.
   // (E <= 128: at most 8 entries per thread, every load issued before the sums)
@@ -593,7 +600,8 @@ void launch_topk(hipStream_t s, const float* z, int rows, int E, int k, int32_t*
 void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t* gain, int rows, int d, float eps,
                    const bf16_t* wr, int E, int k, bf16_t* u, float* z, float* zpart, int32_t* sync, int32_t* idx,
                    float* w, const RouterPermute* perm, const void* const* pf, int64_t pfn) {
-  const int kq = d / RKS;
+  const int rks = rows <= ROUTER_EIGHTHS_MAX_ROWS ? 8 : 4;
+  const int kq = d / rks;
   size_t lds = (size_t)RB * (kq + 8) * 2 + (size_t)RB * (E + 1) * 4 + (size_t)RB * (d / 64) * 4;
   PermuteArgs pa{idx, rows, E, k, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (perm) {
@@ -602,9 +610,17 @@ void launch_router(hipStream_t s, const float* h, const float* ss, const bf16_t*
     lds = std::max(lds, permute_lds_bytes(rows, E, k));
   }
   if (pf) lds = std::max(lds, (size_t)4096);  // prefetch_stripe's scratch: 1 KB a wave
-  hipLaunchKernelGGL(router_kernel, dim3(div_up(rows, RB) * RKS), dim3(256), lds, s, h, ss, gain, rows, d, eps, wr,
-                     E, k, u, z, zpart, sync, idx, w, pa, perm ? 1 : 0, pf ? (const char*)pf[0] : nullptr,
-                     pf ? (const char*)pf[1] : nullptr, pf ? (const char*)pf[2] : nullptr, pf ? pfn : 0);
+  const char* p0 = pf ? (const char*)pf[0] : nullptr;
+  const char* p1 = pf ? (const char*)pf[1] : nullptr;
+  const char* p2 = pf ? (const char*)pf[2] : nullptr;
+  const int64_t pn = pf ? pfn : 0;
+  const dim3 grid(div_up(rows, RB) * rks);
+  if (rks == 8)
+    hipLaunchKernelGGL(router_kernel<8>, grid, dim3(256), lds, s, h, ss, gain, rows, d, eps, wr, E, k, u, z, zpart,
+                       sync, idx, w, pa, perm ? 1 : 0, p0, p1, p2, pn);
+  else
+    hipLaunchKernelGGL(router_kernel<4>, grid, dim3(256), lds, s, h, ss, gain, rows, d, eps, wr, E, k, u, z, zpart,
+                       sync, idx, w, pa, perm ? 1 : 0, p0, p1, p2, pn);
 }
 
 void launch_permute(hipStream_t s, const int32_t* idx, int rows, int E, int k, const RouterPermute& p) {

@@ -40,7 +40,8 @@ extern "C" {
  *   stats    dg_row_stats [rows]     per-row LM-head statistics
  *   ss       fp32 [d/64][rows]       partial sums of squares of h per
  *                                    64-column tile (output projection)
- *   zpart    fp32 [8][rows16][E]     router logits per eighth of d
+ *   zpart    fp32 [8][rows16][E]     router logits per part of d: eight
+ *                                    parts up to 512 rows, four above
  *                                    (rows16 = rows rounded up to 16)
  *   sync     int32 [256]             router row-block arrival counters
  *   prev     int32 [max_requests][canvas]  argmax of each slot's last
