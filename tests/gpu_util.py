@@ -27,6 +27,26 @@ def max_rel(gpu, ref):
     return float(np.max(np.abs(gpu - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
+# Element-wise relative errors are reported beside the per-tensor bar, each
+# element's error taken against max(|o|, ELEM_FLOOR * max|o|) so that
+# elements near zero do not dominate.
+ELEM_FLOOR = 1e-3
+
+
+def elem_stats(gpu, ref):
+    """Element-wise |g - o| / max(|o|, 1e-3 max|o|): its maximum, 99th
+    percentile and median over the tensor."""
+    gpu = np.asarray(gpu, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    floor = ELEM_FLOOR * max(float(np.max(np.abs(ref))), 1e-30)
+    e = np.abs(gpu - ref) / np.maximum(np.abs(ref), floor)
+    return {"max": float(e.max()), "p99": float(np.percentile(e, 99)), "median": float(np.median(e))}
+
+
+def fmt_elem(stats):
+    return "/".join(f"{stats[k]:.1e}" for k in ("max", "p99", "median"))
+
+
 EXPERT_FIELDS = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
 
 

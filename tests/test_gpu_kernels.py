@@ -17,8 +17,8 @@ from block_discrete_diffusion_dg_amd import synth
 from block_discrete_diffusion_dg_amd.engine import Engine, stats_fields
 from oracle import model as om
 from oracle.philox import uniform_ids
-from tests.gpu_util import (REL_TOL, HostWeights, make_engine, make_selfcond, max_rel, moe_with_experts,
-                            router_band, router_swaps, say, tie_gap_ok)
+from tests.gpu_util import (REL_TOL, HostWeights, elem_stats, fmt_elem, make_engine, make_selfcond, max_rel,
+                            moe_with_experts, router_band, router_swaps, say, tie_gap_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -560,10 +560,9 @@ def test_layer_parity(name, causal, P, C, over, fmt):
     o_gpu = eng.ws_view("attn_o", torch.bfloat16, (C, cfg.n_q_heads * cfg.head_dim)).cpu()
     z_gpu = eng.ws_view("z", torch.float32, (C, cfg.n_experts)).cpu()
     idx_gpu = eng.ws_view("idx", torch.int32, (C, cfg.top_k)).cpu().numpy()
-    errs = dict(q=max_rel(om.f64(q_gpu), keep["q"]), k=max_rel(om.f64(k_gpu), k_or),
-                v=max_rel(om.f64(v_gpu), v_or),
-                attn=max_rel(om.f64(o_gpu), keep["attn_o"].reshape(C, -1)),
-                z=max_rel(om.f64(z_gpu), keep["z"]))
+    pairs = dict(q=(om.f64(q_gpu), keep["q"]), k=(om.f64(k_gpu), k_or), v=(om.f64(v_gpu), v_or),
+                 attn=(om.f64(o_gpu), keep["attn_o"].reshape(C, -1)), z=(om.f64(z_gpu), keep["z"]))
+    errs = {n: max_rel(g, o) for n, (g, o) in pairs.items()}
     # router decisions on the GPU's own logits are bit-exact
     idx_from_gpu_z, _ = om.route(om.f64(z_gpu), cfg.top_k)
     assert np.array_equal(idx_gpu, idx_from_gpu_z)
@@ -589,8 +588,11 @@ def test_layer_parity(name, causal, P, C, over, fmt):
                                                         keep["idx"]))
     errs["h"] = max_rel(h_dev.cpu(), h_forced)
     errs["h_free"] = max_rel(h_dev.cpu(), h_or)
+    pairs["h"] = (h_dev.cpu(), h_forced)
     say(f"  router swaps within band: {len(swaps)}/{C}; max rel errors:",
         {k: f"{v:.2e}" for k, v in errs.items()})
+    say("  element-wise rel errors (max/p99/median, floor 1e-3 max|o|):",
+        {n: fmt_elem(elem_stats(g, o)) for n, (g, o) in pairs.items()})
     for k_, e in errs.items():
         if k_ != "h_free" or not swaps:
             assert e <= REL_TOL, (k_, e)

@@ -9,12 +9,13 @@ import numpy as np
 import pytest
 import torch
 
+from block_discrete_diffusion_dg_amd import binding as B
 from block_discrete_diffusion_dg_amd import synth
 from block_discrete_diffusion_dg_amd.engine import stats_fields
 from oracle import model as om
 from oracle import philox as philox_mod
-from tests.gpu_util import (REL_TOL, make_engine, make_selfcond, max_rel, moe_with_experts, router_band, router_swaps, say,
-                            tie_gap_ok)
+from tests.gpu_util import (REL_TOL, elem_stats, fmt_elem, make_engine, make_selfcond, max_rel, moe_with_experts,
+                            router_band, router_swaps, say, tie_gap_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -286,7 +287,8 @@ def test_two_layer_full_width_prefill_step_commit():
         swaps = router_swaps(idx[l], keep["z"], cfg.top_k, router_band(keep["u_moe"], lw["w_router"]))
         h_ref = moe_with_experts(keep, lw, cfg, idx[l])
         err = max_rel(hs[l + 1], h_ref)
-        say(f"  layer {l}: h error {err:.2e}, router swaps in band {len(swaps)}/{C}")
+        say(f"  layer {l}: h error {err:.2e} (element-wise max/p99/median {fmt_elem(elem_stats(hs[l + 1], h_ref))}), "
+            f"router swaps in band {len(swaps)}/{C}")
         assert err <= REL_TOL and len(swaps) <= max(2, C // 20)
     say("[full2] oracle LM head over 262,144 ids")
     tau = om.tau_at(1, S, cfg.tau_first, cfg.tau_last)
@@ -344,3 +346,70 @@ def _kv_errors(got, ks, vs, lo, n, keep0, lw0, cfg):
     errs = {"k0": max_rel(got.k[0, lo:lo + n], ks[0]), "v0": max_rel(got.v[0, lo:lo + n], vs[0]),
             "k1": max_rel(k1[keep_rows], ks[1][keep_rows]), "v1": max_rel(v1[keep_rows], vs[1][keep_rows])}
     return errs, len(moved)
+
+
+# Workspace buffers that every call writes before it reads them (float data
+# only: buffers that carry indices or counters are left alone, and so are the
+# rotation table, the previous-argmax table and the self-conditioning state,
+# which persist between calls).
+SCRATCH = ("h", "u", "q", "attn_o", "attn_part", "attn_ml", "z", "w", "hid", "hid_s", "y", "ss", "zpart",
+           "sc_p", "sc_qpart", "sc_part", "sc_e", "sc_g", "sc_u", "sc_hid", "sc_out")
+
+
+def _fill_scratch(eng, byte):
+    """Fill every scratch buffer's bytes (up to the next buffer) with `byte`:
+    0xff makes every bf16 and fp32 value a NaN."""
+    names = B.WS_FIELDS
+    for n in SCRATCH:
+        lo, hi = getattr(eng.layout, n), getattr(eng.layout, names[names.index(n) + 1])
+        if hi > lo:
+            eng.ws[lo:hi].fill_(byte)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("which", ["tiny", "full2"])
+def test_stale_scratch_is_never_read(which):
+    """Two identical engines run the same prefill, canvas, denoising steps and
+    commit; before every call one has its scratch buffers zeroed and the other
+    filled with NaN. A read of a scratch value that the call did not write
+    first would carry the NaN (or the zero) into the results: canvas, mask,
+    row statistics, the previous-argmax table and the KV cache must be equal
+    bit for bit."""
+    if which == "tiny":
+        cfg, P, S = dataclasses.replace(synth.TINY, n_layers=2), 64, 3
+        sc, n_req, max_rows = make_selfcond(cfg, 64, 3), 2, 2 * cfg.canvas
+    else:
+        cfg, P, S = dataclasses.replace(synth.FULL, n_layers=2), 2048, 2
+        sc, n_req, max_rows = None, 1, None
+    C = cfg.canvas
+    engs = [make_engine(cfg, max_ctx=P + 2 * C, max_requests=n_req, max_rows=max_rows, selfcond=sc)[0]
+            for _ in range(2)]
+    prompts = [synth.make_prompt(P, cfg.vocab, 31 + r).cuda() for r in range(n_req)]
+    reqs, seeds, blocks = list(range(n_req)), [41 + r for r in range(n_req)], [0] * n_req
+    outs = []
+    for i, (eng, byte) in enumerate(zip(engs, (0x00, 0xff))):
+        say(f"[{which}] engine {i}: scratch filled with {byte:#04x} before every call")
+        for r in reqs:
+            _fill_scratch(eng, byte)
+            eng.prefill(r, prompts[r])
+        x = torch.empty(n_req * C, dtype=torch.int32, device="cuda")
+        m = torch.empty(n_req * C, dtype=torch.uint8, device="cuda")
+        _fill_scratch(eng, byte)
+        eng.init_canvas(reqs, x, m, seeds, blocks)
+        rec = []
+        for step in range(1, S + 1):
+            st = eng.new_stats(n_req)
+            _fill_scratch(eng, byte)
+            eng.denoise_step(reqs, x, m, step, S, seeds, blocks, st)
+            torch.cuda.synchronize()
+            rec += [x.cpu(), m.cpu(), st.cpu()]
+        _fill_scratch(eng, byte)
+        eng.commit_block(reqs, x)
+        torch.cuda.synchronize()
+        lo, hi = eng.layout.prev, B.WS_FIELDS[B.WS_FIELDS.index("prev") + 1]
+        rec += [eng.ws[lo:getattr(eng.layout, hi)].cpu(), eng.kv[:eng.kv_bytes].cpu()]
+        assert eng.moe_counters()["spin_timeouts"] == 0
+        outs.append(rec)
+    for j, (a, b) in enumerate(zip(*outs)):
+        assert torch.equal(a, b), f"output {j} differs between zeroed and NaN-filled scratch"
+    say(f"[{which}] {len(outs[0])} outputs equal bit for bit")
