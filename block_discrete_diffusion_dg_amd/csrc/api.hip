@@ -247,9 +247,11 @@ void run_layer(dg_ctx* c, hipStream_t s, int l, const ReqTable& rt, int causal, 
   const RouterPermute rp = permute_outputs(c, rows);
   // shared-expert prefetch by the router's early leavers: only while the
   // router is one short round of work-groups (at more rows it lengthened the
-  // router more than it saved)
+  // router more than it saved) and has enough of them to split the 25 MB
+  // (at one row its 7 early leavers took ~3.6 MB each, and the AR step went
+  // from 2.9 to 4.0 ms)
   const void* const rpf[3] = {w.ws_gate, w.ws_up, w.ws_down};
-  const bool prefetch = rows <= 512;
+  const bool prefetch = rows >= 256 && rows <= 512;
   STAGE(DG_STAGE_ROUTER, launch_router(s, h, c->buf<float>(L.ss), w.moe_norm, rows, d, g.rms_eps, w.w_router,
                                        g.n_experts, g.top_k, u, c->buf<float>(L.z), c->buf<float>(L.zpart),
                                        c->buf<int32_t>(L.sync), c->buf<int32_t>(L.idx), c->buf<float>(L.w), &rp,
