@@ -413,3 +413,45 @@ def test_stale_scratch_is_never_read(which):
     for j, (a, b) in enumerate(zip(*outs)):
         assert torch.equal(a, b), f"output {j} differs between zeroed and NaN-filled scratch"
     say(f"[{which}] {len(outs[0])} outputs equal bit for bit")
+
+
+def test_cache_snapshot_resumes_bit_identically():
+    """The KV cache plus the committed length is a request's whole resumable
+    state: after a prefill and one committed block, a copy of the cache bytes
+    and the length, put into a fresh context with dg_set_cache_len, gives the
+    next block's denoising steps and commit bit for bit as the original
+    context does."""
+    cfg = dataclasses.replace(synth.TINY, n_layers=2)
+    P, S, C = 64, 3, cfg.canvas
+    engs = [make_engine(cfg, max_ctx=P + 3 * C)[0] for _ in range(2)]
+    a, b = engs
+    prompt = synth.make_prompt(P, cfg.vocab, 23).cuda()
+
+    def run_block(eng, block):
+        x = torch.empty(C, dtype=torch.int32, device="cuda")
+        m = torch.empty(C, dtype=torch.uint8, device="cuda")
+        eng.init_canvas([0], x, m, [7], [block])
+        rec = []
+        for step in range(1, S + 1):
+            st = eng.new_stats(1)
+            eng.denoise_step([0], x, m, step, S, [7], [block], st)
+            torch.cuda.synchronize()
+            rec += [x.cpu(), m.cpu(), st.cpu()]
+        eng.commit_block([0], x)
+        torch.cuda.synchronize()
+        return rec
+
+    a.prefill(0, prompt)
+    run_block(a, 0)
+    n = a.cache_len(0)
+    assert n == P + C
+    snap = a.kv[:a.kv_bytes].clone()
+    say(f"[snapshot] {a.kv_bytes} cache bytes, length {n}")
+    b.kv[:b.kv_bytes].copy_(snap)
+    b.set_cache_len(0, n)
+    torch.cuda.synchronize()
+    ra, rb = run_block(a, 1), run_block(b, 1)
+    assert a.cache_len(0) == b.cache_len(0) == n + C
+    for j, (u, v) in enumerate(zip(ra, rb)):
+        assert torch.equal(u, v), f"output {j} differs after the restore"
+    assert torch.equal(a.kv[:a.kv_bytes], b.kv[:b.kv_bytes])
