@@ -105,17 +105,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT >= 8 ? 2
   // work-groups free up, and the down items of their chunks wait for them.
   // Each runs as two half items of 32 columns instead, taken by two
   // work-groups, so that the last gate/up work streams with twice the
-  // concurrency. While its halves fill at most a quarter of the first round,
-  // the shared expert's items run as halves from the start: its chain
-  // (gate/up, then down items with K = Fs) is the longest in the launch,
-  // and halves start its down items about half a gate/up item sooner,
-  // without streaming any weight twice (experts 3.77 -> 3.75 ms per step at
-  // 256 rows). Queue: 2*n_sh shared halves, n_full whole items, 2*n_split
-  // halves, then the down items. Chunk counters count 32-column units (a
-  // whole item adds 2).
+  // concurrency. With bf16 weights, and while its halves fill at most a
+  // quarter of the first round, the shared expert's items run as halves
+  // from the start: its chain (gate/up, then down items with K = Fs) is the
+  // longest in the launch, and halves start its down items about half a
+  // gate/up item sooner, without streaming any weight twice (experts 3.77 ->
+  // 3.75 ms per step at 256 rows; with FP8 weights, whose items are half as
+  // long, the launch took 94 instead of 91 us). Queue: 2*n_sh shared
+  // halves, n_full whole items, 2*n_split halves, then the down items. Chunk
+  // counters count 32-column units (a whole item adds 2).
   __syncthreads();  // the item tables above are in LDS for every thread
   const int n_gu = s_gu[G];
-  const int n_sh = 8 * s_gu[1] <= (int)gridDim.x ? s_gu[1] : 0;
+  const int n_sh = (!W8 && 8 * s_gu[1] <= (int)gridDim.x) ? s_gu[1] : 0;
   const int n_r = n_gu - n_sh;
   const int n_full = min(n_r, max(0, (int)gridDim.x - 2 * n_sh));
   const int n_split = n_r - n_full;
