@@ -124,7 +124,7 @@ def test_tiny_block_loop_parity(confidence, stop_entropy, candidate, n_layers, s
         assert np.array_equal(st["conf"].numpy().view(np.int32), ce.astype(np.float32).view(np.int32))
         assert np.array_equal(acc, acce)
         assert np.array_equal(x.cpu().numpy(), xe) and np.array_equal(m.cpu().numpy(), me)
-        # free-running: the survey's tie band at the acceptance boundary, and
+        # free-running: a fixed tie band of 1e-5(1+|c|) at the acceptance boundary, and
         # the band that the 2e-2 logit tolerance implies (asserted)
         gap_band = 1e-5 * (1 + np.abs(keep["c"]).max())
         swap = not np.array_equal(acc, keep["accept"])
