@@ -31,6 +31,59 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def parse_clocks(text):
+    """rocm-smi --showclocks --json output -> {"card0": {"sclk": MHz, ...}}
+    (every "<name> clock speed:" entry of each card; None when the text
+    holds none)."""
+    import re
+    try:
+        data = json.loads(text)
+    except ValueError:
+        return None
+    out = {}
+    for card, fields in data.items() if isinstance(data, dict) else ():
+        if not isinstance(fields, dict):
+            continue
+        clk = {}
+        for key, val in fields.items():
+            m = re.match(r"\s*(\w+) clock speed", key)
+            v = re.search(r"(\d+(?:\.\d+)?)\s*Mhz", str(val), re.IGNORECASE)
+            if m and v:
+                clk[m.group(1)] = float(v.group(1))
+        if clk:
+            out[card] = clk
+    return out or None
+
+
+def clocks_under_load(step, max_s=5.0):
+    """The GPU clocks while the step runs back to back: rocm-smi runs as a
+    child process and samples them while this process keeps launching
+    steps (untimed). Best effort: None when rocm-smi is missing or fails."""
+    import shutil
+    import subprocess
+    import torch
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if exe is None:
+        return None
+    try:
+        proc = subprocess.Popen([exe, "--showclocks", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.time()
+    while proc.poll() is None and time.time() - t0 < max_s:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    try:
+        text, _ = proc.communicate(timeout=max(1.0, max_s - (time.time() - t0)))
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    return parse_clocks(text) if proc.returncode == 0 else None
+
+
 def fp8_expert_bytes(cfg, touched_experts):
     """Algorithmic bytes of one expert-kernel launch with FP8 expert weights:
     one byte per weight plus a 4-byte scale per weight row, for the touched
@@ -243,6 +296,17 @@ def main():
         if eng.moe_counters()["spin_timeouts"] != moe_g0["spin_timeouts"]:
             raise RuntimeError("expert kernel waits ran out during the graph-launched steps")
 
+    # the engine and memory clocks while steps run back to back (rocm-smi)
+    clocks = None
+    if not args.profile:
+        n_clk = [0]
+
+        def one_step():
+            run(1, n_clk[0])
+            n_clk[0] += 1
+        clocks = clocks_under_load(one_step)
+        log(f"clocks under load: {clocks}")
+
     # commit (the +K-1 forward of each block), timed once, then the length restored
     commit_ms = None
     if not args.profile:
@@ -324,6 +388,7 @@ def main():
         "launches_per_step": launches,
         "commit_ms": round(commit_ms, 3) if commit_ms is not None else None,
         "graph_launched": graph,
+        "clocks_mhz": clocks,
     }
     if not args.no_cpu_baseline and args.workload in ("full", "one_layer", "tiny"):
         hw = _HostWeights(layers, embed, final)

@@ -29,3 +29,14 @@ def test_algorithmic_bytes_of_the_expert_launch():
     assert per_step["lmhead"][0] == 1_073_741_824  # the tied embedding, read once
     # FP8: 64 x (4,325,376 code bytes + 13,824 scale bytes) + 12,582,912 + 24,576
     assert bench.fp8_expert_bytes(synth.FULL, 64.0) == 64 * (4_325_376 + 13_824) + 12_582_912 + 24_576
+
+
+def test_clock_record_parses_rocm_smi_json():
+    sys.path.insert(0, ROOT)
+    import bench
+    text = ('{"card0": {"dcefclk clock speed:": "(0Mhz)", "fclk clock speed:": "(1900Mhz)", '
+            '"mclk clock speed:": "(1900Mhz)", "mclk clock level:": "0", "sclk clock speed:": "(2400Mhz)", '
+            '"sclk clock level:": "1"}, "system": {"driver": "x"}}')
+    assert bench.parse_clocks(text) == {"card0": {"dcefclk": 0.0, "fclk": 1900.0, "mclk": 1900.0, "sclk": 2400.0}}
+    assert bench.parse_clocks("not json") is None
+    assert bench.parse_clocks('{"card0": {"Card series:": "x"}}') is None
