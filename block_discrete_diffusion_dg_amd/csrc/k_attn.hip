@@ -181,9 +181,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
 
   auto compute_tile = [&](int tile, const u32x4 (&tb)[CHUNKS][64]) {
     const int k0 = tile * KT;
-    // The tile's K fragments are read from LDS together, then the products
-    // run dimension step by dimension step over the four 16-key subtiles, so
-    // consecutive products never depend on each other.
+    // All of the tile's K fragments are read from LDS at once, in the order
+    // the products use them (dimension step major), so the first products
+    // wait only for the first reads; the products then run dimension step by
+    // dimension step over the four 16-key subtiles, so consecutive products
+    // never depend on each other. The scheduling barrier keeps the reads
+    // together: left to itself the compiler issued them in pairs, each pair
+    // followed by a wait for all outstanding LDS reads.
     f32x4 s[QB][4];
 #pragma unroll
     for (int j = 0; j < QB; ++j)
@@ -191,15 +195,24 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
       for (int ks = 0; ks < 4; ++ks) s[j][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 kf[4][NS];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
-      for (int st = 0; st < NS; ++st) kf[ks][st] = tb[ks * NS + st][lane];
+      for (int ks = 0; ks < 4; ++ks) kf[ks][st] = tb[ks * NS + st][lane];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < NS; ++st)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int j = 0; j < QB; ++j) s[j][ks] = mfma_bf16(kf[ks][st], qf[j][st], s[j][ks]);
+    // the V fragments of both 32-key blocks are read right behind the
+    // products, so they arrive while the softmax is formed
+    u32x4 vf[2][ND];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) vf[kk][dt] = tb[4 * NS + kk * ND + dt][lane];
+    __builtin_amdgcn_sched_barrier(0);
     const bool v_edge = k0 + KT > nk;
     const bool mask = v_edge || (causal && k0 + KT - 1 > P + qi_lo);
 #pragma unroll
@@ -241,9 +254,6 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
                           pack_bf16x2(s[j][2 * kk][2], s[j][2 * kk][3]),
                           pack_bf16x2(s[j][2 * kk + 1][0], s[j][2 * kk + 1][1]),
                           pack_bf16x2(s[j][2 * kk + 1][2], s[j][2 * kk + 1][3])};
-        u32x4 vf[ND];
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) vf[dt] = tb[4 * NS + kk * ND + dt][lane];
         if (v_edge) {
           // keys past nk: V entries may be unwritten cache rows (any bit
           // pattern); zero them so that 0 * V stays 0
@@ -252,11 +262,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const bf16_t* __restrict__ q,
             const int key = k0 + 32 * kk + (e >> 2) * 16 + 4 * grp + (e & 3);
             const uint32_t keep = key < nk ? 0xffffffffu : ((e & 1) ? 0x0000ffffu : 0xffff0000u);
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt) vf[dt][e >> 1] &= keep;
+            for (int dt = 0; dt < ND; ++dt) vf[kk][dt][e >> 1] &= keep;
           }
         }
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) oacc[j][dt] = mfma_bf16(vf[dt], pf, oacc[j][dt]);
+        for (int dt = 0; dt < ND; ++dt) oacc[j][dt] = mfma_bf16(vf[kk][dt], pf, oacc[j][dt]);
         lacc[j] = mfma_bf16(ones, pf, lacc[j]);
       }
     }
