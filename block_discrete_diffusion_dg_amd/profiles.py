@@ -5,6 +5,8 @@
       --kernel <name regex> --copy-bytes N --command-fetch "<cmd>" --command-write "<cmd>"
   python -m block_discrete_diffusion_dg_amd.profiles mfma <counter_csv> <out.md> --command "<cmd>"
       (counters MfmaUtil, MfmaFlopsBF16, GRBM_GUI_ACTIVE per dispatch)
+  python -m block_discrete_diffusion_dg_amd.profiles counters <counter_csv> <out.md> --kernel-regex R --command "<cmd>"
+      (any counters of the kernels matching R, with the wave-state ratios of SQ_RATIOS)
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) into HBM
 bytes per launch of one kernel, scaled by what the same counter reads for a
@@ -215,6 +217,42 @@ def summarize_mfma(csv_path: str, out_md: str, command: str, marker: str = MARKE
     return out
 
 
+# Wave-state counters of the shader sequencer and their ratios: wave-cycle
+# counters share one unit, so their ratios to SQ_WAVE_CYCLES are fractions of
+# the time waves were resident; bank conflicts are per LDS instruction cycle.
+SQ_RATIOS = [("waiting (any)", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+             ("waiting for an instruction to issue", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+             ("issuing (any)", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+             ("issuing LDS instructions", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+             ("waiting to issue an LDS instruction", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+             ("LDS bank-conflict cycles per LDS issue cycle", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")]
+
+
+def summarize_counters(csv_path: str, out_md: str, kernel_regex: str, command: str,
+                       marker: str = MARKER) -> dict:
+    """Mean per dispatch of every counter in the file for the kernels matching
+    kernel_regex (after the marker), and the SQ_RATIOS that the file holds."""
+    rows, found = after_marker(list(csv.DictReader(open(csv_path))), marker)
+    rx = re.compile(kernel_regex)
+    per = defaultdict(list)
+    for r in rows:
+        if rx.search(r["Kernel_Name"]):
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    means = {k: sum(v) / len(v) for k, v in sorted(per.items())}
+    ratios = {label: means[a] / means[b] for label, a, b in SQ_RATIOS
+              if a in means and b in means and means[b] > 0}
+    lines = [f"# Counters of `{kernel_regex}` (rocprofv3 --pmc)", "", f"Command: `{command}`", "",
+             _scope_line(found, marker), "",
+             "| counter | dispatches | mean per dispatch |", "|---|---:|---:|"]
+    lines += [f"| {k} | {len(per[k])} | {v:.6g} |" for k, v in means.items()]
+    if ratios:
+        lines += ["", "| ratio | value |", "|---|---:|"]
+        lines += [f"| {label} | {v:.3f} |" for label, v in ratios.items()]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return {"means": means, "ratios": ratios}
+
+
 def traffic_for(kernel: str, stem: str):
     """HBM bytes per launch recorded for `kernel`, or None when no record
     exists or the kernel's sources changed since it was taken."""
@@ -253,11 +291,19 @@ def main():
     m.add_argument("out")
     m.add_argument("--command", required=True)
     m.add_argument("--after", default=MARKER)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--kernel-regex", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--after", default=MARKER)
     a = ap.parse_args()
     if a.cmd == "stats":
         print(json.dumps(summarize_stats(a.csv, a.out, a.command, a.after), indent=1))
     elif a.cmd == "mfma":
         print(json.dumps(summarize_mfma(a.csv, a.out, a.command, a.after), indent=1))
+    elif a.cmd == "counters":
+        print(json.dumps(summarize_counters(a.csv, a.out, a.kernel_regex, a.command, a.after), indent=1))
     else:
         print(json.dumps(summarize_traffic(a.fetch_csv, a.write_csv, a.out_stem, a.kernel, a.kernel_regex,
                                            a.copy_bytes, a.command_fetch, a.command_write, a.after), indent=1))

@@ -93,3 +93,23 @@ def test_mfma_active_time_is_per_xcd(tmp_path):
     assert a["dispatches"] == 2 and a["mfma_util_pct"] == pytest.approx(5.0)
     assert a["active_us"] == pytest.approx(20.0)  # 48,000 cycles per XCD at 2.4 GHz
     assert a["tflops"] == pytest.approx(5e9 / 20e-6 / 1e12)
+
+
+def test_counter_means_and_wave_state_ratios(tmp_path):
+    rows = []
+    for did, name, wave, wait, lds, conf in [(1, "attn_kernel<128>", 1.0, 1.0, 1.0, 1.0),   # prefill, dropped
+                                             (2, "init_canvas_kernel", 5.0, 5.0, 5.0, 5.0),
+                                             (3, "attn_kernel<128>", 1000.0, 400.0, 100.0, 10.0),
+                                             (4, "attn_kernel<128>", 3000.0, 1600.0, 300.0, 50.0),
+                                             (5, "router_kernel<8>", 9e9, 9e9, 9e9, 9e9)]:  # other kernel
+        rows += [_pmc(did, name, "SQ_WAVE_CYCLES", wave), _pmc(did, name, "SQ_WAIT_ANY", wait),
+                 _pmc(did, name, "SQ_ACTIVE_INST_LDS", lds), _pmc(did, name, "SQ_LDS_BANK_CONFLICT", conf)]
+    src = tmp_path / "c.csv"
+    _write(src, PMC_COLS, rows)
+    out = P.summarize_counters(str(src), str(tmp_path / "c.md"), "attn_kernel", "cmd")
+    assert out["means"]["SQ_WAVE_CYCLES"] == pytest.approx(2000.0)
+    assert out["ratios"]["waiting (any)"] == pytest.approx(1000.0 / 2000.0)
+    assert out["ratios"]["issuing LDS instructions"] == pytest.approx(200.0 / 2000.0)
+    assert out["ratios"]["LDS bank-conflict cycles per LDS issue cycle"] == pytest.approx(30.0 / 200.0)
+    assert "waiting for an instruction to issue" not in out["ratios"]  # its counter was not collected
+    assert "| SQ_WAIT_ANY | 2 |" in (tmp_path / "c.md").read_text()
