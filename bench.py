@@ -423,6 +423,10 @@ def main():
         if not args.no_selfcond_variant:
             out["variants"]["self_conditioning"] = selfcond_variant(args, cfg, wl, layers, embed, final, reqs,
                                                                     seeds, blocks, canvas0, dev)
+    # every launch on the headline engine (timed, staged, graph-launched,
+    # commit and the variants that reuse it) ran with no expert-kernel wait
+    # running out, or this raises
+    eng.sync()
     print(json.dumps(out), flush=True)
 
 
@@ -507,6 +511,7 @@ def sampled_variant(args, eng, reqs, seeds, blocks, x, m, S):
     run(args.steps, args.warmup + args.steps)
     stages = eng.timing_read()
     eng.timing(False)
+    eng.sync()  # raises if a bounded wait of the expert kernel ran out
     log(f"sampled candidates: {ms:.3f} ms/step")
     return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
             "lmhead_ms": round(stages["lmhead"][0] / max(1, stages["lmhead"][1]), 4),
