@@ -194,6 +194,9 @@ def main():
                     help="for hardware-counter runs: skip the block commit, so that every dispatch after the "
                          "canvas set-up (init_canvas_kernel) belongs to a denoising step; the prefill runs as "
                          "usual, so routing and attention see the same inputs as the headline run")
+    ap.add_argument("--fp8-profile", action="store_true",
+                    help="with --profile only: the headline engine reads FP8 expert and LM-head weights, so that "
+                         "counter runs see the FP8 kernels on the headline's dispatches (never a headline number)")
     ap.add_argument("--no-variants", action="store_true",
                     help="measure the headline step only (no sampled-candidate, AR, FP8 or self-conditioning runs)")
     ap.add_argument("--no-selfcond-variant", action="store_true",
@@ -204,6 +207,9 @@ def main():
                     help="after the run, copy this many MiB device-to-device with a plain copy "
                          "kernel (reference for hardware byte counters)")
     args = ap.parse_args()
+    if args.fp8_profile and not args.profile:
+        print("--fp8-profile is for counter runs and needs --profile", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the denoising step "
               "is measured on a single MI355X; multi-GPU sharding is not implemented.",
@@ -228,7 +234,8 @@ def main():
     layers, embed, final = gpu_weights(cfg, wl.seed, 0.0, dev)
     torch.cuda.synchronize()
     log(f"weights generated on the GPU in {time.time() - t0:.1f}s")
-    eng = Engine(cfg, layers, embed, final, max_ctx=P + 2 * C, max_requests=n_req, max_rows=rows)
+    fmt = {"expert_format": "fp8", "lmhead_format": "fp8"} if args.fp8_profile else {}
+    eng = Engine(cfg, layers, embed, final, max_ctx=P + 2 * C, max_requests=n_req, max_rows=rows, **fmt)
     reqs = list(range(n_req))
     seeds = [wl.seed + r for r in reqs]
     blocks = [0] * n_req
@@ -367,7 +374,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not args.fp8_profile else "bf16 (fp8 expert and LM-head weights, counter run)",
         "data": "synthetic: seeded random-init bf16 weights, uniform prompt ids (no datasets or checkpoints)",
         "config": {"workload": wl.name, "layers": cfg.n_layers, "d_model": cfg.d_model,
                    "experts": f"{cfg.n_experts} routed top-{cfg.top_k} + 1 shared",

@@ -40,3 +40,9 @@ def test_clock_record_parses_rocm_smi_json():
     assert bench.parse_clocks(text) == {"card0": {"dcefclk": 0.0, "fclk": 1900.0, "mclk": 1900.0, "sclk": 2400.0}}
     assert bench.parse_clocks("not json") is None
     assert bench.parse_clocks('{"card0": {"Card series:": "x"}}') is None
+
+
+def test_fp8_profile_needs_profile():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--fp8-profile"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--profile" in r.stderr and r.stdout == ""
